@@ -1,0 +1,160 @@
+"""CPU oracle for the batch-invariant linear and MoE paths.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+benchmark's ``cpu_baseline`` leg may import this package.  The HIP library
+never imports, links or calls it, and it never imports the HIP library.
+
+The arithmetic lives in ``oracle.c`` (plain C, binary64 throughout, one
+round-to-nearest-even per storage point, ascending-index sums); this module
+only marshals numpy arrays into it.  bf16 tensors travel as ``numpy.uint16``
+bit patterns.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+_CFLAGS = ["-O2", "-fopenmp", "-ffp-contract=off", "-fno-fast-math",
+           "-fPIC", "-shared", "-std=c99", "-D_DEFAULT_SOURCE"]
+
+
+def build(force: bool = False) -> str:
+    """Compile oracle.c into liboracle.so with gcc (no HIP involved)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp"
+        subprocess.check_call(["gcc", *_CFLAGS, "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        lib = ctypes.CDLL(build())
+        P = ctypes.c_void_p
+        L = ctypes.c_long
+        lib.oracle_linear_f32.argtypes = [P, P, P, P, P, L, L, L]
+        lib.oracle_linear_bf16.argtypes = [P, P, P, P, P, P, L, L, L]
+        lib.oracle_topk.argtypes = [P, P, L, L, L]
+        lib.oracle_moe.argtypes = [P, P, P, P, P, L, L, L, L, L, P, P, P, P, P]
+        lib.oracle_f64_to_bf16.argtypes = [P, P, L]
+        for f in (lib.oracle_linear_f32, lib.oracle_linear_bf16, lib.oracle_topk,
+                  lib.oracle_moe, lib.oracle_f64_to_bf16, lib.oracle_num_threads):
+            f.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c(a, dtype):
+    if a is None:
+        return None
+    a = np.ascontiguousarray(a)
+    if a.dtype != dtype:
+        raise TypeError(f"expected {np.dtype(dtype)}, got {a.dtype}")
+    return a
+
+
+def num_threads() -> int:
+    return int(_load().oracle_num_threads())
+
+
+def linear_f32(x, w, bias=None, want_f64=False):
+    """y = RN_f32(x @ w.T + bias) with binary64 accumulation; w is [N, K]."""
+    x = _c(x, np.float32)
+    w = _c(w, np.float32)
+    bias = _c(bias, np.float32)
+    M, K = x.shape
+    N, K2 = w.shape
+    assert K == K2 and (bias is None or bias.shape == (N,))
+    y = np.empty((M, N), np.float32)
+    y64 = np.empty((M, N), np.float64) if want_f64 else None
+    rc = _load().oracle_linear_f32(_ptr(x), _ptr(w), _ptr(bias), _ptr(y), _ptr(y64), M, N, K)
+    if rc:
+        raise ValueError("oracle_linear_f32 rejected its arguments")
+    return (y, y64) if want_f64 else y
+
+
+def linear_bf16(x, w, bias=None, out="bf16", want_f64=False):
+    """Same definition with bf16 operands (uint16 bit patterns).
+
+    ``out`` is "bf16" (uint16 result) or "f32" (float32 result)."""
+    x = _c(x, np.uint16)
+    w = _c(w, np.uint16)
+    bias = _c(bias, np.float32)
+    M, K = x.shape
+    N, K2 = w.shape
+    assert K == K2 and (bias is None or bias.shape == (N,))
+    yb = np.empty((M, N), np.uint16) if out == "bf16" else None
+    yf = np.empty((M, N), np.float32) if out == "f32" else None
+    if yb is None and yf is None:
+        raise ValueError("out must be 'bf16' or 'f32'")
+    y64 = np.empty((M, N), np.float64) if want_f64 else None
+    rc = _load().oracle_linear_bf16(_ptr(x), _ptr(w), _ptr(bias), _ptr(yb), _ptr(yf),
+                                    _ptr(y64), M, N, K)
+    if rc:
+        raise ValueError("oracle_linear_bf16 rejected its arguments")
+    y = yb if yb is not None else yf
+    return (y, y64) if want_f64 else y
+
+
+def topk(scores, k):
+    """Per-row top-k ids: descending score, ties to the lower index, +-0 equal."""
+    s = _c(scores, np.float32)
+    M, E = s.shape
+    ids = np.empty((M, k), np.int32)
+    if _load().oracle_topk(_ptr(s), _ptr(ids), M, E, k):
+        raise ValueError("oracle_topk rejected its arguments (NaN score or bad k)")
+    return ids
+
+
+def moe(x, w_router, b_router, w13, w2, topk, ids=None):
+    """Batch-invariant MoE layer, binary64 with the method's storage points.
+
+    Returns (y [M,H] f32, ids [M,topk] i32, probs [M,topk] f64, logits [M,E] f32).
+    ``ids`` forces the expert choice instead of selecting it."""
+    x = _c(x, np.uint16)
+    w_router = _c(w_router, np.float32)
+    b_router = _c(b_router, np.float32)
+    w13 = _c(w13, np.uint16)
+    w2 = _c(w2, np.uint16)
+    M, H = x.shape
+    E, H2 = w_router.shape
+    E2, I2, H3 = w13.shape
+    E3, H4, I = w2.shape
+    assert H == H2 == H3 == H4 and E == E2 == E3 and I2 == 2 * I
+    ids_in = _c(ids, np.int32)
+    if ids_in is not None:
+        assert ids_in.shape == (M, topk)
+    y = np.empty((M, H), np.float32)
+    ids_out = np.empty((M, topk), np.int32)
+    probs = np.empty((M, topk), np.float64)
+    logits = np.empty((M, E), np.float32)
+    rc = _load().oracle_moe(_ptr(x), _ptr(w_router), _ptr(b_router), _ptr(w13), _ptr(w2),
+                            M, H, E, I, topk, _ptr(ids_in), _ptr(logits), _ptr(ids_out),
+                            _ptr(probs), _ptr(y))
+    if rc:
+        raise ValueError("oracle_moe rejected its arguments")
+    return y, ids_out, probs, logits
+
+
+def f64_to_bf16(v):
+    """Round binary64 values to bf16 bit patterns (one RNE step)."""
+    v = _c(np.asarray(v, np.float64), np.float64)
+    out = np.empty(v.shape, np.uint16)
+    if _load().oracle_f64_to_bf16(_ptr(v), _ptr(out), v.size):
+        raise ValueError("bad arguments")
+    return out

@@ -1,0 +1,326 @@
+/*
+ * oracle.c -- plain, slow, obviously correct CPU reference for the
+ * batch-invariant linear layer and the batch-invariant MoE layer.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may link, load or
+ * call this file: only the test suite, the smoke check and the benchmark's
+ * CPU-baseline leg use it.  It shares no source, header, table or helper with
+ * the HIP library.
+ *
+ * Arithmetic: every product and sum is carried in IEEE binary64 and each
+ * storage point is rounded exactly once, round-to-nearest-even.  Inputs of
+ * type fp32 or bf16 convert to binary64 exactly, and a product of two such
+ * values is exact in binary64 (at most 24+24 significant bits).  Sums run in
+ * ascending index order.  Built with -ffp-contract=off so no multiply-add is
+ * fused behind the reader's back.
+ *
+ * Sources (the three pages on batch-invariant inference):
+ *  - "[BI][DSv4] Batch-invariant GateLinear router with fp32 persistent
+ *    matmul", section "What": the router computes Y = X W^T + b in fp32 and
+ *    must never round through bf16; section "Tests": correctness against an
+ *    fp32 linear at atol 2e-3 / rtol 1e-4.
+ *  - "Batch-invariance generation with vLLM fused-MoE backend", section
+ *    "What's included": gated SwiGLU with routing probabilities applied at
+ *    the activation (fp32 math, one final bf16 rounding), fp32-accumulate
+ *    expert GEMMs, and a top-k reduction with unit weights summed in fp64;
+ *    review summary: gate|up half-split and a fixed slot-order reduction.
+ *  - "[BI][DSv4] Pin sparse-MLA decode and prefill scheduling", commit notes
+ *    of the deterministic per-row top-k: score descending, exact ties by
+ *    ascending index, -0.0 treated as +0.0.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* ---------------------------------------------------------------- rounding */
+
+/* bf16 is the top half of an IEEE binary32; widening is exact. */
+static double bf16_to_f64(uint16_t h)
+{
+    uint32_t u = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+/* Round a binary64 value to bf16 (8 significant bits, exponent range of
+ * binary32) with round-to-nearest, ties-to-even, in ONE step -- no detour
+ * through binary32, which would round twice.  The value is scaled by a power
+ * of two so that one bf16 ulp becomes 1.0, rounded to an integer with rint()
+ * (ties-to-even in the default rounding mode), and scaled back. */
+static uint16_t f64_to_bf16(double v)
+{
+    if (isnan(v))
+        return 0x7fc0;
+    if (v == 0.0 || isinf(v)) {
+        float f = (float)v;
+        uint32_t u;
+        memcpy(&u, &f, sizeof u);
+        return (uint16_t)(u >> 16);
+    }
+    int e;
+    frexp(fabs(v), &e);               /* |v| = m * 2^e, m in [0.5, 1) */
+    int ulp_exp = e - 8;              /* 8 significant bits */
+    if (ulp_exp < -133)               /* bf16 subnormal spacing is 2^-133 */
+        ulp_exp = -133;
+    double q = rint(ldexp(fabs(v), -ulp_exp));
+    double r = ldexp(q, ulp_exp);     /* exact, or 2^128 on overflow */
+    float f = (r >= 0x1p128) ? INFINITY : (float)r;
+    if (v < 0)
+        f = -f;
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    return (uint16_t)(u >> 16);
+}
+
+/* binary64 -> binary32 is a C conversion: IEEE round-to-nearest-even. */
+static float f64_to_f32(double v) { return (float)v; }
+
+int oracle_f64_to_bf16(const double* in, uint16_t* out, long n)
+{
+    if (n < 0 || (n > 0 && (!in || !out)))
+        return -1;
+    for (long i = 0; i < n; ++i)
+        out[i] = f64_to_bf16(in[i]);
+    return 0;
+}
+
+int oracle_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/* ------------------------------------------------------------------ linear */
+
+/* Y[m,n] = RN_f32( sum_{k ascending} x[m,k] * w[n,k]  +  b[n] ).
+ *
+ * GateLinear page, section "What": the router is a plain linear layer,
+ * Y = X W^T + b, computed in fp32.  w is the nn.Linear weight, [N,K]
+ * row-major, which is the memory behind the weight.t() [K,N] view the
+ * matmul receives.  b may be NULL (no bias term at all).  If y64 is not
+ * NULL it receives the binary64 value before the final rounding. */
+int oracle_linear_f32(const float* x, const float* w, const float* b,
+                      float* y, double* y64, long M, long N, long K)
+{
+    if (M < 0 || N < 0 || K < 0)
+        return -1;
+    if (M == 0 || N == 0)
+        return 0;
+    if (!x || !w || !y)
+        return -1;
+#pragma omp parallel for collapse(2) schedule(static)
+    for (long m = 0; m < M; ++m) {
+        for (long n = 0; n < N; ++n) {
+            double s = 0.0;
+            for (long k = 0; k < K; ++k)
+                s += (double)x[m * K + k] * (double)w[n * K + k];
+            if (b)
+                s += (double)b[n];
+            y[m * N + n] = f64_to_f32(s);
+            if (y64)
+                y64[m * N + n] = s;
+        }
+    }
+    return 0;
+}
+
+/* Same definition with bf16 operands: bf16 x bf16 products are exact in
+ * binary64.  The single storage rounding goes to bf16 (y_bf16) and/or to
+ * fp32 (y_f32); either pointer may be NULL but not both. */
+int oracle_linear_bf16(const uint16_t* x, const uint16_t* w, const float* b,
+                       uint16_t* y_bf16, float* y_f32, double* y64,
+                       long M, long N, long K)
+{
+    if (M < 0 || N < 0 || K < 0)
+        return -1;
+    if (M == 0 || N == 0)
+        return 0;
+    if (!x || !w || (!y_bf16 && !y_f32))
+        return -1;
+#pragma omp parallel for collapse(2) schedule(static)
+    for (long m = 0; m < M; ++m) {
+        for (long n = 0; n < N; ++n) {
+            double s = 0.0;
+            for (long k = 0; k < K; ++k)
+                s += bf16_to_f64(x[m * K + k]) * bf16_to_f64(w[n * K + k]);
+            if (b)
+                s += (double)b[n];
+            if (y_bf16)
+                y_bf16[m * N + n] = f64_to_bf16(s);
+            if (y_f32)
+                y_f32[m * N + n] = f64_to_f32(s);
+            if (y64)
+                y64[m * N + n] = s;
+        }
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------- top-k */
+
+/* Top-k of one row of fp32 scores: slot j holds the j-th largest value;
+ * equal values are taken in ascending index order; -0.0 and +0.0 compare
+ * equal (C's == already does).  Selection by repeated maximum: obviously
+ * correct, O(k*E).  NaN is outside the definition and is rejected. */
+static int topk_row(const float* v, long E, long k, int32_t* ids)
+{
+    for (long e = 0; e < E; ++e)
+        if (isnan(v[e]))
+            return -1;
+    unsigned char* taken = (unsigned char*)calloc((size_t)E, 1);
+    if (!taken)
+        return -1;
+    for (long j = 0; j < k; ++j) {
+        long best = -1;
+        for (long e = 0; e < E; ++e) {
+            if (taken[e])
+                continue;
+            if (best < 0 || v[e] > v[best])   /* strict: earlier index wins ties */
+                best = e;
+        }
+        taken[best] = 1;
+        ids[j] = (int32_t)best;
+    }
+    free(taken);
+    return 0;
+}
+
+int oracle_topk(const float* scores, int32_t* ids, long M, long E, long k)
+{
+    if (M < 0 || E <= 0 || k <= 0 || k > E)
+        return -1;
+    if (M == 0)
+        return 0;
+    if (!scores || !ids)
+        return -1;
+    int bad = 0;
+    for (long m = 0; m < M; ++m)
+        if (topk_row(scores + m * E, E, k, ids + m * k))
+            bad = 1;
+    return bad ? -1 : 0;
+}
+
+/* --------------------------------------------------------------------- MoE */
+
+/* One token through the batch-invariant MoE layer (fused-MoE page):
+ *
+ *  1. router logits  l[e]  = RN_f32( sum_h x[h] * wr[e,h] + br[e] )
+ *     (the fp32 router is the batch-invariant linear above, fed the bf16
+ *     activations widened to fp32; its fp32 output is a storage point and
+ *     the expert choice is taken on it)
+ *  2. ids = top-k of l (descending, ties to the lower expert index), or the
+ *     caller's ids_in when given
+ *  3. p[j] = exp(l[id_j] - max l) / sum_{e ascending} exp(l[e] - max l),
+ *     the full-softmax probability of the chosen expert, not renormalised
+ *  4. per slot j (expert e = ids[j]):  h[c] = RN_bf16( sum_h x[h]*w13[e,c,h] ),
+ *     c in [0, 2I): the first I rows of w13[e] are the gate, the next I the up
+ *     projection (gate|up half-split)
+ *  5. a[i] = RN_bf16( ((g*s) * u) * p[j] ),  g = h[i], u = h[I+i],
+ *     s = 1 / (1 + exp(-g)): SwiGLU with the routing probability applied at
+ *     the activation, one rounding at the end
+ *  6. y_j[c] = sum_{i ascending} a[i] * w2[e,c,i]
+ *  7. out[c] = RN_f32( sum_{j = 0..topk-1} y_j[c] ): unit-weight combine in
+ *     binary64, slot order
+ */
+int oracle_moe(const uint16_t* x, const float* wr, const float* br,
+               const uint16_t* w13, const uint16_t* w2,
+               long M, long H, long E, long I, long topk,
+               const int32_t* ids_in, float* logits_out, int32_t* ids_out,
+               double* probs_out, float* y)
+{
+    if (M < 0 || H <= 0 || E <= 0 || I <= 0 || topk <= 0 || topk > E)
+        return -1;
+    if (M == 0)
+        return 0;
+    if (!x || !wr || !w13 || !w2 || !ids_out || !probs_out || !y)
+        return -1;
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
+    for (long m = 0; m < M; ++m) {
+        const uint16_t* xm = x + m * H;
+        float* l = (float*)malloc(sizeof(float) * (size_t)E);
+        double* h = (double*)malloc(sizeof(double) * (size_t)(2 * I));
+        double* a = (double*)malloc(sizeof(double) * (size_t)I);
+        double* acc = (double*)calloc((size_t)H, sizeof(double));
+        int32_t* ids = ids_out + m * topk;
+        if (!l || !h || !a || !acc) {
+            bad = 1;
+            goto done;
+        }
+        /* 1. router logits, stored as fp32 */
+        for (long e = 0; e < E; ++e) {
+            double s = 0.0;
+            for (long k = 0; k < H; ++k)
+                s += bf16_to_f64(xm[k]) * (double)wr[e * H + k];
+            if (br)
+                s += (double)br[e];
+            l[e] = f64_to_f32(s);
+        }
+        if (logits_out)
+            memcpy(logits_out + m * E, l, sizeof(float) * (size_t)E);
+        /* 2. expert choice */
+        if (ids_in) {
+            for (long j = 0; j < topk; ++j) {
+                if (ids_in[m * topk + j] < 0 || ids_in[m * topk + j] >= E)
+                    bad = 1;
+                ids[j] = ids_in[m * topk + j];
+            }
+            if (bad)
+                goto done;
+        } else if (topk_row(l, E, topk, ids)) {
+            bad = 1;
+            goto done;
+        }
+        /* 3. softmax probabilities of the chosen experts */
+        double mx = l[0];
+        for (long e = 1; e < E; ++e)
+            if (l[e] > mx)
+                mx = l[e];
+        double den = 0.0;
+        for (long e = 0; e < E; ++e)
+            den += exp((double)l[e] - mx);
+        for (long j = 0; j < topk; ++j) {
+            double p = exp((double)l[ids[j]] - mx) / den;
+            probs_out[m * topk + j] = p;
+            long e = ids[j];
+            /* 4. gate|up projection, bf16 storage point */
+            const uint16_t* w13e = w13 + e * (2 * I) * H;
+            for (long c = 0; c < 2 * I; ++c) {
+                double s = 0.0;
+                for (long k = 0; k < H; ++k)
+                    s += bf16_to_f64(xm[k]) * bf16_to_f64(w13e[c * H + k]);
+                h[c] = bf16_to_f64(f64_to_bf16(s));
+            }
+            /* 5. SwiGLU with the probability applied, bf16 storage point */
+            for (long i = 0; i < I; ++i) {
+                double g = h[i], u = h[I + i];
+                double sg = 1.0 / (1.0 + exp(-g));
+                a[i] = bf16_to_f64(f64_to_bf16(((g * sg) * u) * p));
+            }
+            /* 6.+7. down projection, summed over slots in slot order */
+            const uint16_t* w2e = w2 + e * H * I;
+            for (long c = 0; c < H; ++c) {
+                double s = 0.0;
+                for (long i = 0; i < I; ++i)
+                    s += a[i] * bf16_to_f64(w2e[c * I + i]);
+                acc[c] += s;
+            }
+        }
+        for (long c = 0; c < H; ++c)
+            y[m * H + c] = f64_to_f32(acc[c]);
+    done:
+        free(l);
+        free(h);
+        free(a);
+        free(acc);
+    }
+    return bad ? -1 : 0;
+}
