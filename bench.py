@@ -1,0 +1,224 @@
+"""Benchmark of the batch-invariant router GEMM on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+Workload (one "step"): the DeepSeek-V4-shaped fp32 router GateLinear,
+X[M,4096] x W[256,4096]^T + b, called once for every decode batch size
+M in {1,2,4,8,15,16,17,32,33,64,128}.  The weight is cold: each call reads
+the next of 96 distinct copies of W (384 MiB in total, more than the 256 MB
+Infinity Cache), so HBM claims are not cache hits.  Inputs are synthetic
+(seeded normal draws, see workloads.py) and resident in HBM before timing.
+
+Timing: all launches of the timed region are queued behind a spin kernel, so
+the host's launch latency never shows; every launch is bracketed by HIP
+events on the stream it runs on.  `value` is whole-step throughput
+(algorithmic bytes of the step / step time); the roofline object reports the
+decode kernel's average launch duration against the 8 TB/s HBM peak.
+The prefill leg (M = 1024, 4096) reports TFLOP/s against the fp32 MFMA peak.
+The CPU baseline times the fp64 oracle on the same decode sweep.
+
+Prints exactly one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+FP32_MFMA_PEAK_TFLOPS = 157.3
+N_COPIES = 96
+
+
+def router_bytes(M, N=256, K=4096):
+    """Algorithmic HBM bytes of one router call: W, X, bias read once, Y written once."""
+    return 4 * (N * K + M * K + M * N + N)
+
+
+def router_flops(M, N=256, K=4096):
+    return 2 * M * N * K
+
+
+def spin(torch, ms: float):
+    """Queue a spin kernel of about `ms` milliseconds on the current stream."""
+    torch.cuda._sleep(int(ms * spin.cycles_per_ms))
+
+
+spin.cycles_per_ms = 1.0e6
+
+
+def calibrate_spin(torch):
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    s.record()
+    torch.cuda._sleep(2_000_000)
+    e.record()
+    torch.cuda.synchronize()
+    spin.cycles_per_ms = 2_000_000 / max(s.elapsed_time(e), 1e-3)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import deterministic_persistent_gemm_amd as bi
+    import workloads as wl
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    calibrate_spin(torch)
+
+    w = wl.router_weights(0)
+    w_host = torch.from_numpy(w.w)
+    copies = [w_host.to(dev) for _ in range(N_COPIES)]
+    bias = torch.from_numpy(w.b).to(dev)
+    sweep = list(wl.ROUTER_DECODE_M)
+    xs = {M: torch.from_numpy(wl.router_batch(M, w).x).to(dev) for M in sweep}
+    outs = {M: torch.empty((M, 256), dtype=torch.float32, device=dev) for M in sweep}
+    bytes_step = sum(router_bytes(M) for M in sweep)
+    calls_per_step = len(sweep)
+
+    state = {"i": 0}
+
+    def one_call(M):
+        wd = copies[state["i"] % N_COPIES]
+        state["i"] += 1
+        bi.bi_linear_f32(xs[M], wd.t(), bias, out=outs[M])
+
+    # warm-up (also allocates the workspace outside the timed region)
+    for _ in range(args.warmup):
+        for M in sweep:
+            one_call(M)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(K * calls_per_step)]
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # the host needs ~30 us per call to enqueue; keep the GPU behind it
+    spin(torch, 5.0 + 0.05 * K * calls_per_step)
+    t0.record()
+    j = 0
+    for _ in range(K):
+        for M in sweep:
+            ev[j][0].record()
+            one_call(M)
+            ev[j][1].record()
+            j += 1
+    t1.record()
+    torch.cuda.synchronize()
+    total_ms = t0.elapsed_time(t1)
+    per_call_us = np.array([a.elapsed_time(b) * 1e3 for a, b in ev]).reshape(K, calls_per_step)
+    ms_per_step = total_ms / K
+    value = bytes_step / (ms_per_step * 1e-3) / 1e9
+
+    med_us = np.median(per_call_us, axis=0)
+    per_m = {}
+    for i, M in enumerate(sweep):
+        t = med_us[i] * 1e-6
+        per_m[str(M)] = {
+            "us": round(float(med_us[i]), 3),
+            "GBps": round(router_bytes(M) / t / 1e9, 1),
+            "TFLOPs": round(router_flops(M) / t / 1e12, 2),
+            "hbm_frac": round(router_bytes(M) / t / 1e9 / HBM_PEAK_GBS, 4),
+        }
+    mean_launch_us = float(np.mean(per_call_us))
+    achieved = bytes_step / calls_per_step / (mean_launch_us * 1e-6) / 1e9
+
+    extra = {"decode_per_M": per_m, "weight": f"cold: {N_COPIES} rotating copies of W (384 MiB)",
+             "launch_timing": "HIP events around each launch, queued behind a spin kernel"}
+
+    if not args.no_prefill:
+        extra["prefill"] = prefill_leg(torch, np, bi, wl, w, copies, bias, dev)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(np, wl, w, sweep)
+
+    line = {
+        "metric": "router GateLinear fp32 GEMM, decode sweep M=1..128: HBM GB/s (bit-invariant)",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "DSv4 router GateLinear fp32, X[M,4096] W[256,4096] (weight.t()) + bias, "
+                               "decode sweep M in {1,2,4,8,15,16,17,32,33,64,128}",
+                   "sweep": sweep, "N": 256, "K": 4096},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "k_decode<F32,F32,4> (avg over the sweep's launches)"},
+        "cpu_baseline": cpu,
+        "extra": extra,
+    }
+    print(json.dumps(line))
+
+
+def prefill_leg(torch, np, bi, wl, w, copies, bias, dev):
+    res = {}
+    for M in wl.ROUTER_PREFILL_M:
+        x = torch.from_numpy(wl.router_batch(M, w).x).to(dev)
+        out = torch.empty((M, 256), dtype=torch.float32, device=dev)
+        for i in range(3):
+            bi.bi_linear_f32(x, copies[i].t(), bias, out=out)
+        torch.cuda.synchronize()
+        n = 20
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        spin(torch, 2.0)
+        for i in range(n):
+            ev[i][0].record()
+            bi.bi_linear_f32(x, copies[i % len(copies)].t(), bias, out=out)
+            ev[i][1].record()
+        torch.cuda.synchronize()
+        us = float(np.median([a.elapsed_time(b) * 1e3 for a, b in ev]))
+        tf = router_flops(M) / (us * 1e-6) / 1e12
+        res[str(M)] = {"us": round(us, 2), "TFLOPs": round(tf, 2),
+                       "mfma_frac": round(tf / FP32_MFMA_PEAK_TFLOPS, 4)}
+    return res
+
+
+def cpu_baseline(np, wl, w, sweep):
+    """The fp64 oracle as it stands, on the decode sweep, on the host cores."""
+    import oracle
+    batches = {M: wl.router_batch(M, w).x for M in sweep}
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        for M in sweep:
+            oracle.linear_f32(batches[M], w.w, w.b)
+        reps += 1
+        if time.perf_counter() - t0 > 10.0 or reps >= 50:
+            break
+    dt = time.perf_counter() - t0
+    bytes_step = sum(router_bytes(M) for M in sweep)
+    return {"value": round(bytes_step * reps / dt / 1e9, 3), "unit": "GB/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"{reps} passes of the decode sweep (M=1..128, N=256, K=4096), fp64 C oracle, "
+                      f"{dt:.1f} s"}
+
+
+if __name__ == "__main__":
+    main()

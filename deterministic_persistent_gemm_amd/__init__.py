@@ -1,0 +1,243 @@
+"""Batch-invariant GEMM for MI355X (gfx950): thin Python binding of libbi.so.
+
+Every computation runs in the HIP kernels behind the C ABI declared in
+``include/bi.h``; this module only checks tensor metadata, allocates outputs
+and workspaces with PyTorch, and passes raw device pointers plus the current
+HIP stream.  The library must be built (``python -m
+deterministic_persistent_gemm_amd._build``); importing without it raises.
+
+Weights are taken in the production ``weight.t()`` layout: ``wt`` is the
+[K, N] transposed view of an nn.Linear weight [N, K], i.e. ``wt.stride(0) ==
+1``.  The names match the C entry points.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libbi.so")
+
+BI_OK, BI_EINVAL, BI_EUNSUPPORTED, BI_EWORKSPACE, BI_EHIP = range(5)
+BI_F32, BI_BF16 = 0, 1
+BI_PATH_AUTO, BI_PATH_DECODE, BI_PATH_PERSISTENT = 0, 1, 2
+BI_R2_TILE_PARTIAL = 2
+BI_MFMA_F32_16X16X4_F32, BI_MFMA_F32_16X16X32_BF16 = 1, 2
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is not built; run `python -m deterministic_persistent_gemm_amd._build`")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+
+class Recipe(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in
+                ("dtype", "mfma", "k_group", "reduce", "block_k", "bias_last", "m_decode_max", "reserved")]
+
+    def as_dict(self):
+        return {n: getattr(self, n) for n, _ in self._fields_ if n != "reserved"}
+
+
+_P, _I64, _I32, _SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
+_lib.bi_linear_f32.argtypes = [_P, _I64, _P, _I64, _P, _P, _I64, _I64, _I64, _I64, _P, _SZ, _P]
+_lib.bi_linear_bf16.argtypes = [_P, _I64, _P, _I64, _P, _P, _I32, _I64, _I64, _I64, _I64, _P, _SZ, _P]
+_lib.bi_negctl_linear_f32.argtypes = _lib.bi_linear_f32.argtypes
+_lib.bi_lab_linear.argtypes = [_P, _I64, _P, _I64, _P, _P, _I32, _I64, _I64, _I64, _I64,
+                               ctypes.POINTER(Recipe), _I32, _P, _SZ, _P]
+_lib.bi_moe_grouped_gemm.argtypes = [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _P, _P, _P,
+                                     _P, _SZ, _P]
+_lib.bi_linear_workspace_size.argtypes = [_I32, _I64, _I64, _I64]
+_lib.bi_lab_workspace_size.argtypes = [ctypes.POINTER(Recipe), _I32, _I64, _I64, _I64]
+_lib.bi_moe_workspace_size.argtypes = [_I64, _I64, _I64, _I64, _I64]
+_lib.bi_describe_recipe.argtypes = [_I32, _I64, _I64, ctypes.POINTER(Recipe)]
+_lib.bi_status_str.argtypes = [_I32]
+for _f in (_lib.bi_linear_f32, _lib.bi_linear_bf16, _lib.bi_negctl_linear_f32, _lib.bi_lab_linear,
+           _lib.bi_moe_grouped_gemm, _lib.bi_describe_recipe):
+    _f.restype = _I32
+for _f in (_lib.bi_linear_workspace_size, _lib.bi_lab_workspace_size, _lib.bi_moe_workspace_size):
+    _f.restype = _SZ
+_lib.bi_status_str.restype = ctypes.c_char_p
+
+
+class BIError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {_lib.bi_status_str(status).decode()}")
+
+
+def _check(status: int, where: str):
+    if status != BI_OK:
+        raise BIError(status, where)
+
+
+# ------------------------------------------------------------------ workspace
+
+_ws_lock = threading.Lock()
+_ws_cache: dict = {}
+
+
+def _workspace(nbytes: int, device: torch.device, stream: torch.cuda.Stream) -> torch.Tensor | None:
+    """Zero-filled, grow-only workspace per (device, stream).  The library
+    leaves its counters at zero after every call, so it is reused as is."""
+    if nbytes == 0:
+        return None
+    key = (device.index, stream.cuda_stream)
+    with _ws_lock:
+        ws = _ws_cache.get(key)
+        if ws is None or ws.numel() < nbytes:
+            ws = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
+            _ws_cache[key] = ws
+        return ws
+
+
+def _stream(device) -> torch.cuda.Stream:
+    return torch.cuda.current_stream(device)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check_xw(x: torch.Tensor, wt: torch.Tensor, dtype: torch.dtype, name: str):
+    if x.dtype != dtype or wt.dtype != dtype:
+        raise TypeError(f"{name}: x and wt must be {dtype}, got {x.dtype} and {wt.dtype}")
+    if not (x.is_cuda and wt.is_cuda and x.device == wt.device):
+        raise ValueError(f"{name}: x and wt must be on the same GPU")
+    if x.dim() != 2 or wt.dim() != 2:
+        raise ValueError(f"{name}: x is [M, K] and wt is [K, N]")
+    if x.shape[1] != wt.shape[0]:
+        raise ValueError(f"{name}: K mismatch {tuple(x.shape)} x {tuple(wt.shape)}")
+    if x.stride(1) != 1:
+        raise ValueError(f"{name}: x rows must be contiguous")
+    if wt.stride(0) != 1:
+        raise ValueError(f"{name}: wt must be the weight.t() view of an [N, K] weight (wt.stride(0) == 1)")
+
+
+def _check_bias(bias, N, device, name):
+    if bias is None:
+        return
+    if bias.dtype != torch.float32 or bias.shape != (N,) or not bias.is_contiguous() or bias.device != device:
+        raise ValueError(f"{name}: bias must be a contiguous fp32 [{N}] tensor on {device}")
+
+
+# ---------------------------------------------------------------- entry points
+
+
+def bi_linear_f32(x: torch.Tensor, wt: torch.Tensor, bias: torch.Tensor | None = None,
+                  out: torch.Tensor | None = None) -> torch.Tensor:
+    """y = x @ wt + bias in fp32, batch-invariant.  x [M, K], wt = weight.t() [K, N]."""
+    _check_xw(x, wt, torch.float32, "bi_linear_f32")
+    M, K = x.shape
+    N = wt.shape[1]
+    _check_bias(bias, N, x.device, "bi_linear_f32")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=x.device)
+    s = _stream(x.device)
+    nbytes = _lib.bi_linear_workspace_size(BI_F32, M, N, K)
+    ws = _workspace(nbytes, x.device, s)
+    _check(_lib.bi_linear_f32(_ptr(x), x.stride(0), _ptr(wt), wt.stride(1), _ptr(bias), _ptr(out),
+                              out.stride(0), M, N, K, _ptr(ws), 0 if ws is None else ws.numel(),
+                              ctypes.c_void_p(s.cuda_stream)), "bi_linear_f32")
+    return out
+
+
+def bi_linear_bf16(x: torch.Tensor, wt: torch.Tensor, bias: torch.Tensor | None = None,
+                   out_dtype: torch.dtype = torch.bfloat16, out: torch.Tensor | None = None) -> torch.Tensor:
+    """y = x @ wt + bias with bf16 operands, fp32 accumulation, bf16 or fp32 out."""
+    _check_xw(x, wt, torch.bfloat16, "bi_linear_bf16")
+    M, K = x.shape
+    N = wt.shape[1]
+    _check_bias(bias, N, x.device, "bi_linear_bf16")
+    if out_dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("out_dtype must be bfloat16 or float32")
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=x.device)
+    s = _stream(x.device)
+    nbytes = _lib.bi_linear_workspace_size(BI_BF16, M, N, K)
+    ws = _workspace(nbytes, x.device, s)
+    _check(_lib.bi_linear_bf16(_ptr(x), x.stride(0), _ptr(wt), wt.stride(1), _ptr(bias), _ptr(out),
+                               BI_BF16 if out.dtype == torch.bfloat16 else BI_F32, out.stride(0), M, N, K,
+                               _ptr(ws), 0 if ws is None else ws.numel(), ctypes.c_void_p(s.cuda_stream)),
+           "bi_linear_bf16")
+    return out
+
+
+def bi_negctl_linear_f32(x, wt, bias=None, out=None):
+    """Negative control: same call with an M-dependent BLOCK_K (expected to break invariance)."""
+    _check_xw(x, wt, torch.float32, "bi_negctl_linear_f32")
+    M, K = x.shape
+    N = wt.shape[1]
+    _check_bias(bias, N, x.device, "bi_negctl_linear_f32")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=x.device)
+    s = _stream(x.device)
+    ws = _workspace(_lib.bi_linear_workspace_size(BI_F32, M, N, K), x.device, s)
+    _check(_lib.bi_negctl_linear_f32(_ptr(x), x.stride(0), _ptr(wt), wt.stride(1), _ptr(bias), _ptr(out),
+                                     out.stride(0), M, N, K, _ptr(ws), 0 if ws is None else ws.numel(),
+                                     ctypes.c_void_p(s.cuda_stream)), "bi_negctl_linear_f32")
+    return out
+
+
+def bi_describe_recipe(dtype: int, N: int, K: int) -> Recipe:
+    r = Recipe()
+    _check(_lib.bi_describe_recipe(dtype, N, K, ctypes.byref(r)), "bi_describe_recipe")
+    return r
+
+
+def bi_lab_linear(x, wt, bias=None, recipe: Recipe | None = None, path: int = BI_PATH_AUTO,
+                  out_dtype=None, out=None):
+    """Linear layer with an explicit recipe and kernel path (experiments only)."""
+    dt = torch.float32 if x.dtype == torch.float32 else torch.bfloat16
+    _check_xw(x, wt, dt, "bi_lab_linear")
+    M, K = x.shape
+    N = wt.shape[1]
+    _check_bias(bias, N, x.device, "bi_lab_linear")
+    if recipe is None:
+        recipe = bi_describe_recipe(BI_F32 if dt == torch.float32 else BI_BF16, N, K)
+    out_dtype = out_dtype or (torch.float32 if dt == torch.float32 else torch.bfloat16)
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=x.device)
+    s = _stream(x.device)
+    ws = _workspace(_lib.bi_lab_workspace_size(ctypes.byref(recipe), path, M, N, K), x.device, s)
+    _check(_lib.bi_lab_linear(_ptr(x), x.stride(0), _ptr(wt), wt.stride(1), _ptr(bias), _ptr(out),
+                              BI_BF16 if out.dtype == torch.bfloat16 else BI_F32, out.stride(0), M, N, K,
+                              ctypes.byref(recipe), path, _ptr(ws), 0 if ws is None else ws.numel(),
+                              ctypes.c_void_p(s.cuda_stream)), "bi_lab_linear")
+    return out
+
+
+def bi_moe_grouped_gemm(x, w_router, b_router, w13, w2, topk: int):
+    """Batch-invariant MoE layer.  Returns (y fp32 [M,H], topk_ids int32 [M,topk],
+    topk_probs fp32 [M,topk]).  w13 [E, 2I, H] and w2 [E, H, I] are the experts'
+    nn.Linear weights (their .t() views are what the GEMMs consume)."""
+    if x.dtype != torch.bfloat16 or w13.dtype != torch.bfloat16 or w2.dtype != torch.bfloat16:
+        raise TypeError("bi_moe_grouped_gemm: x, w13, w2 must be bfloat16")
+    if w_router.dtype != torch.float32:
+        raise TypeError("bi_moe_grouped_gemm: w_router must be float32")
+    for t in (x, w_router, w13, w2) + (() if b_router is None else (b_router,)):
+        if not t.is_contiguous() or not t.is_cuda or t.device != x.device:
+            raise ValueError("bi_moe_grouped_gemm: tensors must be contiguous and on the same GPU")
+    M, H = x.shape
+    E = w_router.shape[0]
+    I = w2.shape[2]
+    if w_router.shape != (E, H) or w13.shape != (E, 2 * I, H) or w2.shape != (E, H, I):
+        raise ValueError("bi_moe_grouped_gemm: inconsistent shapes")
+    _check_bias(b_router, E, x.device, "bi_moe_grouped_gemm")
+    y = torch.empty((M, H), dtype=torch.float32, device=x.device)
+    ids = torch.empty((M, topk), dtype=torch.int32, device=x.device)
+    probs = torch.empty((M, topk), dtype=torch.float32, device=x.device)
+    s = _stream(x.device)
+    ws = _workspace(_lib.bi_moe_workspace_size(M, H, E, I, topk), x.device, s)
+    _check(_lib.bi_moe_grouped_gemm(_ptr(x), _ptr(w_router), _ptr(b_router), _ptr(w13), _ptr(w2),
+                                    M, H, E, I, topk, _ptr(ids), _ptr(probs), _ptr(y),
+                                    _ptr(ws), 0 if ws is None else ws.numel(), ctypes.c_void_p(s.cuda_stream)),
+           "bi_moe_grouped_gemm")
+    return y, ids, probs
+
+
+def lib():
+    """The loaded ctypes library (for tests that call the C ABI directly)."""
+    return _lib

@@ -1,0 +1,140 @@
+// bi_device.h -- device building blocks shared by every batch-invariant kernel.
+//
+// The numeric recipe lives here, in one place, so that every kernel path (the
+// k-tile-parallel decode kernel, the persistent kernel, the grouped MoE
+// kernels) performs the identical sequence of floating-point operations for
+// each output element:
+//
+//   * K is walked in k blocks of 32.  In a block starting at k0, lane l of a
+//     wave holds, for its tile row r = l % 16, the eight consecutive operand
+//     values k0 + 8g .. k0 + 8g + 7 of slot g = l / 16.
+//   * fp32 operands: eight v_mfma_f32_16x16x4_f32 per block, instruction s
+//     (s = 0..7, ascending) taking element s of every slot, i.e. the four k
+//     values k0+s, k0+8+s, k0+16+s, k0+24+s in slots 0..3.
+//   * bf16 operands: one v_mfma_f32_16x16x32_bf16 per block taking all 32.
+//   * A tile partial is the chain of these instructions over block_k/32
+//     consecutive blocks, started from +0.0; tile partials are added in
+//     ascending tile order (acc = P0; acc = acc + P1; ...); bias is added once
+//     at the end.
+//
+// GateLinear page, "A correction to why the key excludes M": chunk
+// independence of a chained dot product is a property of how a compiler
+// lowers it, not a contract, so the instruction, the slot assignment and the
+// tile width are fixed here explicitly rather than left to a lowering.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bi {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+constexpr int kKBlock = 32;   // k values per block
+constexpr int kSlotLen = 8;   // consecutive k values per lane slot
+
+// Operand kinds.  F32: fp32 in memory, fp32 instruction.  BF16: bf16 in
+// memory, bf16 instruction.  BF16W: bf16 in memory, widened exactly to fp32
+// and fed to the fp32 instruction (the MoE router reads bf16 activations).
+struct F32   { using elem = float;    static constexpr bool f32_frag = true;  static constexpr bool widen = false; };
+struct BF16  { using elem = uint16_t; static constexpr bool f32_frag = false; static constexpr bool widen = false; };
+struct BF16W { using elem = uint16_t; static constexpr bool f32_frag = true;  static constexpr bool widen = true; };
+
+// One lane's eight operand values of one k block, in instruction form.
+template <bool F32Frag> struct Frag;
+template <> struct Frag<true>  { f32x4 lo, hi; };   // fp32: elements 0..3, 4..7
+template <> struct Frag<false> { u32x4 v; };        // bf16: 8 packed values
+
+template <typename Op> using FragOf = Frag<Op::f32_frag>;
+
+__device__ __forceinline__ f32x4 widen_lo(u32x4 v)
+{
+    f32x4 r;
+    r[0] = __uint_as_float(v[0] << 16); r[1] = __uint_as_float(v[0] & 0xffff0000u);
+    r[2] = __uint_as_float(v[1] << 16); r[3] = __uint_as_float(v[1] & 0xffff0000u);
+    return r;
+}
+__device__ __forceinline__ f32x4 widen_hi(u32x4 v)
+{
+    f32x4 r;
+    r[0] = __uint_as_float(v[2] << 16); r[1] = __uint_as_float(v[2] & 0xffff0000u);
+    r[2] = __uint_as_float(v[3] << 16); r[3] = __uint_as_float(v[3] & 0xffff0000u);
+    return r;
+}
+
+// Load one lane's slot (8 consecutive elements at p, 16-byte aligned).
+template <typename Op>
+__device__ __forceinline__ void load_frag(FragOf<Op>& f, const typename Op::elem* p)
+{
+    if constexpr (Op::f32_frag && !Op::widen) {
+        f.lo = *reinterpret_cast<const f32x4*>(p);
+        f.hi = *reinterpret_cast<const f32x4*>(p + 4);
+    } else if constexpr (Op::widen) {
+        u32x4 v = *reinterpret_cast<const u32x4*>(p);
+        f.lo = widen_lo(v);
+        f.hi = widen_hi(v);
+    } else {
+        f.v = *reinterpret_cast<const u32x4*>(p);
+    }
+}
+
+template <typename Op>
+__device__ __forceinline__ void zero_frag(FragOf<Op>& f)
+{
+    if constexpr (Op::f32_frag) {
+        f.lo = f32x4{0.f, 0.f, 0.f, 0.f};
+        f.hi = f.lo;
+    } else {
+        f.v = u32x4{0u, 0u, 0u, 0u};
+    }
+}
+
+// One fp32 instruction of a block: step s takes element s of the slot.
+template <int S>
+__device__ __forceinline__ f32x4 mfma_f32_step(const Frag<true>& a, const Frag<true>& b, f32x4 acc)
+{
+    const float av = S < 4 ? a.lo[S & 3] : a.hi[S & 3];
+    const float bv = S < 4 ? b.lo[S & 3] : b.hi[S & 3];
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, acc, 0, 0, 0);
+}
+
+// The whole block for one 16x16 output tile, in recipe order.
+__device__ __forceinline__ f32x4 mfma_block(const Frag<true>& a, const Frag<true>& b, f32x4 acc)
+{
+    acc = mfma_f32_step<0>(a, b, acc);
+    acc = mfma_f32_step<1>(a, b, acc);
+    acc = mfma_f32_step<2>(a, b, acc);
+    acc = mfma_f32_step<3>(a, b, acc);
+    acc = mfma_f32_step<4>(a, b, acc);
+    acc = mfma_f32_step<5>(a, b, acc);
+    acc = mfma_f32_step<6>(a, b, acc);
+    acc = mfma_f32_step<7>(a, b, acc);
+    return acc;
+}
+
+__device__ __forceinline__ f32x4 mfma_block(const Frag<false>& a, const Frag<false>& b, f32x4 acc)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a.v),
+                                                   __builtin_bit_cast(bf16x8, b.v), acc, 0, 0, 0);
+}
+
+// fp32 -> bf16, round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u)
+        return (uint16_t)((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+// Output element a lane owns in a 16x16 accumulator tile: register q of lane
+// l is row 4*(l/16) + q, column l % 16.
+__device__ __forceinline__ int acc_row(int lane, int q) { return 4 * (lane >> 4) + q; }
+__device__ __forceinline__ int acc_col(int lane) { return lane & 15; }
+
+}  // namespace bi

@@ -1,0 +1,29 @@
+// bi_launch.h -- kernel launchers behind the C ABI (host side).
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+#include "bi_plan.h"
+
+namespace bi {
+
+// How X is stored for an fp32-recipe call: fp32, or bf16 widened exactly to
+// fp32 on load (the MoE router reads the layer's bf16 activations).
+enum XKind { kXF32 = 0, kXBF16Widen = 1, kXBF16 = 2 };
+
+struct LinearArgs {
+    const void* x;
+    int64_t ldx;
+    const void* w;
+    int64_t ldw;
+    const float* bias;
+    void* y;
+    int y_bf16;
+    int64_t ldy;
+    int M, N, K;
+};
+
+hipError_t launch_linear(int xkind, const LinearArgs& a, const Plan& p, void* ws, hipStream_t s);
+
+}  // namespace bi

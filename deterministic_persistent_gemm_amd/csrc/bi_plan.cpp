@@ -1,0 +1,136 @@
+// bi_plan.cpp -- the (dtype, N, K) recipe table and the launch planner.
+//
+// GateLinear page, sections "What" and "A correction to why the key excludes
+// M": the persistent-matmul config is keyed on (dtype, N[, K]) and never on M,
+// so one config serves every batch size.  Here the key fixes the whole
+// numeric recipe; M only chooses between two kernel shapes that carry out the
+// same recipe bit for bit.
+#include "bi_plan.h"
+
+#include <atomic>
+
+#include <hip/hip_runtime_api.h>
+
+namespace bi {
+
+namespace {
+
+// fp32: tile partials of 128 k (32 instructions of 16x16x4 per partial chain)
+// keep the decode kernel's dependent chain short enough to stream the weight
+// at HBM speed; the persistent kernel pays one fp32 add per 128 k.
+constexpr int kF32BlockK = 128;
+// bf16: one 16x16x32 instruction covers 32 k, so a 512-k partial is a chain
+// of 16 instructions.
+constexpr int kBF16BlockK = 512;
+
+}  // namespace
+
+bi_status_t recipe_for(int32_t dtype, int64_t N, int64_t K, bi_recipe_t* out)
+{
+    if (!out)
+        return BI_EINVAL;
+    if (dtype != BI_F32 && dtype != BI_BF16)
+        return BI_EINVAL;
+    if (N <= 0 || K <= 0)
+        return BI_EUNSUPPORTED;
+    if (N % 16 != 0 || K % 32 != 0 || N > (int64_t(1) << 30) || K > (int64_t(1) << 30))
+        return BI_EUNSUPPORTED;
+    bi_recipe_t r{};
+    r.dtype = dtype;
+    r.k_group = 8;
+    r.reduce = BI_R2_TILE_PARTIAL;
+    r.bias_last = 1;
+    if (dtype == BI_F32) {
+        r.mfma = BI_MFMA_F32_16X16X4_F32;
+        r.block_k = (K % kF32BlockK == 0) ? kF32BlockK : (int32_t)K;
+        r.m_decode_max = 128;
+    } else {
+        r.mfma = BI_MFMA_F32_16X16X32_BF16;
+        r.block_k = (K % kBF16BlockK == 0) ? kBF16BlockK : (int32_t)K;
+        r.m_decode_max = 64;
+    }
+    *out = r;
+    return BI_OK;
+}
+
+bi_status_t recipe_valid(const bi_recipe_t& r, int64_t N, int64_t K)
+{
+    if (r.dtype != BI_F32 && r.dtype != BI_BF16)
+        return BI_EINVAL;
+    const int want_mfma = r.dtype == BI_F32 ? BI_MFMA_F32_16X16X4_F32 : BI_MFMA_F32_16X16X32_BF16;
+    if (r.mfma != want_mfma || r.k_group != 8 || r.reduce != BI_R2_TILE_PARTIAL || r.bias_last != 1)
+        return BI_EUNSUPPORTED;
+    if (N <= 0 || K <= 0 || N % 16 != 0 || K % 32 != 0)
+        return BI_EUNSUPPORTED;
+    if (r.block_k <= 0 || r.block_k % 32 != 0 || K % r.block_k != 0)
+        return BI_EUNSUPPORTED;
+    if (r.m_decode_max < 0)
+        return BI_EINVAL;
+    return BI_OK;
+}
+
+int device_cu_count()
+{
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0)
+        return 256;
+    if (dev < 64) {
+        int v = cache[dev].load(std::memory_order_relaxed);
+        if (v > 0)
+            return v;
+    }
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+        cus = 256;
+    if (dev < 64)
+        cache[dev].store(cus, std::memory_order_relaxed);
+    return cus;
+}
+
+static Tiling persistent_tiling(const bi_recipe_t& r)
+{
+    (void)r;
+    return Tiling{64, 64, 2, 2};
+}
+
+bi_status_t make_plan(const bi_recipe_t& r, int32_t path_req, int64_t M, int64_t N, int64_t K,
+                      Plan* plan)
+{
+    bi_status_t st = recipe_valid(r, N, K);
+    if (st != BI_OK)
+        return st;
+    if (M < 0 || M > (int64_t(1) << 30))
+        return BI_EINVAL;
+    Plan p{};
+    p.recipe = r;
+    p.kbpt = r.block_k / 32;
+    p.tiles_k = (int)(K / r.block_k);
+    p.mtiles = (int)((M + 15) / 16);
+    p.ntiles = (int)(N / 16);
+    p.tiling = persistent_tiling(r);
+    if (path_req == BI_PATH_DECODE)
+        p.path = kPathDecode;
+    else if (path_req == BI_PATH_PERSISTENT)
+        p.path = kPathPersistent;
+    else if (path_req == BI_PATH_AUTO)
+        p.path = (M <= r.m_decode_max) ? kPathDecode : kPathPersistent;
+    else
+        return BI_EINVAL;
+    p.ws_bytes = 0;
+    p.ws_counter_bytes = 0;
+    if (p.path == kPathDecode && p.tiles_k > 1) {
+        // The counter area has the same place and size for every plan, so
+        // calls of different shapes can share one workspace: no plan's
+        // partials ever land where another plan expects a zero counter.
+        const size_t tiles = (size_t)p.mtiles * (size_t)p.ntiles;
+        if (tiles > kMaxDecodeTiles)
+            return BI_EUNSUPPORTED;
+        p.ws_counter_bytes = kWorkspaceCounterBytes;
+        p.ws_bytes = p.ws_counter_bytes + tiles * (size_t)p.tiles_k * 64 * 16;
+    }
+    *plan = p;
+    return BI_OK;
+}
+
+}  // namespace bi

@@ -1,0 +1,50 @@
+// bi_plan.h -- the recipe table and the launch plan (host only).
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "bi.h"
+
+namespace bi {
+
+enum Path { kPathDecode = 1, kPathPersistent = 2 };
+
+// Every workspace starts with this many bytes of 32-bit arrival counters, one
+// per 16x16 output tile of a decode call; partials follow.  Fixed, so that the
+// layout does not depend on the shape of the call.
+constexpr size_t kWorkspaceCounterBytes = 64 * 1024;
+constexpr size_t kMaxDecodeTiles = kWorkspaceCounterBytes / sizeof(uint32_t);
+
+// Persistent-kernel tiling: a workgroup computes a BM x BN output tile with
+// WM x WN waves.  Tiling never changes the numerics.
+struct Tiling {
+    int bm, bn, wm, wn;
+};
+
+struct Plan {
+    bi_recipe_t recipe;
+    int path;
+    int kbpt;        // k blocks (of 32) per tile partial = block_k / 32
+    int tiles_k;     // tile partials per output element = K / block_k
+    int mtiles;      // 16-row tiles of M (decode path)
+    int ntiles;      // 16-column tiles of N (decode path)
+    Tiling tiling;   // persistent path
+    size_t ws_bytes; // workspace the plan needs
+    size_t ws_counter_bytes;
+};
+
+// The recipe of a key -- a pure function of (dtype, N, K).
+bi_status_t recipe_for(int32_t dtype, int64_t N, int64_t K, bi_recipe_t* out);
+
+// Checks a recipe is one the kernels can carry out for this (N, K).
+bi_status_t recipe_valid(const bi_recipe_t& r, int64_t N, int64_t K);
+
+// Picks the kernel path and its shape for M rows.  path_req: BI_PATH_*.
+bi_status_t make_plan(const bi_recipe_t& r, int32_t path_req, int64_t M, int64_t N, int64_t K,
+                      Plan* plan);
+
+// Number of compute units of the current device (cached per device).
+int device_cu_count();
+
+}  // namespace bi

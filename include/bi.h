@@ -1,0 +1,193 @@
+/*
+ * bi.h -- batch-invariant GEMM library for AMD Instinct MI355X (gfx950).
+ *
+ * A batch-invariant linear layer returns, for every row of X, the same bits
+ * whatever the number of rows M it is computed with.  The library gets there
+ * by making the whole reduction recipe -- matrix instruction, which k values
+ * share one instruction and in which slot, the width BLOCK_K of a k tile, and
+ * the order in which the k tiles are added -- a function of (dtype, N, K)
+ * alone.  M only decides which kernel shape carries the recipe out, never the
+ * recipe itself.
+ *
+ * Sources: "[BI][DSv4] Batch-invariant GateLinear router with fp32 persistent
+ * matmul" (sections "What", "Tests", "Review follow-up" and "A correction to
+ * why the key excludes M"), and "Batch-invariance generation with vLLM
+ * fused-MoE backend" ("What's included" and the strict-review summary).
+ *
+ * Conventions shared by every entry point:
+ *  - All tensor pointers are DEVICE pointers on the current HIP device, owned
+ *    by the caller.  The library allocates no device memory, never
+ *    synchronises the host, enqueues its kernels on `stream` and returns.
+ *  - Weights use the nn.Linear layout: W is [N, K] row-major with row pitch
+ *    `ldw` elements, i.e. exactly the memory behind the transposed view
+ *    W.t() ([K, N], strides (1, ldw)) that a linear layer hands to its matmul.
+ *    No other weight layout is accepted.
+ *  - X is [M, K] row-major with row pitch `ldx`; Y is [M, N] row-major with
+ *    row pitch `ldy`.  Base pointers must be 16-byte aligned and row pitches
+ *    must keep every row 16-byte aligned.
+ *  - `ws` is a caller-owned device workspace of at least the size reported by
+ *    the matching *_workspace_size() call (16-byte aligned).  Its first 64 KiB
+ *    hold arrival counters that must be zero before the first call: zero-fill
+ *    the workspace once when it is allocated.  Every call leaves the counters
+ *    at zero again and their place does not depend on the call's shape, so
+ *    one workspace serves calls of any shape in sequence (and can be captured
+ *    in a HIP graph) without clearing.  Two calls that are in flight at the
+ *    same time must not share one workspace.
+ *  - Arguments are validated on the host before anything is enqueued; a
+ *    rejected call enqueues nothing.  There is no fallback to a
+ *    non-invariant path: a shape the recipe table cannot serve returns
+ *    BI_EUNSUPPORTED.  M == 0 returns BI_OK and enqueues nothing.
+ *  - Thread safety: the library has no mutable global state.
+ */
+#ifndef BI_H
+#define BI_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    BI_OK = 0,
+    BI_EINVAL = 1,        /* null/misaligned pointer, negative size, bad pitch   */
+    BI_EUNSUPPORTED = 2,  /* (dtype, N, K) outside what the recipe table serves  */
+    BI_EWORKSPACE = 3,    /* ws missing or smaller than *_workspace_size()       */
+    BI_EHIP = 4           /* a HIP launch failed; see hipGetLastError()         */
+} bi_status_t;
+
+typedef enum { BI_F32 = 0, BI_BF16 = 1 } bi_dtype_t;
+
+/* How the per-element k reduction is carried out.
+ * BI_R2_TILE_PARTIAL: K is cut into tiles of block_k; each tile's partial sum
+ *   is formed from zero by a chain of matrix instructions in ascending k, and
+ *   the tile partials are added into one fp32 accumulator in ascending tile
+ *   order: acc = P_0; acc = acc + P_1; ... .  block_k == K is the fully
+ *   chained recipe (one accumulator threaded through every k block).      */
+typedef enum { BI_R2_TILE_PARTIAL = 2 } bi_reduce_t;
+
+typedef enum {
+    BI_MFMA_F32_16X16X4_F32 = 1,   /* fp32 operands, 4 products per instruction  */
+    BI_MFMA_F32_16X16X32_BF16 = 2  /* bf16 operands, 32 products per instruction */
+} bi_mfma_t;
+
+/* The numeric recipe of a (dtype, N, K) key.  Every field is a function of
+ * the key only; bi_describe_recipe() takes no M, by design. */
+typedef struct {
+    int32_t dtype;          /* bi_dtype_t of the operands                        */
+    int32_t mfma;           /* bi_mfma_t                                         */
+    int32_t k_group;        /* k values per lane slot in one 32-wide k block: 8.
+                               Slot g (g = 0..3) of a block starting at k0 holds
+                               k0+8g .. k0+8g+7; an fp32 instruction s (0..7)
+                               takes element s of each slot, a bf16 instruction
+                               takes all eight.                                  */
+    int32_t reduce;         /* bi_reduce_t                                       */
+    int32_t block_k;        /* width of one tile partial (multiple of 32)        */
+    int32_t bias_last;      /* 1: bias is added once, after the full reduction   */
+    int32_t m_decode_max;   /* largest M served by the k-tile-parallel decode
+                               kernel; larger M uses the persistent kernel.  This
+                               picks a kernel shape, never the numerics.         */
+    int32_t reserved;
+} bi_recipe_t;
+
+/* Y[M,N] = X[M,K] . W^T + bias, all fp32, fp32 accumulation.
+ * GateLinear page, "What": the router GEMM is computed in the input dtype
+ * (fp32) and its scores never round through bf16; bias and skip-bias are
+ * preserved ("Review follow-up").  bias may be NULL (no bias term). */
+bi_status_t bi_linear_f32(const float* x, int64_t ldx,
+                          const float* w, int64_t ldw,
+                          const float* bias,
+                          float* y, int64_t ldy,
+                          int64_t M, int64_t N, int64_t K,
+                          void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Y[M,N] = X[M,K] . W^T + bias with bf16 X and W (uint16 bit patterns), fp32
+ * accumulation, fp32 bias (or NULL), and Y stored as bf16 (round to nearest
+ * even, y_dtype == BI_BF16) or fp32 (y_dtype == BI_F32).  GateLinear page,
+ * "A correction to why the key excludes M": the bf16 path goes through
+ * matrix cores, so its recipe is pinned just as the fp32 one is. */
+bi_status_t bi_linear_bf16(const uint16_t* x, int64_t ldx,
+                           const uint16_t* w, int64_t ldw,
+                           const float* bias,
+                           void* y, int32_t y_dtype, int64_t ldy,
+                           int64_t M, int64_t N, int64_t K,
+                           void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Batch-invariant MoE layer with gated SwiGLU experts (fused-MoE page, "What's
+ * included"; strict-review summary):
+ *   logits = fp32(x) . w_router^T (+ b_router)      fp32 router, recipe of
+ *                                                    key (fp32, E, H)
+ *   topk_ids[m, j]  : j-th largest logit, exact ties to the lower expert index,
+ *                     -0.0 equal to +0.0
+ *   topk_probs[m,j] : softmax over all E logits of the chosen expert (fp32,
+ *                     not renormalised over the top-k)
+ *   h   = bf16( x . w13[e]^T )       w13[e] = [gate rows 0..I-1 ; up rows I..2I-1]
+ *   a   = bf16( silu(gate) * up * p )  fp32 math, one rounding; the routing
+ *                                      probability is applied here
+ *   y_j = a . w2[e]^T                 fp32 accumulation, fp32 partial per slot
+ *   y[m] = fp32( sum_{j = 0..topk-1} (double) y_j )   unit weights, fp64, slot order
+ * Layouts: x [M,H] bf16, w_router [E,H] fp32, b_router [E] fp32 or NULL,
+ * w13 [E, 2I, H] bf16, w2 [E, H, I] bf16 (each expert an nn.Linear weight),
+ * topk_ids [M,topk] int32, topk_probs [M,topk] fp32, y [M,H] fp32; all
+ * contiguous.  Expert counts stay on the device (no host synchronisation).
+ * Requires H % 32 == 0, I % 32 == 0, E <= 1024, topk <= E and topk <= 32. */
+bi_status_t bi_moe_grouped_gemm(const uint16_t* x,
+                                const float* w_router, const float* b_router,
+                                const uint16_t* w13, const uint16_t* w2,
+                                int64_t M, int64_t H, int64_t E, int64_t I, int64_t topk,
+                                int32_t* topk_ids, float* topk_probs, float* y,
+                                void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Workspace bytes the calls above need for a given problem (0 if none). */
+size_t bi_linear_workspace_size(int32_t dtype, int64_t M, int64_t N, int64_t K);
+size_t bi_moe_workspace_size(int64_t M, int64_t H, int64_t E, int64_t I, int64_t topk);
+
+/* The recipe of a key; takes no M.  Returns BI_EUNSUPPORTED for keys the
+ * table cannot serve. */
+bi_status_t bi_describe_recipe(int32_t dtype, int64_t N, int64_t K, bi_recipe_t* out);
+
+/* Static string for a status code. */
+const char* bi_status_str(bi_status_t status);
+
+/* ---------------------------------------------------------------------------
+ * Experiment and control entry points.  Not for production use.
+ * ------------------------------------------------------------------------- */
+
+/* Path selectors for bi_lab_linear(). */
+enum { BI_PATH_AUTO = 0, BI_PATH_DECODE = 1, BI_PATH_PERSISTENT = 2 };
+
+/* The same linear layer with an explicit recipe and an explicit kernel path,
+ * for A/B experiments (e.g. fully chained vs tile-partial, or one BLOCK_K
+ * against another) and for showing that the two kernel paths agree bit for
+ * bit.  Results are batch-invariant only while the recipe is held fixed.
+ * x/w are fp32 or bf16 per recipe->dtype; y is fp32 or bf16 per y_dtype. */
+bi_status_t bi_lab_linear(const void* x, int64_t ldx, const void* w, int64_t ldw,
+                          const float* bias, void* y, int32_t y_dtype, int64_t ldy,
+                          int64_t M, int64_t N, int64_t K,
+                          const bi_recipe_t* recipe, int32_t path,
+                          void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Workspace bytes bi_lab_linear() needs for this recipe, path and shape. */
+size_t bi_lab_workspace_size(const bi_recipe_t* recipe, int32_t path,
+                             int64_t M, int64_t N, int64_t K);
+
+/* Negative control (GateLinear page, "What" and "Tests": the default library
+ * route split K and switched algorithm with M, so a row's scores changed with
+ * the batch).  Same arguments as bi_linear_f32, but BLOCK_K is chosen from M
+ * (twice the shipped width for M < 64, the shipped width otherwise): a
+ * deliberately M-dependent recipe that is expected to break bitwise
+ * invariance.  Its workspace never exceeds bi_linear_workspace_size(). */
+bi_status_t bi_negctl_linear_f32(const float* x, int64_t ldx,
+                                 const float* w, int64_t ldw,
+                                 const float* bias,
+                                 float* y, int64_t ldy,
+                                 int64_t M, int64_t N, int64_t K,
+                                 void* ws, size_t ws_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BI_H */

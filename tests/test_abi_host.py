@@ -1,0 +1,124 @@
+"""The C ABI on the host: exports, validation, error codes, recipe purity.
+
+All checks here run before the library touches the GPU, so they need none.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bi.h")
+
+bi = pytest.importorskip("deterministic_persistent_gemm_amd")
+L = bi.lib()
+
+FAKE = ctypes.c_void_p(0x10000)        # aligned, never dereferenced by validation
+NULL = None
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*[A-Za-z_][\w \*]*?\b(bi_\w+)\s*\(", src, flags=re.M)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert {"bi_linear_f32", "bi_linear_bf16", "bi_moe_grouped_gemm", "bi_describe_recipe",
+            "bi_linear_workspace_size", "bi_moe_workspace_size", "bi_status_str",
+            "bi_lab_linear", "bi_negctl_linear_f32"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), f"{n} declared in bi.h but not exported"
+
+
+def test_describe_recipe_takes_no_m():
+    src = open(HEADER).read()
+    m = re.search(r"bi_status_t bi_describe_recipe\(([^)]*)\)", src)
+    params = [p.strip() for p in m.group(1).split(",")]
+    assert len(params) == 4 and not any(re.search(r"\bM\b", p) for p in params)
+
+
+def test_recipe_is_a_function_of_the_key():
+    r1 = bi.bi_describe_recipe(bi.BI_F32, 256, 4096).as_dict()
+    r2 = bi.bi_describe_recipe(bi.BI_F32, 256, 4096).as_dict()
+    assert r1 == r2
+    assert r1["mfma"] == bi.BI_MFMA_F32_16X16X4_F32 and r1["block_k"] == 128 and r1["bias_last"] == 1
+    rb = bi.bi_describe_recipe(bi.BI_BF16, 4096, 4096).as_dict()
+    assert rb["mfma"] == bi.BI_MFMA_F32_16X16X32_BF16 and 4096 % rb["block_k"] == 0
+    # keys whose K is not a multiple of the tile width fall back to one chain
+    assert bi.bi_describe_recipe(bi.BI_BF16, 2048, 768).block_k == 768
+    assert bi.bi_describe_recipe(bi.BI_F32, 32, 256).block_k == 128
+
+
+@pytest.mark.parametrize("N,K", [(0, 256), (15, 256), (32, 48), (32, 0), (17, 4096)])
+def test_unsupported_keys(N, K):
+    r = bi.Recipe()
+    assert L.bi_describe_recipe(bi.BI_F32, N, K, ctypes.byref(r)) == bi.BI_EUNSUPPORTED
+
+
+def test_unknown_dtype_and_null_out():
+    r = bi.Recipe()
+    assert L.bi_describe_recipe(7, 256, 4096, ctypes.byref(r)) == bi.BI_EINVAL
+    assert L.bi_describe_recipe(bi.BI_F32, 256, 4096, None) == bi.BI_EINVAL
+
+
+def call_f32(x=FAKE, ldx=4096, w=FAKE, ldw=4096, b=NULL, y=FAKE, ldy=256, M=1, N=256, K=4096,
+             ws=NULL, ws_bytes=0):
+    return L.bi_linear_f32(x, ldx, w, ldw, b, y, ldy, M, N, K, ws, ws_bytes, None)
+
+
+def test_m_zero_is_ok_and_enqueues_nothing():
+    assert call_f32(M=0) == bi.BI_OK
+    assert call_f32(M=0, x=NULL, w=NULL, y=NULL) == bi.BI_OK
+
+
+@pytest.mark.parametrize("kw", [dict(x=NULL), dict(w=NULL), dict(y=NULL), dict(M=-1),
+                                dict(ldx=100), dict(ldw=4095), dict(ldy=100),
+                                dict(x=ctypes.c_void_p(0x10004)), dict(w=ctypes.c_void_p(0x10008)),
+                                dict(ldx=4097)])
+def test_invalid_arguments(kw):
+    assert call_f32(**kw) == bi.BI_EINVAL
+
+
+def test_unsupported_shape_is_an_error_not_a_fallback():
+    assert call_f32(N=250, ldy=256) == bi.BI_EUNSUPPORTED
+    assert call_f32(K=4001, ldx=4096, ldw=4096) == bi.BI_EUNSUPPORTED
+
+
+def test_workspace_required_and_sized():
+    need = L.bi_linear_workspace_size(bi.BI_F32, 1, 256, 4096)
+    assert need > 0
+    assert call_f32() == bi.BI_EWORKSPACE
+    assert call_f32(ws=FAKE, ws_bytes=need - 1) == bi.BI_EWORKSPACE
+    # the persistent path keeps its accumulators in registers: no workspace
+    assert L.bi_linear_workspace_size(bi.BI_F32, 4096, 256, 4096) == 0
+    # workspace grows with M on the decode path, never beyond the decode limit
+    sizes = [L.bi_linear_workspace_size(bi.BI_F32, m, 256, 4096) for m in (1, 16, 17, 64, 128)]
+    assert sizes == sorted(sizes)
+
+
+def test_bf16_entry_validation():
+    f = L.bi_linear_bf16
+    assert f(FAKE, 4096, FAKE, 4096, None, FAKE, 5, 4096, 1, 4096, 4096, None, 0, None) == bi.BI_EINVAL
+    assert f(FAKE, 4100, FAKE, 4096, None, FAKE, bi.BI_BF16, 4096, 1, 4096, 4096, None, 0, None) == bi.BI_EINVAL
+    assert f(FAKE, 4096, FAKE, 4096, None, FAKE, bi.BI_BF16, 4096, 0, 4096, 4096, None, 0, None) == bi.BI_OK
+
+
+def test_lab_recipe_validation():
+    r = bi.bi_describe_recipe(bi.BI_F32, 256, 4096)
+    r.block_k = 96                      # does not divide K
+    f = L.bi_lab_linear
+    args = (FAKE, 4096, FAKE, 4096, None, FAKE, bi.BI_F32, 256, 1, 256, 4096)
+    assert f(*args, ctypes.byref(r), bi.BI_PATH_AUTO, None, 0, None) == bi.BI_EUNSUPPORTED
+    r = bi.bi_describe_recipe(bi.BI_F32, 256, 4096)
+    r.mfma = bi.BI_MFMA_F32_16X16X32_BF16   # instruction must match the operand type
+    assert f(*args, ctypes.byref(r), bi.BI_PATH_AUTO, None, 0, None) == bi.BI_EUNSUPPORTED
+    r = bi.bi_describe_recipe(bi.BI_F32, 256, 4096)
+    assert f(*args, ctypes.byref(r), 9, None, 0, None) == bi.BI_EINVAL
+
+
+def test_status_strings():
+    for s in range(5):
+        assert L.bi_status_str(s).startswith(b"BI_")

@@ -1,0 +1,286 @@
+"""fp32 batch-invariant linear on the GPU against the oracle, through the C ABI.
+
+Workloads: the tiny fp32 layer and the DeepSeek-V4-shaped router (decode and
+prefill batch sizes); see workloads.py.  Bars: oracle agreement at atol 2e-3 /
+rtol 1e-4 (GateLinear page, "Tests"), and bitwise equality of every probe row
+across every batch size, batch position and kernel path.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import workloads as wl
+from tests.gpu_util import (F32_ATOL, F32_RTOL, assert_bitwise, assert_close, banner, dev, host,
+                            weight_t)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def bi():
+    import deterministic_persistent_gemm_amd as m
+    return m
+
+
+@pytest.fixture(scope="module")
+def router():
+    w = wl.router_weights(0)
+    return w, dev(w.w), dev(w.b)
+
+
+def run(bi, x_np, w_dev, b_dev, **kw):
+    return host(bi.bi_linear_f32(dev(x_np), weight_t(w_dev), b_dev, **kw))
+
+
+# ----------------------------------------------------------------- tiny fp32
+
+
+def test_tiny_layer_against_oracle_and_invariant(bi):
+    w = wl.tiny_weights(0)
+    wd, bd = dev(w.w), dev(w.b)
+    rows = {}
+    for M in wl.TINY_M_SWEEP:
+        banner(f"tiny fp32 M={M} bi_linear_f32")
+        batch = wl.tiny_batch(M, w)
+        y = run(bi, batch.x, wd, bd)
+        assert_close(y, oracle.linear_f32(batch.x, w.w, w.b), F32_ATOL, F32_RTOL, f"tiny M={M}")
+        rows[M] = y[0]
+    for M in wl.TINY_M_SWEEP:
+        assert_bitwise(rows[M], rows[1], f"tiny probe row, M={M} vs M=1")
+
+
+# ------------------------------------------------------------ router decode
+
+
+def test_router_decode_sweep(bi, router):
+    w, wd, bd = router
+    probe_out = {}
+    worst = 0.0
+    for M in wl.ROUTER_DECODE_M:
+        banner(f"router fp32 decode M={M} bi_linear_f32")
+        batch = wl.router_batch(M, w)
+        y = run(bi, batch.x, wd, bd)
+        ref = oracle.linear_f32(batch.x, w.w, w.b)
+        worst = max(worst, assert_close(y, ref, F32_ATOL, F32_RTOL, f"router M={M}"))
+        for pid, pos in batch.probes.items():
+            for p in pos:
+                probe_out.setdefault(pid, []).append((M, p, y[p]))
+    for pid, outs in probe_out.items():
+        for M, p, row in outs:
+            assert_bitwise(row, outs[0][2], f"probe {pid} at M={M} row {p} vs M={outs[0][0]} row {outs[0][1]}")
+    # the fp64 reference differs from any fp32 order by far less than the bar
+    assert worst < 1e-4, worst
+
+
+def test_router_prefill_rows_match_decode(bi, router):
+    w, wd, bd = router
+    banner("router fp32 M=1 reference row")
+    solo = run(bi, w.probes, wd, bd)
+    for M in wl.ROUTER_PREFILL_M:
+        banner(f"router fp32 prefill M={M} bi_linear_f32")
+        batch = wl.router_batch(M, w, copies=8)
+        y = run(bi, batch.x, wd, bd)
+        for pid, pos in batch.probes.items():
+            assert len(pos) >= 8
+            for p in pos:
+                assert_bitwise(y[p], solo[pid], f"M={M} probe {pid} at row {p}")
+        sample = np.unique(np.concatenate([np.arange(0, M, M // 48), [M - 1], np.arange(60, 70)]))
+        ref = oracle.linear_f32(batch.x[sample], w.w, w.b)
+        assert_close(y[sample], ref, F32_ATOL, F32_RTOL, f"router M={M} sampled rows")
+
+
+def test_both_kernel_paths_agree_bitwise(bi, router):
+    w, wd, bd = router
+    for M in (1, 17, 64, 128, 200):
+        banner(f"router fp32 M={M} decode vs persistent (bi_lab_linear)")
+        batch = wl.router_batch(M, w)
+        x = dev(batch.x)
+        a = host(bi.bi_lab_linear(x, weight_t(wd), bd, path=bi.BI_PATH_DECODE))
+        b = host(bi.bi_lab_linear(x, weight_t(wd), bd, path=bi.BI_PATH_PERSISTENT))
+        assert_bitwise(a, b, f"decode vs persistent at M={M}")
+
+
+def test_repeat_determinism_with_workspace_reuse(bi, router):
+    # alternate two different batches through the same workspace: a stale
+    # partial or a counter left non-zero would change the second result
+    w, wd, bd = router
+    xa = dev(wl.router_batch(16, w).x)
+    xb = dev(wl.router_batch(32, w).x)
+    banner("router fp32 repeat-determinism x10")
+    ya0 = host(bi.bi_linear_f32(xa, weight_t(wd), bd))
+    yb0 = host(bi.bi_linear_f32(xb, weight_t(wd), bd))
+    for i in range(10):
+        assert_bitwise(host(bi.bi_linear_f32(xa, weight_t(wd), bd)), ya0, f"repeat {i} batch a")
+        assert_bitwise(host(bi.bi_linear_f32(xb, weight_t(wd), bd)), yb0, f"repeat {i} batch b")
+
+
+def test_poisoned_tail_rows_and_guard_bands(bi, router):
+    import torch
+    w, wd, bd = router
+    M = 33
+    batch = wl.router_batch(M, w)
+    x_big = np.full((M + 16, wl.ROUTER_K), np.nan, np.float32)
+    x_big[:M] = batch.x
+    xd = dev(x_big)[:M]                        # rows past M hold NaN
+    out_big = torch.full((M + 4, 256 + 32), 12345.0, dtype=torch.float32, device="cuda")
+    out = out_big[2:M + 2, 16:16 + 256]       # strided window with canaries around it
+    banner("router fp32 poisoned tail + guard bands")
+    bi.bi_linear_f32(xd, weight_t(wd), bd, out=out)
+    big = host(out_big)
+    assert np.all(big[:2] == 12345.0) and np.all(big[M + 2:] == 12345.0)
+    assert np.all(big[:, :16] == 12345.0) and np.all(big[:, 16 + 256:] == 12345.0)
+    assert_bitwise(big[2:M + 2, 16:16 + 256], run(bi, batch.x, wd, bd), "strided out vs contiguous")
+
+
+def test_poisoned_workspace_partials(bi, router):
+    # only the counters must start at zero; the partial area is fully written
+    # before it is read, so NaN there must not leak into the result.  Uses its
+    # own workspace through the C ABI.  Layout: 64 KiB of counters, then the
+    # partials.
+    import ctypes
+    import torch
+    w, wd, bd = router
+    M, N, K = 17, 256, 4096
+    batch = wl.router_batch(M, w)
+    ref = run(bi, batch.x, wd, bd)
+    L = bi.lib()
+    need = L.bi_linear_workspace_size(bi.BI_F32, M, N, K)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    counter_bytes = 64 * 1024
+    ws[counter_bytes:].fill_(0xFF)             # 0xFFFFFFFF is a NaN pattern
+    x = dev(batch.x)
+    y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    s = torch.cuda.current_stream()
+    banner("router fp32 NaN-poisoned workspace partials (direct C ABI)")
+    for _ in range(2):
+        st = L.bi_linear_f32(ctypes.c_void_p(x.data_ptr()), K, ctypes.c_void_p(wd.data_ptr()), K,
+                             ctypes.c_void_p(bd.data_ptr()), ctypes.c_void_p(y.data_ptr()), N, M, N, K,
+                             ctypes.c_void_p(ws.data_ptr()), need, ctypes.c_void_p(s.cuda_stream))
+        assert st == bi.BI_OK
+        assert_bitwise(host(y), ref, "after poisoning partials")
+    assert int(ws[:counter_bytes].sum()) == 0, "counters not left at zero"
+
+
+def _abi_f32(bi, x, wd, bd, y, ws):
+    import ctypes
+    import torch
+    M, K = x.shape
+    N = wd.shape[0]
+    return bi.lib().bi_linear_f32(ctypes.c_void_p(x.data_ptr()), K, ctypes.c_void_p(wd.data_ptr()), K,
+                                  ctypes.c_void_p(bd.data_ptr()), ctypes.c_void_p(y.data_ptr()), N, M, N, K,
+                                  ctypes.c_void_p(ws.data_ptr()), ws.numel(),
+                                  ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+
+
+def test_one_workspace_serves_every_shape_in_sequence(bi, router):
+    # regression: the counter area once grew with M, so a small-M call left
+    # partials where a larger-M call expected zero counters
+    import torch
+    w, wd, bd = router
+    seq = (64, 128, 17, 128, 1, 64, 33, 128)
+    need = max(bi.lib().bi_linear_workspace_size(bi.BI_F32, M, 256, 4096) for M in seq)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    for i, M in enumerate(seq):
+        banner(f"shared workspace call {i}: M={M}")
+        batch = wl.router_batch(M, w)
+        x = dev(batch.x)
+        y = torch.empty((M, 256), dtype=torch.float32, device="cuda")
+        fresh = torch.zeros_like(ws)
+        y_ref = torch.empty_like(y)
+        assert _abi_f32(bi, x, wd, bd, y_ref, fresh) == bi.BI_OK
+        assert _abi_f32(bi, x, wd, bd, y, ws) == bi.BI_OK
+        assert_bitwise(host(y), host(y_ref), f"shared workspace, call {i} (M={M})")
+    assert int(ws[:64 * 1024].sum()) == 0
+
+
+# ------------------------------------------------------------- closed forms
+
+
+def test_closed_forms_bitwise(bi):
+    g = np.random.default_rng(31)
+    K = 256
+    x = g.standard_normal((40, K)).astype(np.float32)
+    b = g.standard_normal(K).astype(np.float32)
+    banner("fp32 identity weight")
+    y = run(bi, x, dev(np.eye(K, dtype=np.float32)), dev(b))
+    assert_bitwise(y, x + b, "W = I")
+    perm = g.permutation(K)[:64]
+    wh = np.zeros((64, K), np.float32)
+    wh[np.arange(64), perm] = 1.0
+    banner("fp32 one-hot weight")
+    assert_bitwise(run(bi, x, dev(wh), dev(b[:64])), x[:, perm] + b[:64], "one-hot W")
+    banner("fp32 zero weight")
+    assert_bitwise(run(bi, x, dev(np.zeros((32, K), np.float32)), dev(b[:32])),
+                   np.broadcast_to(b[:32], (40, 32)), "W = 0")
+    xi = g.integers(-8, 9, (70, 512)).astype(np.float32)
+    wi = g.integers(-8, 9, (48, 512)).astype(np.float32)
+    banner("fp32 small-integer exact")
+    assert_bitwise(run(bi, xi, dev(wi), None), (xi.astype(np.int64) @ wi.astype(np.int64).T).astype(np.float32),
+                   "small integers")
+
+
+def test_power_of_two_scaling_bitwise(bi, router):
+    import torch
+    w, wd, bd = router
+    x = wl.router_batch(8, w).x
+    banner("router fp32 power-of-two scaling")
+    y = run(bi, x, wd, bd)
+    y8 = host(bi.bi_linear_f32(dev(x * np.float32(8)), weight_t(wd), bd * 8))
+    assert_bitwise(y8, y * np.float32(8), "y(8x, 8b) == 8 y(x, b)")
+
+
+# --------------------------------------------------------- recipe controls
+
+
+def test_negative_control_breaks_invariance(bi, router):
+    # the same machinery with an M-dependent BLOCK_K must change the probe row
+    # between batch sizes on either side of its switch (GateLinear page,
+    # "Tests": a negative control that actually fails)
+    w, wd, bd = router
+    rows = {}
+    for M in (1, 8, 32, 64, 128):
+        banner(f"negative control M={M}")
+        batch = wl.router_batch(M, w)
+        y = host(bi.bi_negctl_linear_f32(dev(batch.x), weight_t(wd), bd))
+        rows[M] = y[M - 1]                  # probe 2 sits at M-1 for every M
+        assert_close(y, oracle.linear_f32(batch.x, w.w, w.b), F32_ATOL, F32_RTOL, "negctl still accurate")
+    assert np.array_equal(rows[1].view(np.uint32), rows[32].view(np.uint32))
+    assert not np.array_equal(rows[32].view(np.uint32), rows[64].view(np.uint32)), \
+        "negative control failed to break invariance"
+
+
+def test_block_k_is_part_of_the_recipe(bi, router):
+    # tile-partial recipes with different BLOCK_K round differently: the width
+    # is load-bearing and has to stay in the key (GateLinear page, "A
+    # correction to why the key excludes M").  Both stay within the bar.
+    w, wd, bd = router
+    batch = wl.router_batch(64, w)
+    x = dev(batch.x)
+    ref = oracle.linear_f32(batch.x, w.w, w.b)
+    outs = {}
+    for bk in (128, 256, 4096):
+        r = bi.bi_describe_recipe(bi.BI_F32, 256, 4096)
+        r.block_k = bk
+        banner(f"router fp32 lab block_k={bk}")
+        outs[bk] = host(bi.bi_lab_linear(x, weight_t(wd), bd, recipe=r))
+        assert_close(outs[bk], ref, F32_ATOL, F32_RTOL, f"block_k={bk}")
+        dec = host(bi.bi_lab_linear(x, weight_t(wd), bd, recipe=r, path=bi.BI_PATH_DECODE))
+        per = host(bi.bi_lab_linear(x, weight_t(wd), bd, recipe=r, path=bi.BI_PATH_PERSISTENT))
+        assert_bitwise(dec, per, f"paths agree at block_k={bk}")
+    assert not np.array_equal(outs[128].view(np.uint32), outs[256].view(np.uint32))
+    assert not np.array_equal(outs[128].view(np.uint32), outs[4096].view(np.uint32))
+
+
+def test_bf16_roundtrip_control_fails_tolerance(bi, router):
+    # GateLinear page, "What": routing through bf16 must fail the fp32 bar
+    import torch
+    w, wd, bd = router
+    batch = wl.router_batch(128, w)
+    banner("router bf16 round-trip control")
+    xb = dev(batch.x).to(torch.bfloat16)
+    wb = wd.to(torch.bfloat16)
+    y = host(bi.bi_linear_bf16(xb, weight_t(wb), bd, out_dtype=torch.bfloat16).float())
+    ref = oracle.linear_f32(batch.x, w.w, w.b)
+    ratio = np.max(np.abs(y - ref) / (F32_ATOL + F32_RTOL * np.abs(ref)))
+    print(f"bf16 round-trip error / fp32 tolerance = {ratio:.1f}x")
+    assert ratio > 1.0
