@@ -80,15 +80,15 @@ _ws_cache: dict = {}
 
 
 def _workspace(nbytes: int, device: torch.device, stream: torch.cuda.Stream) -> torch.Tensor | None:
-    """Zero-filled, grow-only workspace per (device, stream).  The library
-    leaves its counters at zero after every call, so it is reused as is."""
+    """Grow-only workspace per (device, stream); the library needs it only
+    for intermediate partials, so it is reused as is between calls."""
     if nbytes == 0:
         return None
     key = (device.index, stream.cuda_stream)
     with _ws_lock:
         ws = _ws_cache.get(key)
         if ws is None or ws.numel() < nbytes:
-            ws = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
+            ws = torch.empty(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
             _ws_cache[key] = ws
         return ws
 

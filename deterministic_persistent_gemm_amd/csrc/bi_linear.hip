@@ -50,83 +50,6 @@ __device__ __forceinline__ void store_acc(const LinearArgs& a, int row0, int col
             store_elem(a, row0 + q, col, acc[q]);
 }
 
-// -------------------------------------------------------------------- decode
-
-template <typename OX, typename OW, int CH>
-__global__ __launch_bounds__(64) void k_decode(LinearArgs a, int kbpt, int tiles_k,
-                                               f32x4* __restrict__ partials,
-                                               unsigned* __restrict__ counters)
-{
-    using EX = typename OX::elem;
-    using EW = typename OW::elem;
-    const int lane = threadIdx.x;
-    const int r = lane & 15, g = lane >> 4;
-    const int t = blockIdx.x % tiles_k;
-    const int nt = blockIdx.x / tiles_k;
-    const int mt = blockIdx.y;
-    const int ntiles = a.N >> 4;
-
-    const int64_t kbase = (int64_t)t * kbpt * kKBlock + kSlotLen * g;
-    const EW* wp = reinterpret_cast<const EW*>(a.w) + (int64_t)(nt * 16 + r) * a.ldw + kbase;
-    // rows past M read row M-1 (always valid); their results are never stored
-    const int xrow = min(mt * 16 + r, a.M - 1);
-    const EX* xp = reinterpret_cast<const EX*>(a.x) + (int64_t)xrow * a.ldx + kbase;
-
-    f32x4 P = {0.f, 0.f, 0.f, 0.f};
-    for (int c = 0; c < kbpt; c += CH) {
-        FragOf<OW> wf[CH];
-        FragOf<OX> xf[CH];
-#pragma unroll
-        for (int i = 0; i < CH; ++i)
-            load_frag<OW>(wf[i], wp + (int64_t)(c + i) * kKBlock);
-#pragma unroll
-        for (int i = 0; i < CH; ++i)
-            load_frag<OX>(xf[i], xp + (int64_t)(c + i) * kKBlock);
-        // every load of the chunk is in flight before the first instruction
-        // of the chain waits on one (memory-level parallelism for streaming)
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int i = 0; i < CH; ++i)
-            P = mfma_block(xf[i], wf[i], P);
-    }
-
-    const int row0 = mt * 16 + acc_row(lane, 0);
-    const int col = nt * 16 + acc_col(lane);
-    if (tiles_k == 1) {
-        store_acc(a, row0, col, P);
-        return;
-    }
-
-    // publish this tile partial, then count arrivals for the output tile
-    const int64_t otile = (int64_t)mt * ntiles + nt;
-    f32x4* base = partials + otile * tiles_k * 64;
-    if (row0 < a.M)
-        base[(int64_t)t * 64 + lane] = P;
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-    unsigned prev = 0;
-    if (lane == 0)
-        prev = __hip_atomic_fetch_add(&counters[otile], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    prev = __shfl(prev, 0);
-    if (prev != (unsigned)(tiles_k - 1))
-        return;
-
-    // last arrival: ordered combine acc = P0; acc = acc + P1; ...
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    if (row0 < a.M) {
-        acc = base[lane];
-        for (int u = 1; u < tiles_k; ++u) {
-            const f32x4 p = base[(int64_t)u * 64 + lane];
-            acc = acc + p;
-        }
-    }
-    if (lane == 0)
-        __hip_atomic_store(&counters[otile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    store_acc(a, row0, col, acc);
-}
-
-// ---------------------------------------------------------------- persistent
-
 // s-outer order across the FM x FN tiles keeps eight independent chains in
 // flight; per output element the order is still s = 0..7 within the block.
 template <int FM, int FN>
@@ -151,6 +74,103 @@ __device__ __forceinline__ void mfma_tiles(const Frag<false> (&xf)[FM], const Fr
         for (int fn = 0; fn < FN; ++fn)
             part[fm][fn] = mfma_block(xf[fm], wf[fn], part[fm][fn]);
 }
+
+// -------------------------------------------------------------------- decode
+
+// One wave per (16-column N tile, k tile partial, group of MT 16-row M tiles).
+// The wave loads its slab of W once and runs MT independent chains over it,
+// one per M tile.  With a single k tile (block_k == K) the wave finishes the
+// output itself; otherwise it stores its tile partials, and k_decode_fold
+// adds them up in ascending tile order in a second launch (the kernel
+// boundary makes the partials visible; no device-wide fences or counters).
+template <typename OX, typename OW, int CH, int MT>
+__global__ __launch_bounds__(64) void k_decode(LinearArgs a, int kbpt, int tiles_k, int mtiles,
+                                               f32x4* __restrict__ partials)
+{
+    using EX = typename OX::elem;
+    using EW = typename OW::elem;
+    const int lane = threadIdx.x;
+    const int r = lane & 15, g = lane >> 4;
+    const int t = blockIdx.x % tiles_k;
+    const int nt = blockIdx.x / tiles_k;
+    const int mt0 = blockIdx.y * MT;
+    const int ntiles = a.N >> 4;
+
+    const int64_t kbase = (int64_t)t * kbpt * kKBlock + kSlotLen * g;
+    const EW* wp = reinterpret_cast<const EW*>(a.w) + (int64_t)(nt * 16 + r) * a.ldw + kbase;
+    const EX* xp[MT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+        // rows past M read row M-1 (always valid); their results are never stored
+        const int xrow = min((mt0 + m) * 16 + r, a.M - 1);
+        xp[m] = reinterpret_cast<const EX*>(a.x) + (int64_t)xrow * a.ldx + kbase;
+    }
+
+    f32x4 P[MT][1];
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+        P[m][0] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int c = 0; c < kbpt; c += CH) {
+        FragOf<OW> wf[CH][1];
+        FragOf<OX> xf[CH][MT];
+#pragma unroll
+        for (int i = 0; i < CH; ++i)
+            load_frag<OW>(wf[i][0], wp + (int64_t)(c + i) * kKBlock);
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+#pragma unroll
+            for (int i = 0; i < CH; ++i)
+                load_frag<OX>(xf[i][m], xp[m] + (int64_t)(c + i) * kKBlock);
+        // every load of the chunk is in flight before the first instruction
+        // of the chain waits on one (memory-level parallelism for streaming)
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < CH; ++i)
+            mfma_tiles<MT, 1>(xf[i], wf[i], P);
+    }
+
+    const int col = nt * 16 + acc_col(lane);
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+        const int mt = mt0 + m;
+        const int row0 = mt * 16 + acc_row(lane, 0);
+        if (mt >= mtiles || row0 >= a.M)
+            continue;
+        if (tiles_k == 1)
+            store_acc(a, row0, col, P[m][0]);
+        else
+            partials[(((int64_t)mt * ntiles + nt) * tiles_k + t) * 64 + lane] = P[m][0];
+    }
+}
+
+// Ordered fold of the tile partials: acc = P0; acc = acc + P1; ...; + bias.
+__global__ __launch_bounds__(64) void k_decode_fold(LinearArgs a, int tiles_k,
+                                                    const f32x4* __restrict__ partials)
+{
+    const int lane = threadIdx.x;
+    const int nt = blockIdx.x, mt = blockIdx.y;
+    const int ntiles = a.N >> 4;
+    const int row0 = mt * 16 + acc_row(lane, 0);
+    if (row0 >= a.M)
+        return;
+    const f32x4* p = partials + ((int64_t)mt * ntiles + nt) * tiles_k * 64 + lane;
+    constexpr int kBatch = 16;   // loads in flight per batch
+    f32x4 acc = p[0];
+    for (int u0 = 1; u0 < tiles_k; u0 += kBatch) {
+        f32x4 v[kBatch];
+#pragma unroll
+        for (int i = 0; i < kBatch; ++i)
+            if (u0 + i < tiles_k)
+                v[i] = p[(int64_t)(u0 + i) * 64];
+#pragma unroll
+        for (int i = 0; i < kBatch; ++i)
+            if (u0 + i < tiles_k)
+                acc = acc + v[i];
+    }
+    store_acc(a, row0, nt * 16 + acc_col(lane), acc);
+}
+
+// ---------------------------------------------------------------- persistent
 
 // Stage rows [row0, row0 + ROWS) x one 32-wide k block into LDS with pitch
 // PITCH elements; rows past `rows_valid` read the last valid row.
@@ -242,14 +262,13 @@ __global__ __launch_bounds__(WM * WN * 64) void k_persistent(LinearArgs a, int k
 
 // ------------------------------------------------------------------ launcher
 
-template <typename OX, typename OW>
-static hipError_t launch_decode(const LinearArgs& a, const Plan& p, void* ws, hipStream_t s)
+template <typename OX, typename OW, int MT>
+static hipError_t launch_decode_mt(const LinearArgs& a, const Plan& p, f32x4* partials, hipStream_t s)
 {
-    unsigned* counters = reinterpret_cast<unsigned*>(ws);
-    f32x4* partials = reinterpret_cast<f32x4*>(reinterpret_cast<char*>(ws) + p.ws_counter_bytes);
-    dim3 grid((unsigned)(p.ntiles * p.tiles_k), (unsigned)p.mtiles);
+    dim3 grid((unsigned)(p.ntiles * p.tiles_k), (unsigned)((p.mtiles + MT - 1) / MT));
     const int kbpt = p.kbpt;
-    constexpr int kMaxCH = OX::f32_frag ? 8 : 16;   // register budget per chunk
+    // register budget per chunk of k blocks: W fragments plus MT X fragments
+    constexpr int kMaxCH = (OX::f32_frag ? 8 : 16) / (MT > 2 ? 2 : 1);
     int ch = 1;
     for (int c = kMaxCH; c >= 1; c >>= 1)
         if (kbpt % c == 0) {
@@ -257,12 +276,32 @@ static hipError_t launch_decode(const LinearArgs& a, const Plan& p, void* ws, hi
             break;
         }
     switch (ch) {
-    case 16: k_decode<OX, OW, 16><<<grid, 64, 0, s>>>(a, kbpt, p.tiles_k, partials, counters); break;
-    case 8:  k_decode<OX, OW, 8><<<grid, 64, 0, s>>>(a, kbpt, p.tiles_k, partials, counters); break;
-    case 4:  k_decode<OX, OW, 4><<<grid, 64, 0, s>>>(a, kbpt, p.tiles_k, partials, counters); break;
-    case 2:  k_decode<OX, OW, 2><<<grid, 64, 0, s>>>(a, kbpt, p.tiles_k, partials, counters); break;
-    default: k_decode<OX, OW, 1><<<grid, 64, 0, s>>>(a, kbpt, p.tiles_k, partials, counters); break;
+    case 16: k_decode<OX, OW, 16, MT><<<grid, 64, 0, s>>>(a, kbpt, p.tiles_k, p.mtiles, partials); break;
+    case 8:  k_decode<OX, OW, 8, MT><<<grid, 64, 0, s>>>(a, kbpt, p.tiles_k, p.mtiles, partials); break;
+    case 4:  k_decode<OX, OW, 4, MT><<<grid, 64, 0, s>>>(a, kbpt, p.tiles_k, p.mtiles, partials); break;
+    case 2:  k_decode<OX, OW, 2, MT><<<grid, 64, 0, s>>>(a, kbpt, p.tiles_k, p.mtiles, partials); break;
+    default: k_decode<OX, OW, 1, MT><<<grid, 64, 0, s>>>(a, kbpt, p.tiles_k, p.mtiles, partials); break;
     }
+    return hipGetLastError();
+}
+
+template <typename OX, typename OW>
+static hipError_t launch_decode(const LinearArgs& a, const Plan& p, void* ws, hipStream_t s)
+{
+    f32x4* partials = reinterpret_cast<f32x4*>(ws);
+    hipError_t e;
+    // M tiles per wave: keep >= ~1024 waves in flight while reusing each
+    // wave's W fragments across as many M tiles as that allows
+    const int waves1 = p.ntiles * p.tiles_k * p.mtiles;
+    if (p.mtiles >= 4 && waves1 >= 4 * 2048)
+        e = launch_decode_mt<OX, OW, 4>(a, p, partials, s);
+    else if (p.mtiles >= 2 && waves1 >= 2 * 2048)
+        e = launch_decode_mt<OX, OW, 2>(a, p, partials, s);
+    else
+        e = launch_decode_mt<OX, OW, 1>(a, p, partials, s);
+    if (e != hipSuccess || p.tiles_k == 1)
+        return e;
+    k_decode_fold<<<dim3((unsigned)p.ntiles, (unsigned)p.mtiles), 64, 0, s>>>(a, p.tiles_k, partials);
     return hipGetLastError();
 }
 

@@ -118,17 +118,8 @@ bi_status_t make_plan(const bi_recipe_t& r, int32_t path_req, int64_t M, int64_t
     else
         return BI_EINVAL;
     p.ws_bytes = 0;
-    p.ws_counter_bytes = 0;
-    if (p.path == kPathDecode && p.tiles_k > 1) {
-        // The counter area has the same place and size for every plan, so
-        // calls of different shapes can share one workspace: no plan's
-        // partials ever land where another plan expects a zero counter.
-        const size_t tiles = (size_t)p.mtiles * (size_t)p.ntiles;
-        if (tiles > kMaxDecodeTiles)
-            return BI_EUNSUPPORTED;
-        p.ws_counter_bytes = kWorkspaceCounterBytes;
-        p.ws_bytes = p.ws_counter_bytes + tiles * (size_t)p.tiles_k * 64 * 16;
-    }
+    if (p.path == kPathDecode && p.tiles_k > 1)
+        p.ws_bytes = (size_t)p.mtiles * (size_t)p.ntiles * (size_t)p.tiles_k * 64 * 16;
     *plan = p;
     return BI_OK;
 }

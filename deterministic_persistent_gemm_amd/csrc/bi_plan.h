@@ -10,12 +10,6 @@ namespace bi {
 
 enum Path { kPathDecode = 1, kPathPersistent = 2 };
 
-// Every workspace starts with this many bytes of 32-bit arrival counters, one
-// per 16x16 output tile of a decode call; partials follow.  Fixed, so that the
-// layout does not depend on the shape of the call.
-constexpr size_t kWorkspaceCounterBytes = 64 * 1024;
-constexpr size_t kMaxDecodeTiles = kWorkspaceCounterBytes / sizeof(uint32_t);
-
 // Persistent-kernel tiling: a workgroup computes a BM x BN output tile with
 // WM x WN waves.  Tiling never changes the numerics.
 struct Tiling {
@@ -30,8 +24,7 @@ struct Plan {
     int mtiles;      // 16-row tiles of M (decode path)
     int ntiles;      // 16-column tiles of N (decode path)
     Tiling tiling;   // persistent path
-    size_t ws_bytes; // workspace the plan needs
-    size_t ws_counter_bytes;
+    size_t ws_bytes; // workspace the plan needs (decode tile partials)
 };
 
 // The recipe of a key -- a pure function of (dtype, N, K).

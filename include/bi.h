@@ -26,13 +26,11 @@
  *    row pitch `ldy`.  Base pointers must be 16-byte aligned and row pitches
  *    must keep every row 16-byte aligned.
  *  - `ws` is a caller-owned device workspace of at least the size reported by
- *    the matching *_workspace_size() call (16-byte aligned).  Its first 64 KiB
- *    hold arrival counters that must be zero before the first call: zero-fill
- *    the workspace once when it is allocated.  Every call leaves the counters
- *    at zero again and their place does not depend on the call's shape, so
- *    one workspace serves calls of any shape in sequence (and can be captured
- *    in a HIP graph) without clearing.  Two calls that are in flight at the
- *    same time must not share one workspace.
+ *    the matching *_workspace_size() call (16-byte aligned; NULL when that
+ *    size is 0).  It holds intermediate tile partials only: it needs no
+ *    initialisation, every byte a call reads it has written earlier in the
+ *    same call, and one workspace serves calls of any shape in sequence.  Two
+ *    calls that are in flight at the same time must not share one workspace.
  *  - Arguments are validated on the host before anything is enqueued; a
  *    rejected call enqueues nothing.  There is no fallback to a
  *    non-invariant path: a shape the recipe table cannot serve returns

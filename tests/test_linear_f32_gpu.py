@@ -132,11 +132,10 @@ def test_poisoned_tail_rows_and_guard_bands(bi, router):
     assert_bitwise(big[2:M + 2, 16:16 + 256], run(bi, batch.x, wd, bd), "strided out vs contiguous")
 
 
-def test_poisoned_workspace_partials(bi, router):
-    # only the counters must start at zero; the partial area is fully written
-    # before it is read, so NaN there must not leak into the result.  Uses its
-    # own workspace through the C ABI.  Layout: 64 KiB of counters, then the
-    # partials.
+def test_poisoned_workspace(bi, router):
+    # the workspace needs no initialisation: every partial is written before
+    # it is read in the same call, so NaN left there must not leak into the
+    # result.  Uses its own workspace through the C ABI.
     import ctypes
     import torch
     w, wd, bd = router
@@ -145,20 +144,17 @@ def test_poisoned_workspace_partials(bi, router):
     ref = run(bi, batch.x, wd, bd)
     L = bi.lib()
     need = L.bi_linear_workspace_size(bi.BI_F32, M, N, K)
-    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
-    counter_bytes = 64 * 1024
-    ws[counter_bytes:].fill_(0xFF)             # 0xFFFFFFFF is a NaN pattern
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda")   # 0xFFFFFFFF is a NaN
     x = dev(batch.x)
     y = torch.empty((M, N), dtype=torch.float32, device="cuda")
     s = torch.cuda.current_stream()
-    banner("router fp32 NaN-poisoned workspace partials (direct C ABI)")
+    banner("router fp32 NaN-poisoned workspace (direct C ABI)")
     for _ in range(2):
         st = L.bi_linear_f32(ctypes.c_void_p(x.data_ptr()), K, ctypes.c_void_p(wd.data_ptr()), K,
                              ctypes.c_void_p(bd.data_ptr()), ctypes.c_void_p(y.data_ptr()), N, M, N, K,
                              ctypes.c_void_p(ws.data_ptr()), need, ctypes.c_void_p(s.cuda_stream))
         assert st == bi.BI_OK
-        assert_bitwise(host(y), ref, "after poisoning partials")
-    assert int(ws[:counter_bytes].sum()) == 0, "counters not left at zero"
+        assert_bitwise(host(y), ref, "after poisoning the workspace")
 
 
 def _abi_f32(bi, x, wd, bd, y, ws):
@@ -173,8 +169,8 @@ def _abi_f32(bi, x, wd, bd, y, ws):
 
 
 def test_one_workspace_serves_every_shape_in_sequence(bi, router):
-    # regression: the counter area once grew with M, so a small-M call left
-    # partials where a larger-M call expected zero counters
+    # calls of different shapes in sequence through one workspace (an early
+    # layout let a small-M call leave data a larger-M call misread)
     import torch
     w, wd, bd = router
     seq = (64, 128, 17, 128, 1, 64, 33, 128)
@@ -190,7 +186,6 @@ def test_one_workspace_serves_every_shape_in_sequence(bi, router):
         assert _abi_f32(bi, x, wd, bd, y_ref, fresh) == bi.BI_OK
         assert _abi_f32(bi, x, wd, bd, y, ws) == bi.BI_OK
         assert_bitwise(host(y), host(y_ref), f"shared workspace, call {i} (M={M})")
-    assert int(ws[:64 * 1024].sum()) == 0
 
 
 # ------------------------------------------------------------- closed forms
