@@ -120,6 +120,31 @@ __device__ __forceinline__ f32x4 mfma_block(const Frag<false>& a, const Frag<fal
                                                    __builtin_bit_cast(bf16x8, b.v), acc, 0, 0, 0);
 }
 
+// s-outer order across the FM x FN tiles keeps eight independent chains in
+// flight; per output element the order is still s = 0..7 within the block.
+template <int FM, int FN>
+__device__ __forceinline__ void mfma_tiles(const Frag<true> (&xf)[FM], const Frag<true> (&wf)[FN],
+                                           f32x4 (&part)[FM][FN])
+{
+#define BI_STEP(S)                                                            \
+    _Pragma("unroll") for (int fm = 0; fm < FM; ++fm)                         \
+        _Pragma("unroll") for (int fn = 0; fn < FN; ++fn)                     \
+            part[fm][fn] = mfma_f32_step<S>(xf[fm], wf[fn], part[fm][fn]);
+    BI_STEP(0) BI_STEP(1) BI_STEP(2) BI_STEP(3) BI_STEP(4) BI_STEP(5) BI_STEP(6) BI_STEP(7)
+#undef BI_STEP
+}
+
+template <int FM, int FN>
+__device__ __forceinline__ void mfma_tiles(const Frag<false> (&xf)[FM], const Frag<false> (&wf)[FN],
+                                           f32x4 (&part)[FM][FN])
+{
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn)
+            part[fm][fn] = mfma_block(xf[fm], wf[fn], part[fm][fn]);
+}
+
 // fp32 -> bf16, round to nearest even; NaN stays a quiet NaN.
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f)
 {

@@ -1,0 +1,146 @@
+"""Batch-invariant MoE layer on the GPU against the oracle, through the C ABI.
+
+Workload: Qwen3-30B-A3B-shaped layer -- hidden 2048, 128 experts, top-8 fp32
+softmax router, gated SwiGLU experts with intermediate 768, bf16 weights
+~ N(0,0.02) -- at M in {1,16,64,256} (workloads.py).
+
+Bars:
+* expert ids: the oracle's top-k rule applied to the GPU's own fp32 router
+  logits reproduces the GPU ids bit for bit for every token; against the
+  oracle's own logits, ids match bit for bit wherever the oracle's 8th/9th
+  gap exceeds TAU (near ties may legitimately resolve either way; they are
+  listed and checked stage-wise);
+* probabilities: rtol 1e-5 against the oracle's softmax of the same ids;
+* outputs: rtol 1e-2, atol 1e-3 * rms against the oracle re-run with the
+  GPU's ids (bf16 storage points may round one ulp apart);
+* probe tokens: ids, probs and outputs bitwise equal across every M.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import workloads as wl
+from tests.gpu_util import assert_bitwise, assert_close, banner, bf16_to_f32, dev, host, weight_t
+
+pytestmark = pytest.mark.gpu
+
+TAU = 1e-4
+
+
+@pytest.fixture(scope="module")
+def bi():
+    import deterministic_persistent_gemm_amd as m
+    return m
+
+
+@pytest.fixture(scope="module")
+def moe():
+    w = wl.moe_weights(0)
+    d = dict(wr=dev(w.w_router), w13=dev(w.w13), w2=dev(w.w2))
+    return w, d
+
+
+def run_moe(bi, x_np, d, topk=wl.MOE_TOPK, b_router=None):
+    y, ids, probs = bi.bi_moe_grouped_gemm(dev(x_np), d["wr"], b_router, d["w13"], d["w2"], topk)
+    return host(y), host(ids), host(probs)
+
+
+def gpu_logits(bi, x_np, d):
+    xf = dev(bf16_to_f32(x_np))
+    return host(bi.bi_linear_f32(xf, weight_t(d["wr"]), None))
+
+
+def sample_rows(M, probes):
+    rows = set(range(M)) if M <= 64 else set(range(0, M, 8)) | {M - 1}
+    for pos in probes.values():
+        rows |= set(pos)
+    return np.array(sorted(rows))
+
+
+def test_moe_sweep_against_oracle_and_invariant(bi, moe):
+    w, d = moe
+    probe_out = {}
+    near_ties = 0
+    for M in wl.MOE_M_SWEEP:
+        banner(f"moe Qwen3-shape M={M} bi_moe_grouped_gemm")
+        batch = wl.moe_batch(M, w)
+        y, ids, probs = run_moe(bi, batch.x, d)
+        assert ids.min() >= 0 and ids.max() < wl.MOE_E
+        # stage-wise: the top-k rule on the GPU's own logits gives the GPU ids
+        banner(f"moe M={M} router logits via bi_linear_f32")
+        lg = gpu_logits(bi, batch.x, d)
+        np.testing.assert_array_equal(oracle.topk(lg, wl.MOE_TOPK), ids)
+        rows = sample_rows(M, batch.probes)
+        xs = batch.x[rows]
+        yo, ido, po, lo = oracle.moe(xs, w.w_router, None, w.w13, w.w2, wl.MOE_TOPK)
+        srt = np.sort(lo.astype(np.float64), axis=1)[:, ::-1]
+        gap = srt[:, wl.MOE_TOPK - 1] - srt[:, wl.MOE_TOPK]
+        clear = gap > TAU
+        near_ties += int((~clear).sum())
+        np.testing.assert_array_equal(ids[rows][clear], ido[clear])
+        assert_close(lg[rows], lo, 2e-5, 1e-5, f"router logits M={M}")
+        # outputs and probabilities against the oracle run with the GPU ids
+        yf, _, pf, _ = oracle.moe(xs, w.w_router, None, w.w13, w.w2, wl.MOE_TOPK, ids=ids[rows])
+        assert_close(probs[rows], pf, 0.0, 1e-5, f"probs M={M}")
+        rms = float(np.sqrt(np.mean(yf.astype(np.float64) ** 2)))
+        err = assert_close(y[rows], yf, 1e-3 * rms, 1e-2, f"moe out M={M}")
+        print(f"M={M}: rms(out)={rms:.3e} max|err|={err:.2e} near-tie tokens={int((~clear).sum())}")
+        for pid, pos in batch.probes.items():
+            for p in pos:
+                probe_out.setdefault(pid, []).append((M, p, y[p], ids[p], probs[p]))
+    for pid, outs in probe_out.items():
+        M0, p0, y0, i0, q0 = outs[0]
+        for M, p, yy, ii, qq in outs:
+            assert_bitwise(yy, y0, f"moe probe {pid} y at M={M} row {p}")
+            np.testing.assert_array_equal(ii, i0)
+            assert_bitwise(qq, q0, f"moe probe {pid} probs at M={M}")
+
+
+def test_moe_repeat_and_poisoned_workspace(bi, moe):
+    import torch
+    w, d = moe
+    batch = wl.moe_batch(64, w)
+    banner("moe M=64 repeat + poisoned workspace")
+    y0, i0, p0 = run_moe(bi, batch.x, d)
+    s = torch.cuda.current_stream()
+    ws = bi._ws_cache[(torch.cuda.current_device(), s.cuda_stream)]
+    ws.fill_(0xFF)
+    y1, i1, p1 = run_moe(bi, batch.x, d)
+    assert_bitwise(y1, y0, "after poisoning the workspace")
+    np.testing.assert_array_equal(i1, i0)
+    assert_bitwise(p1, p0, "probs after poisoning")
+
+
+def test_moe_zero_router_and_zero_down_projection(bi, moe):
+    import torch
+    w, d = moe
+    batch = wl.moe_batch(16, w)
+    banner("moe zero router")
+    zr = torch.zeros_like(d["wr"])
+    dz = dict(d, wr=zr)
+    y, ids, probs = run_moe(bi, batch.x, dz)
+    np.testing.assert_array_equal(ids, np.tile(np.arange(8, dtype=np.int32), (16, 1)))
+    assert np.all(probs == np.float32(1.0 / 128.0))
+    yo, _, _, _ = oracle.moe(batch.x[:4], np.zeros_like(w.w_router), None, w.w13, w.w2, 8)
+    rms = float(np.sqrt(np.mean(yo.astype(np.float64) ** 2)))
+    assert_close(y[:4], yo, 1e-3 * rms, 1e-2, "zero-router outputs")
+    banner("moe zero down projection")
+    y2, _, _ = run_moe(bi, batch.x, dict(d, w2=torch.zeros_like(d["w2"])))
+    assert np.all(y2 == 0.0)
+
+
+def test_moe_small_shape_full_oracle(bi):
+    # a small layer, every token checked, with a router bias and ragged M
+    w = wl.moe_weights(5, H=256, E=32, I=64)
+    b = (np.random.default_rng(9).standard_normal(32) * 0.05).astype(np.float32)
+    d = dict(wr=dev(w.w_router), w13=dev(w.w13), w2=dev(w.w2))
+    for M in (1, 5, 70):
+        banner(f"moe small H=256 E=32 I=64 topk=4 M={M}")
+        x = wl.moe_batch(M, w).x
+        y, ids, probs = run_moe(bi, x, d, topk=4, b_router=dev(b))
+        lg = host(bi.bi_linear_f32(dev(bf16_to_f32(x)), weight_t(d["wr"]), dev(b)))
+        np.testing.assert_array_equal(oracle.topk(lg, 4), ids)
+        yf, _, pf, _ = oracle.moe(x, w.w_router, b, w.w13, w.w2, 4, ids=ids)
+        assert_close(probs, pf, 0.0, 1e-5, f"small probs M={M}")
+        rms = float(np.sqrt(np.mean(yf.astype(np.float64) ** 2)))
+        assert_close(y, yf, 1e-3 * rms, 1e-2, f"small moe M={M}")
