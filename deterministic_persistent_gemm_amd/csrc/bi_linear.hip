@@ -119,6 +119,8 @@ __global__ __launch_bounds__(64) void k_decode(LinearArgs a, int kbpt, int tiles
 }
 
 // Ordered fold of the tile partials: acc = P0; acc = acc + P1; ...; + bias.
+// Up to 32 partials are requested at once, so the usual case is a single
+// memory round trip.
 __global__ __launch_bounds__(64) void k_decode_fold(LinearArgs a, int tiles_k,
                                                     const f32x4* __restrict__ partials)
 {
@@ -129,101 +131,161 @@ __global__ __launch_bounds__(64) void k_decode_fold(LinearArgs a, int tiles_k,
     if (row0 >= a.M)
         return;
     const f32x4* p = partials + ((int64_t)mt * ntiles + nt) * tiles_k * 64 + lane;
-    constexpr int kBatch = 16;   // loads in flight per batch
-    f32x4 acc = p[0];
-    for (int u0 = 1; u0 < tiles_k; u0 += kBatch) {
+    constexpr int kBatch = 32;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int u0 = 0; u0 < tiles_k; u0 += kBatch) {
+        const int n = min(kBatch, tiles_k - u0);
         f32x4 v[kBatch];
 #pragma unroll
         for (int i = 0; i < kBatch; ++i)
-            if (u0 + i < tiles_k)
+            if (i < n)
                 v[i] = p[(int64_t)(u0 + i) * 64];
 #pragma unroll
         for (int i = 0; i < kBatch; ++i)
-            if (u0 + i < tiles_k)
-                acc = acc + v[i];
+            if (i < n)
+                acc = (u0 + i == 0) ? v[i] : acc + v[i];
     }
     store_acc(a, row0, nt * 16 + acc_col(lane), acc);
 }
 
-// ---------------------------------------------------------------- persistent
+// One LDS stage holds KBS k blocks of BM rows of X and BN rows of W.  Each
+// thread moves whole 16-byte chunks: consecutive threads take consecutive
+// chunks of a row, so a row segment is read with coalesced 16-byte loads.
+// Rows are padded by 16 bytes in LDS, which spreads the 16 rows a fragment
+// read touches over distinct banks.
+template <typename E, int ROWS, int KS, int NT>
+struct Stager {
+    static constexpr int kPer16 = 16 / (int)sizeof(E);
+    static constexpr int kChunks = KS / kPer16;          // 16-byte chunks per row
+    static constexpr int kPitch = KS + kPer16;           // LDS row pitch, elements
+    static constexpr int kTotal = ROWS * kChunks;
+    static constexpr int kPerThread = (kTotal + NT - 1) / NT;
 
-// Stage rows [row0, row0 + ROWS) x one 32-wide k block into LDS with pitch
-// PITCH elements; rows past `rows_valid` read the last valid row.
-template <typename E, int ROWS, int PITCH, int NT>
-__device__ __forceinline__ void stage_block(E* __restrict__ lds, const E* __restrict__ g, int64_t ld,
-                                            int row0, int rows_valid, int64_t k0, int tid)
-{
-    constexpr int kPer16 = 16 / (int)sizeof(E);
-    constexpr int kChunks = kKBlock / kPer16;           // 16-byte chunks per row
-    constexpr int kTotal = ROWS * kChunks;
+    // rows past rows_valid read the last valid row (never stored)
+    __device__ __forceinline__ static void load(u32x4 (&v)[kPerThread], const E* __restrict__ g, int64_t ld,
+                                                int row0, int rows_valid, int64_t k0, int tid)
+    {
 #pragma unroll
-    for (int i = tid; i < kTotal; i += NT) {
-        const int row = i / kChunks, c = i % kChunks;
-        const int grow = min(row0 + row, rows_valid - 1);
-        const u32x4 v = *reinterpret_cast<const u32x4*>(g + (int64_t)grow * ld + k0 + c * kPer16);
-        *reinterpret_cast<u32x4*>(lds + row * PITCH + c * kPer16) = v;
+        for (int j = 0; j < kPerThread; ++j) {
+            const int i = tid + j * NT;
+            if (kTotal % NT != 0 && i >= kTotal)
+                break;
+            const int row = i / kChunks, c = i % kChunks;
+            const int grow = min(row0 + row, rows_valid - 1);
+            v[j] = *reinterpret_cast<const u32x4*>(g + (int64_t)grow * ld + k0 + c * kPer16);
+        }
     }
+    __device__ __forceinline__ static void store(E* __restrict__ lds, const u32x4 (&v)[kPerThread], int tid)
+    {
+#pragma unroll
+        for (int j = 0; j < kPerThread; ++j) {
+            const int i = tid + j * NT;
+            if (kTotal % NT != 0 && i >= kTotal)
+                break;
+            const int row = i / kChunks, c = i % kChunks;
+            *reinterpret_cast<u32x4*>(lds + row * kPitch + c * kPer16) = v[j];
+        }
+    }
+};
+
+// Tiles are taken in an order that gives each of the 8 XCDs (workgroup w
+// runs on XCD w % 8) a contiguous block of row-major tiles, so the N tiles
+// that share rows of X sit behind the same L2.
+__device__ __forceinline__ int xcd_tile(int it, int tiles, int grid)
+{
+    if (grid != tiles || (tiles & 7) != 0)
+        return it;
+    return (it & 7) * (tiles >> 3) + (it >> 3);
 }
 
-template <typename OX, typename OW, int BM, int BN, int WM, int WN>
+template <typename OX, typename OW, int BM, int BN, int WM, int WN, int KBS>
 __global__ __launch_bounds__(WM * WN * 64) void k_persistent(LinearArgs a, int kbpt, int tiles_m, int tiles_n)
 {
     using EX = typename OX::elem;
     using EW = typename OW::elem;
     constexpr int NT = WM * WN * 64;
     constexpr int FM = BM / (WM * 16), FN = BN / (WN * 16);
-    constexpr int XP = kKBlock + 16 / (int)sizeof(EX);   // pitch, elements (16 B pad)
-    constexpr int WP = kKBlock + 16 / (int)sizeof(EW);
-    __shared__ __attribute__((aligned(16))) EX sx[BM * XP];
-    __shared__ __attribute__((aligned(16))) EW sw[BN * WP];
+    constexpr int KS = KBS * kKBlock;
+    using SX = Stager<EX, BM, KS, NT>;
+    using SW = Stager<EW, BN, KS, NT>;
+    __shared__ __attribute__((aligned(16))) EX sx[2][BM * SX::kPitch];
+    __shared__ __attribute__((aligned(16))) EW sw[2][BN * SW::kPitch];
 
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     const int wm = wid / WN, wn = wid % WN;
     const int r = lane & 15, g = lane >> 4;
-    const int nkb = a.K / kKBlock;
+    const int nstages = a.K / KS;
+    const int tiles = tiles_m * tiles_n;
     const EX* xg = reinterpret_cast<const EX*>(a.x);
     const EW* wg = reinterpret_cast<const EW*>(a.w);
 
-    for (int tile = blockIdx.x; tile < tiles_m * tiles_n; tile += gridDim.x) {
+    for (int it = blockIdx.x; it < tiles; it += gridDim.x) {
+        const int tile = xcd_tile(it, tiles, gridDim.x);
         const int tm = tile / tiles_n, tn = tile % tiles_n;
         const int m0 = tm * BM, n0 = tn * BN;
         f32x4 acc[FM][FN], part[FM][FN];
 #pragma unroll
         for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
-            for (int fn = 0; fn < FN; ++fn)
+            for (int fn = 0; fn < FN; ++fn) {
                 acc[fm][fn] = f32x4{0.f, 0.f, 0.f, 0.f};
+                part[fm][fn] = acc[fm][fn];
+            }
 
-        for (int kb = 0; kb < nkb; ++kb) {
-            if (kb % kbpt == 0) {
+        // prologue: stage 0 in LDS, stage 1 in flight in registers
+        u32x4 rx[SX::kPerThread], rw[SW::kPerThread];
+        SX::load(rx, xg, a.ldx, m0, a.M, 0, tid);
+        SW::load(rw, wg, a.ldw, n0, a.N, 0, tid);
+        SX::store(sx[0], rx, tid);
+        SW::store(sw[0], rw, tid);
+        if (nstages > 1) {
+            SX::load(rx, xg, a.ldx, m0, a.M, KS, tid);
+            SW::load(rw, wg, a.ldw, n0, a.N, KS, tid);
+        }
+        __syncthreads();
+
+        for (int st = 0; st < nstages; ++st) {
+            const int buf = st & 1;
+#pragma unroll
+            for (int kbl = 0; kbl < KBS; ++kbl) {
+                const int kb = st * KBS + kbl;
+                if (kb % kbpt == 0) {
+#pragma unroll
+                    for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+                        for (int fn = 0; fn < FN; ++fn)
+                            part[fm][fn] = f32x4{0.f, 0.f, 0.f, 0.f};
+                }
+                FragOf<OX> xf[FM];
+                FragOf<OW> wf[FN];
 #pragma unroll
                 for (int fm = 0; fm < FM; ++fm)
+                    load_frag<OX>(xf[fm], sx[buf] + (wm * FM * 16 + fm * 16 + r) * SX::kPitch + kbl * kKBlock +
+                                              kSlotLen * g);
 #pragma unroll
-                    for (int fn = 0; fn < FN; ++fn)
-                        part[fm][fn] = f32x4{0.f, 0.f, 0.f, 0.f};
+                for (int fn = 0; fn < FN; ++fn)
+                    load_frag<OW>(wf[fn], sw[buf] + (wn * FN * 16 + fn * 16 + r) * SW::kPitch + kbl * kKBlock +
+                                              kSlotLen * g);
+                mfma_tiles<FM, FN>(xf, wf, part);
+                if (kb % kbpt == kbpt - 1) {
+                    const bool first = kb < kbpt;
+#pragma unroll
+                    for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+                        for (int fn = 0; fn < FN; ++fn)
+                            acc[fm][fn] = first ? part[fm][fn] : acc[fm][fn] + part[fm][fn];
+                }
             }
-            const int64_t k0 = (int64_t)kb * kKBlock;
-            stage_block<EX, BM, XP, NT>(sx, xg, a.ldx, m0, a.M, k0, tid);
-            stage_block<EW, BN, WP, NT>(sw, wg, a.ldw, n0, a.N, k0, tid);
-            __syncthreads();
-            FragOf<OX> xf[FM];
-            FragOf<OW> wf[FN];
-#pragma unroll
-            for (int fm = 0; fm < FM; ++fm)
-                load_frag<OX>(xf[fm], sx + (wm * FM * 16 + fm * 16 + r) * XP + kSlotLen * g);
-#pragma unroll
-            for (int fn = 0; fn < FN; ++fn)
-                load_frag<OW>(wf[fn], sw + (wn * FN * 16 + fn * 16 + r) * WP + kSlotLen * g);
-            __syncthreads();
-            mfma_tiles<FM, FN>(xf, wf, part);
-            if (kb % kbpt == kbpt - 1) {
-                const bool first = kb < kbpt;
-#pragma unroll
-                for (int fm = 0; fm < FM; ++fm)
-#pragma unroll
-                    for (int fn = 0; fn < FN; ++fn)
-                        acc[fm][fn] = first ? part[fm][fn] : acc[fm][fn] + part[fm][fn];
+            // the other buffer was last read before the previous barrier
+            if (st + 1 < nstages) {
+                SX::store(sx[buf ^ 1], rx, tid);
+                SW::store(sw[buf ^ 1], rw, tid);
             }
+            if (st + 2 < nstages) {
+                SX::load(rx, xg, a.ldx, m0, a.M, (int64_t)(st + 2) * KS, tid);
+                SW::load(rw, wg, a.ldw, n0, a.N, (int64_t)(st + 2) * KS, tid);
+            }
+            __syncthreads();
         }
 
 #pragma unroll
@@ -280,16 +342,67 @@ static hipError_t launch_decode(const LinearArgs& a, const Plan& p, void* ws, hi
     return hipGetLastError();
 }
 
-template <typename OX, typename OW>
-static hipError_t launch_persistent(const LinearArgs& a, const Plan& p, hipStream_t s)
+template <typename OX, typename OW, int BM, int BN, int WM, int WN, int KBS>
+static hipError_t launch_persistent_t(const LinearArgs& a, const Plan& p, hipStream_t s)
 {
-    constexpr int BM = 64, BN = 64, WM = 2, WN = 2;
+    // the k loop walks whole stages: K must be a multiple of the stage width
+    if (a.K % (KBS * kKBlock) != 0)
+        return hipErrorInvalidValue;
     const int tiles_m = (a.M + BM - 1) / BM;
     const int tiles_n = (a.N + BN - 1) / BN;
     const int tiles = tiles_m * tiles_n;
     const int grid = min(tiles, device_cu_count() * 2);
-    k_persistent<OX, OW, BM, BN, WM, WN><<<grid, WM * WN * 64, 0, s>>>(a, p.kbpt, tiles_m, tiles_n);
+    k_persistent<OX, OW, BM, BN, WM, WN, KBS><<<grid, WM * WN * 64, 0, s>>>(a, p.kbpt, tiles_m, tiles_n);
     return hipGetLastError();
+}
+
+// Persistent tile shapes (BM x BN, waves WM x WN, k blocks per LDS stage).
+// Code 0 picks automatically: the largest tile that still gives every compute
+// unit a tile.  Tiling never changes the numerics, only the speed.
+template <typename OX, typename OW>
+static hipError_t launch_persistent(const LinearArgs& a, const Plan& p, hipStream_t s)
+{
+    const int cus = device_cu_count();
+    auto tiles = [&](int bm, int bn) { return ((a.M + bm - 1) / bm) * ((a.N + bn - 1) / bn); };
+    int code = p.tile_code;
+    // stage width of each shape, in k: shapes whose stage does not divide K
+    // fall back to the 32-k-stage shape of the same dtype
+    auto stage_k = [](int c) { return (c == 7 || c == 8 || c == 17) ? 32 : (c == 9 || c == 13 || c == 16) ? 128 : 64; };
+    if constexpr (OX::f32_frag) {
+        // measured on MI355X for the (fp32, 256, 4096) router: 64x64 on 8
+        // waves at M=4096 (99 us), 32x32 at M=1024 and 2048 (48 / 68 us)
+        if (code == 0)
+            code = tiles(64, 64) >= cus ? 4 : 3;
+        if (a.K % stage_k(code) != 0)
+            code = 7;
+        switch (code) {
+        case 1: return launch_persistent_t<OX, OW, 64, 64, 2, 2, 2>(a, p, s);
+        case 2: return launch_persistent_t<OX, OW, 32, 64, 2, 2, 2>(a, p, s);
+        case 3: return launch_persistent_t<OX, OW, 32, 32, 2, 2, 2>(a, p, s);
+        case 4: return launch_persistent_t<OX, OW, 64, 64, 4, 2, 2>(a, p, s);
+        case 5: return launch_persistent_t<OX, OW, 128, 64, 4, 2, 2>(a, p, s);
+        case 6: return launch_persistent_t<OX, OW, 64, 128, 2, 4, 2>(a, p, s);
+        case 8: return launch_persistent_t<OX, OW, 64, 256, 2, 4, 1>(a, p, s);
+        case 9: return launch_persistent_t<OX, OW, 32, 64, 2, 2, 4>(a, p, s);
+        default: return launch_persistent_t<OX, OW, 32, 32, 2, 2, 1>(a, p, s);
+        }
+    } else {
+        // measured on MI355X for the (bf16, 4096, 4096) GEMM: 128x256 on 8
+        // waves at M=4096 (169 us); 64x64 at M=256 (42 us)
+        if (code == 0)
+            code = tiles(128, 256) >= cus ? 15 : 12;
+        if (a.K % stage_k(code) != 0)
+            code = 17;
+        switch (code) {
+        case 11: return launch_persistent_t<OX, OW, 128, 128, 2, 2, 2>(a, p, s);
+        case 12: return launch_persistent_t<OX, OW, 64, 64, 2, 2, 2>(a, p, s);
+        case 13: return launch_persistent_t<OX, OW, 128, 128, 2, 2, 4>(a, p, s);
+        case 14: return launch_persistent_t<OX, OW, 256, 128, 4, 2, 2>(a, p, s);
+        case 15: return launch_persistent_t<OX, OW, 128, 256, 2, 4, 2>(a, p, s);
+        case 16: return launch_persistent_t<OX, OW, 64, 128, 2, 2, 4>(a, p, s);
+        default: return launch_persistent_t<OX, OW, 64, 64, 2, 2, 1>(a, p, s);
+        }
+    }
 }
 
 template <typename OX, typename OW>

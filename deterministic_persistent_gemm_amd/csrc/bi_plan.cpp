@@ -88,6 +88,13 @@ int device_cu_count()
     return cus;
 }
 
+bool tile_code_valid(int dtype, int code)
+{
+    if (dtype == BI_F32)
+        return (code >= 1 && code <= 9);
+    return code >= 11 && code <= 17;
+}
+
 static Tiling persistent_tiling(const bi_recipe_t& r)
 {
     (void)r;
@@ -109,6 +116,11 @@ bi_status_t make_plan(const bi_recipe_t& r, int32_t path_req, int64_t M, int64_t
     p.mtiles = (int)((M + 15) / 16);
     p.ntiles = (int)(N / 16);
     p.tiling = persistent_tiling(r);
+    const int tile_code = (path_req >> 8) & 0xff;
+    path_req &= 0xff;
+    if (tile_code != 0 && (path_req != BI_PATH_PERSISTENT || !tile_code_valid(r.dtype, tile_code)))
+        return BI_EINVAL;
+    p.tile_code = tile_code;
     if (path_req == BI_PATH_DECODE)
         p.path = kPathDecode;
     else if (path_req == BI_PATH_PERSISTENT)

@@ -24,6 +24,7 @@ struct Plan {
     int mtiles;      // 16-row tiles of M (decode path)
     int ntiles;      // 16-column tiles of N (decode path)
     Tiling tiling;   // persistent path
+    int tile_code;   // persistent tile shape, 0 = automatic
     size_t ws_bytes; // workspace the plan needs (decode tile partials)
 };
 
@@ -36,6 +37,9 @@ bi_status_t recipe_valid(const bi_recipe_t& r, int64_t N, int64_t K);
 // Picks the kernel path and its shape for M rows.  path_req: BI_PATH_*.
 bi_status_t make_plan(const bi_recipe_t& r, int32_t path_req, int64_t M, int64_t N, int64_t K,
                       Plan* plan);
+
+// Persistent tile shapes selectable through the experiment entry point.
+bool tile_code_valid(int dtype, int code);
 
 // Number of compute units of the current device (cached per device).
 int device_cu_count();

@@ -153,7 +153,14 @@ const char* bi_status_str(bi_status_t status);
  * Experiment and control entry points.  Not for production use.
  * ------------------------------------------------------------------------- */
 
-/* Path selectors for bi_lab_linear(). */
+/* Path selectors for bi_lab_linear().  With BI_PATH_PERSISTENT, bits 8..15
+ * of `path` may name a persistent tile shape (0: automatic; fp32: 1 = 64x64,
+ * 2 = 32x64, 3 = 32x32, 4 = 64x64 on 8 waves, 5 = 128x64, 6 = 64x128,
+ * 7 = 32x32 with 32-k stages, 8 = 64x256 with 32-k stages, 9 = 32x64 with
+ * 128-k stages;
+ * bf16: 11 = 128x128, 12 = 64x64, 13 = 128x128 with 128-k stages,
+ * 14 = 256x128, 15 = 128x256, 16 = 64x128 with 128-k stages, 17 = 64x64
+ * with 32-k stages).  Tile shapes never change the numerics. */
 enum { BI_PATH_AUTO = 0, BI_PATH_DECODE = 1, BI_PATH_PERSISTENT = 2 };
 
 /* The same linear layer with an explicit recipe and an explicit kernel path,

@@ -100,6 +100,29 @@ def test_both_kernel_paths_agree_bitwise(bi, router):
         assert_bitwise(a, b, f"decode vs persistent at M={M}")
 
 
+def test_every_persistent_tile_shape_gives_the_same_bits(bi, router):
+    # tiling is not part of the recipe: every persistent tile shape must
+    # reproduce the automatic choice bit for bit (ragged M and N tails too)
+    w, wd, bd = router
+    batch = wl.router_batch(300, w)
+    x = dev(batch.x)
+    ref = host(bi.bi_linear_f32(x, weight_t(wd), bd))
+    for code in range(1, 10):
+        banner(f"router fp32 M=300 persistent tile code {code}")
+        y = host(bi.bi_lab_linear(x, weight_t(wd), bd, path=bi.BI_PATH_PERSISTENT | (code << 8)))
+        assert_bitwise(y, ref, f"tile code {code}")
+    # a narrow N that no tile divides evenly
+    banner("fp32 N=48 K=320 tile codes")
+    g = np.random.default_rng(77)
+    w2 = g.standard_normal((48, 320)).astype(np.float32)
+    x2 = dev(g.standard_normal((70, 320)).astype(np.float32))
+    ref2 = host(bi.bi_linear_f32(x2, weight_t(dev(w2)), None))
+    assert_close(ref2, oracle.linear_f32(host(x2), w2, None), F32_ATOL, F32_RTOL, "N=48 K=320")
+    for code in range(1, 10):
+        y = host(bi.bi_lab_linear(x2, weight_t(dev(w2)), None, path=bi.BI_PATH_PERSISTENT | (code << 8)))
+        assert_bitwise(y, ref2, f"N=48 tile code {code}")
+
+
 def test_repeat_determinism_with_workspace_reuse(bi, router):
     # alternate two different batches through the same workspace: a stale
     # partial or a counter left non-zero would change the second result
