@@ -32,7 +32,24 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 FP32_MFMA_PEAK_TFLOPS = 157.3
+BF16_MFMA_PEAK_TFLOPS = 2500.0
 N_COPIES = 96
+
+# HBM bytes per decode call (k_decode + k_decode_fold), averaged over the sweep, from two rocprofv3
+# PMC runs: FETCH_SIZE scaled x2.0 and WRITE_SIZE x1.0 by a 512 MiB copy of known size (see
+# profiles/router_decode_hbm_bytes.md).  Valid only for the kernel sources with this digest; any
+# later change to them reports traffic as null until the counters are taken again.
+MEASURED_TRAFFIC = {"sources_sha256": "94c9623246254654ac3c6837b34816bfe46d801082c2e46043d38c07aeacbe4e", "bytes_per_call": 6811055}
+KERNEL_SOURCES = ("bi_device.h", "bi_launch.h", "bi_linear.hip", "bi_plan.cpp", "bi_plan.h")
+
+
+def kernel_sources_digest():
+    import hashlib
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "deterministic_persistent_gemm_amd", "csrc", name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
 
 
 def router_bytes(M, N=256, K=4096):
@@ -69,7 +86,14 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-bf16", action="store_true")
+    ap.add_argument("--no-moe", action="store_true")
+    ap.add_argument("--mode", choices=("step", "copy"), default="step",
+                    help="copy: one 512 MiB device-to-device copy, the known-size kernel that "
+                         "scales the PMC byte counters")
     args = ap.parse_args()
+    if args.mode == "copy":
+        return copy_calibration()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
                           "n_gpus": args.gpus}))
@@ -147,6 +171,11 @@ def main():
 
     if not args.no_prefill:
         extra["prefill"] = prefill_leg(torch, np, bi, wl, w, copies, bias, dev)
+    del copies
+    if not args.no_bf16:
+        extra["dense_bf16"] = dense_bf16_leg(torch, np, bi, wl, dev)
+    if not args.no_moe:
+        extra["moe"] = moe_leg(torch, np, bi, wl, dev)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -169,8 +198,11 @@ def main():
                                "decode sweep M in {1,2,4,8,15,16,17,32,33,64,128}",
                    "sweep": sweep, "N": 256, "K": 4096},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "k_decode<F32,F32,4> (avg over the sweep's launches)"},
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": (MEASURED_TRAFFIC["bytes_per_call"]
+                                 if kernel_sources_digest() == MEASURED_TRAFFIC["sources_sha256"] else None),
+                     "kernel": "decode call = k_decode (k-tile partials) + k_decode_fold, "
+                               "average over the sweep's launches"},
         "cpu_baseline": cpu,
         "extra": extra,
     }
@@ -198,6 +230,77 @@ def prefill_leg(torch, np, bi, wl, w, copies, bias, dev):
         res[str(M)] = {"us": round(us, 2), "TFLOPs": round(tf, 2),
                        "mfma_frac": round(tf / FP32_MFMA_PEAK_TFLOPS, 4)}
     return res
+
+
+def time_calls(torch, np, fn, n, spin_ms=2.0):
+    """Median device time of fn() in microseconds: HIP events around each
+    call, all queued behind a spin kernel."""
+    for i in range(3):
+        fn(i)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    spin(torch, spin_ms)
+    for i in range(n):
+        ev[i][0].record()
+        fn(i)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    return float(np.median([a.elapsed_time(b) * 1e3 for a, b in ev]))
+
+
+def dense_bf16_leg(torch, np, bi, wl, dev):
+    """bf16 dense X[M,4096] W[4096,4096] -> bf16, cold W (12 rotating copies, 384 MiB)."""
+    w = wl.dense_bf16_weights(0)
+    wt = torch.from_numpy(w.w.view(np.int16)).view(torch.bfloat16).to(dev)
+    copies = [wt] + [wt.clone() for _ in range(11)]
+    res = {}
+    for M in wl.DENSE_M_SWEEP:
+        x = torch.from_numpy(wl.dense_bf16_batch(M, w).x.view(np.int16)).view(torch.bfloat16).to(dev)
+        out = torch.empty((M, 4096), dtype=torch.bfloat16, device=dev)
+        us = time_calls(torch, np, lambda i: bi.bi_linear_bf16(x, copies[i % 12].t(), None, out=out),
+                        10 if M >= 1024 else 30)
+        nbytes = 2 * (4096 * 4096 + M * 4096 + M * 4096)
+        flops = 2 * M * 4096 * 4096
+        res[str(M)] = {"us": round(us, 2), "GBps": round(nbytes / us / 1e3, 1),
+                       "TFLOPs": round(flops / us / 1e6, 1),
+                       "hbm_frac": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4),
+                       "mfma_frac": round(flops / us / 1e6 / BF16_MFMA_PEAK_TFLOPS, 4)}
+    return res
+
+
+def moe_leg(torch, np, bi, wl, dev):
+    """Qwen3-30B-A3B-shaped MoE layer; algorithmic bytes count each distinct
+    expert touched once (measured from the returned ids)."""
+    w = wl.moe_weights(0)
+    wr = torch.from_numpy(w.w_router).to(dev)
+    w13 = torch.from_numpy(w.w13.view(np.int16)).view(torch.bfloat16).to(dev)
+    w2 = torch.from_numpy(w.w2.view(np.int16)).view(torch.bfloat16).to(dev)
+    H, E, I, k = wl.MOE_H, wl.MOE_E, wl.MOE_I, wl.MOE_TOPK
+    res = {}
+    for M in wl.MOE_M_SWEEP:
+        x = torch.from_numpy(wl.moe_batch(M, w).x.view(np.int16)).view(torch.bfloat16).to(dev)
+        _, ids, _ = bi.bi_moe_grouped_gemm(x, wr, None, w13, w2, k)
+        distinct = int(torch.unique(ids).numel())
+        us = time_calls(torch, np, lambda i: bi.bi_moe_grouped_gemm(x, wr, None, w13, w2, k), 20)
+        nbytes = (E * H * 4 + M * H * 2 + distinct * 3 * I * H * 2 + M * H * 4 + M * k * 8)
+        flops = 2 * M * E * H + 2 * M * k * 3 * I * H
+        res[str(M)] = {"us": round(us, 2), "distinct_experts": distinct,
+                       "GBps": round(nbytes / us / 1e3, 1), "TFLOPs": round(flops / us / 1e6, 2),
+                       "hbm_frac": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4)}
+    return res
+
+
+def copy_calibration():
+    """One device-to-device copy of exactly 512 MiB (read 512 MiB, write 512 MiB)."""
+    import torch
+    dev = torch.device("cuda:0")
+    n = 512 * 1024 * 1024 // 4
+    a = torch.ones(n, dtype=torch.float32, device=dev)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": 4 * n, "ok": bool(b[-1].item() == 1.0)}))
 
 
 def cpu_baseline(np, wl, w, sweep):
