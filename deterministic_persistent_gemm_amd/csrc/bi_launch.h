@@ -24,6 +24,10 @@ struct LinearArgs {
     int M, N, K;
 };
 
-hipError_t launch_linear(int xkind, const LinearArgs& a, const Plan& p, void* ws, hipStream_t s);
+// fold == false leaves a decode-path call with several k tiles at its tile
+// partials (layout: [M tile][N tile][k tile][64 lanes] of f32x4 in ws) for a
+// consumer that folds them itself in the same order.
+hipError_t launch_linear(int xkind, const LinearArgs& a, const Plan& p, void* ws, hipStream_t s,
+                         bool fold = true);
 
 }  // namespace bi

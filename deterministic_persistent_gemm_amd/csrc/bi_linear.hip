@@ -323,7 +323,7 @@ static hipError_t launch_decode_mt(const LinearArgs& a, const Plan& p, f32x4* pa
 }
 
 template <typename OX, typename OW>
-static hipError_t launch_decode(const LinearArgs& a, const Plan& p, void* ws, hipStream_t s)
+static hipError_t launch_decode(const LinearArgs& a, const Plan& p, void* ws, hipStream_t s, bool fold)
 {
     f32x4* partials = reinterpret_cast<f32x4*>(ws);
     hipError_t e;
@@ -336,7 +336,7 @@ static hipError_t launch_decode(const LinearArgs& a, const Plan& p, void* ws, hi
         e = launch_decode_mt<OX, OW, 2>(a, p, partials, s);
     else
         e = launch_decode_mt<OX, OW, 1>(a, p, partials, s);
-    if (e != hipSuccess || p.tiles_k == 1)
+    if (e != hipSuccess || p.tiles_k == 1 || !fold)
         return e;
     k_decode_fold<<<dim3((unsigned)p.ntiles, (unsigned)p.mtiles), 64, 0, s>>>(a, p.tiles_k, partials);
     return hipGetLastError();
@@ -406,21 +406,21 @@ static hipError_t launch_persistent(const LinearArgs& a, const Plan& p, hipStrea
 }
 
 template <typename OX, typename OW>
-static hipError_t launch_typed(const LinearArgs& a, const Plan& p, void* ws, hipStream_t s)
+static hipError_t launch_typed(const LinearArgs& a, const Plan& p, void* ws, hipStream_t s, bool fold)
 {
     if (p.path == kPathDecode)
-        return launch_decode<OX, OW>(a, p, ws, s);
+        return launch_decode<OX, OW>(a, p, ws, s, fold);
     return launch_persistent<OX, OW>(a, p, s);
 }
 
-hipError_t launch_linear(int xkind, const LinearArgs& a, const Plan& p, void* ws, hipStream_t s)
+hipError_t launch_linear(int xkind, const LinearArgs& a, const Plan& p, void* ws, hipStream_t s, bool fold)
 {
     if (p.recipe.dtype == BI_F32) {
         if (xkind == kXF32)
-            return launch_typed<F32, F32>(a, p, ws, s);
-        return launch_typed<BF16W, F32>(a, p, ws, s);
+            return launch_typed<F32, F32>(a, p, ws, s, fold);
+        return launch_typed<BF16W, F32>(a, p, ws, s, fold);
     }
-    return launch_typed<BF16, BF16>(a, p, ws, s);
+    return launch_typed<BF16, BF16>(a, p, ws, s, fold);
 }
 
 }  // namespace bi

@@ -30,7 +30,7 @@ namespace bi {
 
 namespace {
 
-constexpr int kUnitRows = 16;     // rows per grouped-GEMM work unit
+constexpr int kTileRows = 16;     // rows of one MFMA output tile
 constexpr int kMaxExperts = 1024;
 constexpr int kMaxTopk = 32;
 
@@ -42,11 +42,16 @@ struct MoELayout {
     int64_t max_units;
 };
 
+// Rows per grouped-GEMM work unit: 32 (two M tiles per wave, each weight
+// fragment used twice) once experts average 16 rows or more, else 16.
+int unit_rows_for(int64_t M, int64_t E, int64_t topk) { return M * topk >= 16 * E ? 32 : 16; }
+
 MoELayout moe_layout(int64_t M, int64_t H, int64_t E, int64_t I, int64_t topk, size_t router_ws_bytes)
 {
     MoELayout L{};
     const int64_t P = M * topk;
-    L.max_units = (P + kUnitRows - 1) / kUnitRows + (P < E ? P : E);
+    const int64_t U = unit_rows_for(M, E, topk);
+    L.max_units = (P + U - 1) / U + (P < E ? P : E);
     size_t o = 0;
     L.router_ws = o;   o = align256(o + router_ws_bytes);
     L.logits = o;      o = align256(o + (size_t)M * E * sizeof(float));
@@ -65,27 +70,60 @@ MoELayout moe_layout(int64_t M, int64_t H, int64_t E, int64_t I, int64_t topk, s
 
 // ------------------------------------------------------------------- routing
 
-__device__ __forceinline__ bool better(float va, int ia, float vb, int ib)
-{
-    // an unset candidate (index INT_MAX) loses to any set one; otherwise the
-    // larger value wins and equal values go to the lower index (-0.0 == +0.0)
-    if (ib == INT_MAX)
-        return ia != INT_MAX;
-    if (ia == INT_MAX)
-        return false;
-    return va > vb || (va == vb && ia < ib);
-}
+constexpr int kRouteTokens = 16;   // tokens per routing workgroup, one wave each
 
-// One wave per token: softmax probabilities over all E experts (fixed
-// per-lane order, then a fixed butterfly across lanes), then the top-k by
-// repeated arg-max.  E <= 1024, topk <= 32.
-__global__ __launch_bounds__(64) void k_route(const float* __restrict__ logits, int M, int E, int topk,
-                                              int32_t* __restrict__ ids, float* __restrict__ probs)
+// Ordering key of a logit for the expert choice: NaN ranks like -inf.
+__device__ __forceinline__ float rank_key(float v) { return (v != v) ? -INFINITY : v; }
+
+// One workgroup per 16 tokens, one wave per token.
+//  1. Logits of the 16 tokens into LDS: either read from `logits` [M,E], or
+//     folded here from the router's k tile partials in ascending tile order
+//     (acc = P0; acc = acc + P1; ...; + bias) -- the linear fold, same bits.
+//  2. Softmax over all E: max (exact), exp, a sum in a fixed order (each
+//     lane ascending over its experts, then a fixed butterfly), p = e / sum.
+//  3. Top-k by rank: an expert's slot is the number of experts that beat it
+//     (larger logit, or equal logit and lower index; -0.0 == +0.0).  Ranks
+//     are distinct, so slot j receives exactly one expert.
+template <int kPer>   // experts per lane: E <= 64 * kPer
+__global__ __launch_bounds__(kRouteTokens * 64) void k_route(const float* __restrict__ logits,
+                                                             const f32x4* __restrict__ partials,
+                                                             const float* __restrict__ bias, int tiles_k,
+                                                             int M, int E, int topk,
+                                                             int32_t* __restrict__ ids,
+                                                             float* __restrict__ probs)
 {
-    const int m = blockIdx.x;
-    const int lane = threadIdx.x;
-    constexpr int kPer = kMaxExperts / 64;
-    const float* l = logits + (int64_t)m * E;
+    __shared__ float lg[kRouteTokens][kMaxExperts];
+    const int mt = blockIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    if (partials) {
+        const int ntiles = E >> 4;
+        for (int pi = tid; pi < ntiles * 64; pi += kRouteTokens * 64) {
+            const int nt = pi >> 6, ln = pi & 63;
+            const f32x4* p = partials + ((int64_t)mt * ntiles + nt) * tiles_k * 64 + ln;
+            f32x4 acc = p[0];
+            for (int u = 1; u < tiles_k; ++u)
+                acc = acc + p[(int64_t)u * 64];
+            const int col = nt * 16 + acc_col(ln);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                float v = acc[q];
+                if (bias)
+                    v = v + bias[col];
+                lg[acc_row(ln, q)][col] = v;
+            }
+        }
+    } else {
+        for (int i = tid; i < kRouteTokens * E; i += kRouteTokens * 64) {
+            const int r = i / E, e = i % E;
+            const int m = mt * kRouteTokens + r;
+            lg[r][e] = m < M ? logits[(int64_t)m * E + e] : 0.f;
+        }
+    }
+    __syncthreads();
+    const int m = mt * kRouteTokens + wave;
+    if (m >= M)
+        return;
+    const float* l = lg[wave];
     float v[kPer];
     float mx = -INFINITY;
 #pragma unroll
@@ -107,52 +145,44 @@ __global__ __launch_bounds__(64) void k_route(const float* __restrict__ logits, 
     for (int off = 1; off <= 32; off <<= 1)
         sum = sum + __shfl_xor(sum, off);
 
-    unsigned taken = 0;   // bit i: candidate lane + 64 i already chosen
-    for (int j = 0; j < topk; ++j) {
-        float bv = 0.f;
-        int bi = INT_MAX;
+    int rank[kPer];
+    float key[kPer];
 #pragma unroll
-        for (int i = 0; i < kPer; ++i) {
-            const int e = lane + 64 * i;
-            if (e < E && !(taken & (1u << i)) && better(v[i], e, bv, bi)) {
-                bv = v[i];
-                bi = e;
+    for (int i = 0; i < kPer; ++i) {
+        rank[i] = 0;
+        key[i] = rank_key(v[i]);
+    }
+    for (int e2 = 0; e2 < E; e2 += 4) {
+        const f32x4 o4 = *reinterpret_cast<const f32x4*>(l + e2);   // same address on every lane
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float ok = rank_key(o4[j]);
+#pragma unroll
+            for (int i = 0; i < kPer; ++i) {
+                const int e = lane + 64 * i;
+                rank[i] += (ok > key[i] || (ok == key[i] && e2 + j < e)) ? 1 : 0;
             }
         }
-        for (int off = 32; off >= 1; off >>= 1) {
-            const float ov = __shfl_xor(bv, off);
-            const int oi = __shfl_xor(bi, off);
-            if (better(ov, oi, bv, bi)) {
-                bv = ov;
-                bi = oi;
-            }
-        }
-        // bi is now the same on every lane
-        if ((bi & 63) == lane)
-            taken |= 1u << (bi >> 6);
-        if (lane == 0) {
-            ids[(int64_t)m * topk + j] = bi;
-        }
-        // probability of the chosen expert, read from its owner lane
-        float pe = 0.f;
+    }
 #pragma unroll
-        for (int i = 0; i < kPer; ++i)
-            if (lane + 64 * i == bi)
-                pe = ex[i] / sum;
-        pe = __shfl(pe, bi & 63);
-        if (lane == 0)
-            probs[(int64_t)m * topk + j] = pe;
+    for (int i = 0; i < kPer; ++i) {
+        const int e = lane + 64 * i;
+        if (e < E && rank[i] < topk) {
+            ids[(int64_t)m * topk + rank[i]] = e;
+            probs[(int64_t)m * topk + rank[i]] = ex[i] / sum;
+        }
     }
 }
 
 // ------------------------------------------------------------------ dispatch
 
 // Stable counting sort of the M*topk (token, slot) pairs by expert, tokens
-// ascending within an expert, and the 16-row work units.  One workgroup of
+// ascending within an expert, and the work units (unit_rows rows each).  One workgroup of
 // 1024 threads.  A token selects an expert at most once, so within a chunk
 // of 64 tokens a pair's rank among the expert's pairs is a popcount of the
 // chunk's per-expert token mask below it.
 __global__ __launch_bounds__(1024) void k_dispatch(const int32_t* __restrict__ ids, int M, int E, int topk,
+                                                   int unit_rows,
                                                    int32_t* __restrict__ offsets,
                                                    int32_t* __restrict__ sorted,
                                                    int32_t* __restrict__ unit_expert,
@@ -175,7 +205,7 @@ __global__ __launch_bounds__(1024) void k_dispatch(const int32_t* __restrict__ i
     // inclusive scans of the counts and of the unit counts (Hillis-Steele)
     for (int e = tid; e < E; e += blockDim.x) {
         scan_tmp[0][e] = cnt[e];
-        scan_tmp[1][e] = (cnt[e] + kUnitRows - 1) / kUnitRows;
+        scan_tmp[1][e] = (cnt[e] + unit_rows - 1) / unit_rows;
     }
     __syncthreads();
     for (int off = 1; off < E; off <<= 1) {
@@ -195,7 +225,7 @@ __global__ __launch_bounds__(1024) void k_dispatch(const int32_t* __restrict__ i
         const int start = scan_tmp[0][e] - cnt[e];
         cursor[e] = start;
         offsets[e] = start;
-        ustart[e] = scan_tmp[1][e] - (cnt[e] + kUnitRows - 1) / kUnitRows;
+        ustart[e] = scan_tmp[1][e] - (cnt[e] + unit_rows - 1) / unit_rows;
     }
     if (tid == 0) {
         offsets[E] = P;
@@ -204,10 +234,10 @@ __global__ __launch_bounds__(1024) void k_dispatch(const int32_t* __restrict__ i
     __syncthreads();
     // work units: expert e owns units ustart[e] .. covering its rows
     for (int e = tid; e < E; e += blockDim.x) {
-        const int nu = (cnt[e] + kUnitRows - 1) / kUnitRows;
+        const int nu = (cnt[e] + unit_rows - 1) / unit_rows;
         for (int u = 0; u < nu; ++u) {
             unit_expert[ustart[e] + u] = e;
-            unit_row[ustart[e] + u] = cursor[e] + u * kUnitRows;
+            unit_row[ustart[e] + u] = cursor[e] + u * unit_rows;
         }
     }
     // stable placement, 64 tokens at a time
@@ -258,13 +288,15 @@ struct GroupedArgs {
 
 // Workgroup = TW x NW waves: TW waves split the k tile partials of one
 // output tile (folded in ascending order through LDS), NW waves take NW
-// neighbouring 16-column tiles.  SWIGLU: each wave carries a gate block and
-// the matching up block (two independent chains) and applies the activation.
-template <int TW, int NW, bool SWIGLU, int CH>
+// neighbouring 16-column tiles.  A work unit is MT tiles of 16 rows of one
+// expert; each wave runs MT x NB independent chains over one weight slab.
+// SWIGLU: each wave carries a gate block and the matching up block and
+// applies the activation in the epilogue.
+template <int TW, int NW, int MT, bool SWIGLU, int CH>
 __global__ __launch_bounds__(TW * NW * 64) void k_grouped(GroupedArgs g)
 {
     constexpr int NB = SWIGLU ? 2 : 1;                  // output blocks per wave
-    __shared__ f32x4 lds[(TW > 1) ? TW * NW * NB * 64 : 1];
+    __shared__ f32x4 lds[(TW > 1) ? TW * NW * MT * NB * 64 : 1];
     const int u = blockIdx.y;
     if (u >= g.nunits[0])
         return;
@@ -277,10 +309,14 @@ __global__ __launch_bounds__(TW * NW * 64) void k_grouped(GroupedArgs g)
     const int row0 = g.unit_row[u];
     const int row_end = g.offsets[e + 1];
 
-    // this lane's operand rows
-    const int pos = min(row0 + r, row_end - 1);
-    const int arow = g.a_by_token ? g.sorted[pos] / g.topk : pos;
-    const uint16_t* ap = g.a + (int64_t)arow * g.lda + kSlotLen * gslot;
+    // this lane's operand rows (rows past the expert's last read its last row)
+    const uint16_t* ap[MT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+        const int pos = min(row0 + m * kTileRows + r, row_end - 1);
+        const int arow = g.a_by_token ? g.sorted[pos] / g.topk : pos;
+        ap[m] = g.a + (int64_t)arow * g.lda + kSlotLen * gslot;
+    }
     const uint16_t* we = g.w + (int64_t)e * g.w_stride;
     const int ntc = nt_ok ? nt : 0;
     const uint16_t* wp[NB];
@@ -288,37 +324,45 @@ __global__ __launch_bounds__(TW * NW * 64) void k_grouped(GroupedArgs g)
     if (SWIGLU)
         wp[NB - 1] = we + (int64_t)(g.up_offset + ntc * 16 + r) * g.ldw + kSlotLen * gslot;
 
-    f32x4 acc[NB];
+    f32x4 acc[MT][NB];
     for (int t = tw; t < g.tiles_k; t += TW) {
-        f32x4 P[1][NB];
+        f32x4 P[MT][NB];
 #pragma unroll
-        for (int b = 0; b < NB; ++b)
-            P[0][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int m = 0; m < MT; ++m)
+#pragma unroll
+            for (int b = 0; b < NB; ++b)
+                P[m][b] = f32x4{0.f, 0.f, 0.f, 0.f};
         const int64_t k0 = (int64_t)t * g.kbpt * kKBlock;
         for (int c = 0; c < g.kbpt; c += CH) {
-            Frag<false> af[CH][1];
+            Frag<false> af[CH][MT];
             Frag<false> bf[CH][NB];
 #pragma unroll
             for (int i = 0; i < CH; ++i) {
-                load_frag<BF16>(af[i][0], ap + k0 + (int64_t)(c + i) * kKBlock);
 #pragma unroll
                 for (int b = 0; b < NB; ++b)
                     load_frag<BF16>(bf[i][b], wp[b] + k0 + (int64_t)(c + i) * kKBlock);
+#pragma unroll
+                for (int m = 0; m < MT; ++m)
+                    load_frag<BF16>(af[i][m], ap[m] + k0 + (int64_t)(c + i) * kKBlock);
             }
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int i = 0; i < CH; ++i)
-                mfma_tiles<1, NB>(af[i], bf[i], P);
+                mfma_tiles<MT, NB>(af[i], bf[i], P);
         }
         if (TW == 1) {
 #pragma unroll
-            for (int b = 0; b < NB; ++b)
-                acc[b] = (t == 0) ? P[0][b] : acc[b] + P[0][b];
-        } else {
-            // one tile per wave when TW == tiles_k; stage it for the ordered fold
+            for (int m = 0; m < MT; ++m)
 #pragma unroll
-            for (int b = 0; b < NB; ++b)
-                lds[((t * NW + nw) * NB + b) * 64 + lane] = P[0][b];
+                for (int b = 0; b < NB; ++b)
+                    acc[m][b] = (t == 0) ? P[m][b] : acc[m][b] + P[m][b];
+        } else {
+            // one tile per wave (TW == tiles_k); stage it for the ordered fold
+#pragma unroll
+            for (int m = 0; m < MT; ++m)
+#pragma unroll
+                for (int b = 0; b < NB; ++b)
+                    lds[(((t * NW + nw) * MT + m) * NB + b) * 64 + lane] = P[m][b];
         }
     }
     if (TW > 1) {
@@ -326,34 +370,38 @@ __global__ __launch_bounds__(TW * NW * 64) void k_grouped(GroupedArgs g)
         if (tw != 0)
             return;
 #pragma unroll
-        for (int b = 0; b < NB; ++b) {
-            acc[b] = lds[((0 * NW + nw) * NB + b) * 64 + lane];
-            for (int t = 1; t < g.tiles_k; ++t)
-                acc[b] = acc[b] + lds[((t * NW + nw) * NB + b) * 64 + lane];
-        }
+        for (int m = 0; m < MT; ++m)
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                acc[m][b] = lds[(((0 * NW + nw) * MT + m) * NB + b) * 64 + lane];
+                for (int t = 1; t < g.tiles_k; ++t)
+                    acc[m][b] = acc[m][b] + lds[(((t * NW + nw) * MT + m) * NB + b) * 64 + lane];
+            }
     }
     if (!nt_ok)
         return;
 
     const int col = nt * 16 + acc_col(lane);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const int p = row0 + acc_row(lane, q);
-        if (p >= row_end)
-            continue;
-        if (SWIGLU) {
-            // storage point of the gate/up projection, then the activation in
-            // fp32 with the routing probability, one rounding to bf16
-            const float hg = bf16_to_f32(f32_to_bf16_rne(acc[0][q]));
-            const float hu = bf16_to_f32(f32_to_bf16_rne(acc[NB - 1][q]));
-            const float prob = g.probs[g.sorted[p]];
-            const float sg = 1.0f / (1.0f + expf(-hg));
-            const float av = ((hg * sg) * hu) * prob;
-            g.act[(int64_t)p * g.n_out + col] = f32_to_bf16_rne(av);
-        } else {
-            g.part[(int64_t)g.sorted[p] * g.n_out + col] = acc[0][q];
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int p = row0 + m * kTileRows + acc_row(lane, q);
+            if (p >= row_end)
+                continue;
+            if (SWIGLU) {
+                // storage point of the gate/up projection, then the activation
+                // in fp32 with the routing probability, one rounding to bf16
+                const float hg = bf16_to_f32(f32_to_bf16_rne(acc[m][0][q]));
+                const float hu = bf16_to_f32(f32_to_bf16_rne(acc[m][NB - 1][q]));
+                const float prob = g.probs[g.sorted[p]];
+                const float sg = 1.0f / (1.0f + expf(-hg));
+                const float av = ((hg * sg) * hu) * prob;
+                g.act[(int64_t)p * g.n_out + col] = f32_to_bf16_rne(av);
+            } else {
+                g.part[(int64_t)g.sorted[p] * g.n_out + col] = acc[m][0][q];
+            }
         }
-    }
 }
 
 // ------------------------------------------------------------------- combine
@@ -383,31 +431,42 @@ static int pick_ch(int kbpt)
     return 1;
 }
 
-template <int TW, int NW, bool SWIGLU>
+template <int TW, int NW, int MT, bool SWIGLU>
 static hipError_t launch_grouped_tw(const GroupedArgs& g, int64_t max_units, hipStream_t s)
 {
     const int ntiles = (g.n_out / 16 + NW - 1) / NW;
     dim3 grid((unsigned)ntiles, (unsigned)max_units);
-    switch (pick_ch(g.kbpt)) {
-    case 16: k_grouped<TW, NW, SWIGLU, 16><<<grid, TW * NW * 64, 0, s>>>(g); break;
-    case 8:  k_grouped<TW, NW, SWIGLU, 8><<<grid, TW * NW * 64, 0, s>>>(g); break;
-    case 4:  k_grouped<TW, NW, SWIGLU, 4><<<grid, TW * NW * 64, 0, s>>>(g); break;
-    case 2:  k_grouped<TW, NW, SWIGLU, 2><<<grid, TW * NW * 64, 0, s>>>(g); break;
-    default: k_grouped<TW, NW, SWIGLU, 1><<<grid, TW * NW * 64, 0, s>>>(g); break;
+    // register budget: CH k blocks of MT activation and NB weight fragments
+    int ch = pick_ch(g.kbpt);
+    if (MT * (SWIGLU ? 2 : 1) > 2 && ch > 8)
+        ch = 8;
+    switch (ch) {
+    case 16: k_grouped<TW, NW, MT, SWIGLU, 16><<<grid, TW * NW * 64, 0, s>>>(g); break;
+    case 8:  k_grouped<TW, NW, MT, SWIGLU, 8><<<grid, TW * NW * 64, 0, s>>>(g); break;
+    case 4:  k_grouped<TW, NW, MT, SWIGLU, 4><<<grid, TW * NW * 64, 0, s>>>(g); break;
+    case 2:  k_grouped<TW, NW, MT, SWIGLU, 2><<<grid, TW * NW * 64, 0, s>>>(g); break;
+    default: k_grouped<TW, NW, MT, SWIGLU, 1><<<grid, TW * NW * 64, 0, s>>>(g); break;
     }
     return hipGetLastError();
 }
 
-template <bool SWIGLU>
-static hipError_t launch_grouped(const GroupedArgs& g, int64_t max_units, hipStream_t s)
+template <int MT, bool SWIGLU>
+static hipError_t launch_grouped_mt(const GroupedArgs& g, int64_t max_units, hipStream_t s)
 {
     // k tile partials of one output tile are spread over the workgroup's
-    // waves when there are several; otherwise the waves take more columns
+    // waves when there are 2 or 4; otherwise the waves take more columns
     if (g.tiles_k == 4)
-        return launch_grouped_tw<4, 1, SWIGLU>(g, max_units, s);
+        return launch_grouped_tw<4, 1, MT, SWIGLU>(g, max_units, s);
     if (g.tiles_k == 2)
-        return launch_grouped_tw<2, 2, SWIGLU>(g, max_units, s);
-    return launch_grouped_tw<1, 4, SWIGLU>(g, max_units, s);
+        return launch_grouped_tw<2, 2, MT, SWIGLU>(g, max_units, s);
+    return launch_grouped_tw<1, 4, MT, SWIGLU>(g, max_units, s);
+}
+
+template <bool SWIGLU>
+static hipError_t launch_grouped(const GroupedArgs& g, int unit_rows, int64_t max_units, hipStream_t s)
+{
+    return unit_rows == 32 ? launch_grouped_mt<2, SWIGLU>(g, max_units, s)
+                           : launch_grouped_mt<1, SWIGLU>(g, max_units, s);
 }
 
 size_t moe_workspace_size(int64_t M, int64_t H, int64_t E, int64_t I, int64_t topk)
@@ -466,13 +525,30 @@ bi_status_t moe_run(const uint16_t* x, const float* w_router, const float* b_rou
     uint16_t* act = reinterpret_cast<uint16_t*>(base + L.act);
     float* part = reinterpret_cast<float*>(base + L.part);
 
-    // router: the batch-invariant fp32 linear layer on the widened bf16 rows
+    // router: the batch-invariant fp32 linear layer on the widened bf16 rows;
+    // on the decode path its k tile partials are folded by the routing kernel
     LinearArgs ra{x, H, w_router, H, b_router, logits, 0, E, (int)M, (int)E, (int)H};
-    if (launch_linear(kXBF16Widen, ra, pr, base + L.router_ws, stream) != hipSuccess)
+    const bool fused_fold = pr.path == kPathDecode && pr.tiles_k > 1;
+    if (launch_linear(kXBF16Widen, ra, pr, base + L.router_ws, stream, !fused_fold) != hipSuccess)
         return BI_EHIP;
-    k_route<<<(unsigned)M, 64, 0, stream>>>(logits, (int)M, (int)E, (int)topk, topk_ids, topk_probs);
-    k_dispatch<<<1, 1024, 0, stream>>>(topk_ids, (int)M, (int)E, (int)topk, offsets, sorted, unit_expert,
-                                       unit_row, nunits);
+    const unsigned route_groups = (unsigned)((M + kRouteTokens - 1) / kRouteTokens);
+    const float* lsrc = fused_fold ? nullptr : logits;
+    const f32x4* psrc = fused_fold ? reinterpret_cast<const f32x4*>(base + L.router_ws) : nullptr;
+    if (E <= 128)
+        k_route<2><<<route_groups, kRouteTokens * 64, 0, stream>>>(lsrc, psrc, b_router, pr.tiles_k, (int)M,
+                                                                   (int)E, (int)topk, topk_ids, topk_probs);
+    else if (E <= 256)
+        k_route<4><<<route_groups, kRouteTokens * 64, 0, stream>>>(lsrc, psrc, b_router, pr.tiles_k, (int)M,
+                                                                   (int)E, (int)topk, topk_ids, topk_probs);
+    else if (E <= 512)
+        k_route<8><<<route_groups, kRouteTokens * 64, 0, stream>>>(lsrc, psrc, b_router, pr.tiles_k, (int)M,
+                                                                   (int)E, (int)topk, topk_ids, topk_probs);
+    else
+        k_route<16><<<route_groups, kRouteTokens * 64, 0, stream>>>(lsrc, psrc, b_router, pr.tiles_k, (int)M,
+                                                                    (int)E, (int)topk, topk_ids, topk_probs);
+    const int unit_rows = unit_rows_for(M, E, topk);
+    k_dispatch<<<1, 1024, 0, stream>>>(topk_ids, (int)M, (int)E, (int)topk, unit_rows, offsets, sorted,
+                                       unit_expert, unit_row, nunits);
     if (hipGetLastError() != hipSuccess)
         return BI_EHIP;
 
@@ -496,7 +572,7 @@ bi_status_t moe_run(const uint16_t* x, const float* w_router, const float* b_rou
     g1.probs = topk_probs;
     g1.topk = (int)topk;
     g1.act = act;
-    if (launch_grouped<true>(g1, L.max_units, stream) != hipSuccess)
+    if (launch_grouped<true>(g1, unit_rows, L.max_units, stream) != hipSuccess)
         return BI_EHIP;
 
     GroupedArgs g2 = g1;
@@ -513,7 +589,7 @@ bi_status_t moe_run(const uint16_t* x, const float* w_router, const float* b_rou
     g2.tiles_k = (int)(I / r_g2.block_k);
     g2.act = nullptr;
     g2.part = part;
-    if (launch_grouped<false>(g2, L.max_units, stream) != hipSuccess)
+    if (launch_grouped<false>(g2, unit_rows, L.max_units, stream) != hipSuccess)
         return BI_EHIP;
 
     const int64_t n = M * H;

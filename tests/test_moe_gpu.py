@@ -11,8 +11,13 @@ Bars:
   gap exceeds TAU (near ties may legitimately resolve either way; they are
   listed and checked stage-wise);
 * probabilities: rtol 1e-5 against the oracle's softmax of the same ids;
-* outputs: rtol 1e-2, atol 1e-3 * rms against the oracle re-run with the
-  GPU's ids (bf16 storage points may round one ulp apart);
+* outputs: rtol 1e-2 and atol = 32 * 2^-8 / sqrt(topk * I) * rms(out)
+  against the oracle re-run with the GPU's ids.  The GPU rounds its fp32
+  values and the oracle its binary64 values to the bf16 storage points, so a
+  value near a rounding boundary can land one bf16 ulp apart; one such flip
+  moves an output by about 2^-8 |a| |w2|, while rms(out) grows like
+  sqrt(topk * I) |a| |w2|.  The bound allows ~8 flips of a 4-sigma activation
+  in one output (1.6e-3 rms at the Qwen shape);
 * probe tokens: ids, probs and outputs bitwise equal across every M.
 """
 import numpy as np
@@ -25,6 +30,10 @@ from tests.gpu_util import assert_bitwise, assert_close, banner, bf16_to_f32, de
 pytestmark = pytest.mark.gpu
 
 TAU = 1e-4
+
+
+def moe_atol(rms, topk, I):
+    return 32.0 * 2.0 ** -8 / np.sqrt(topk * I) * rms
 
 
 @pytest.fixture(scope="module")
@@ -83,7 +92,7 @@ def test_moe_sweep_against_oracle_and_invariant(bi, moe):
         yf, _, pf, _ = oracle.moe(xs, w.w_router, None, w.w13, w.w2, wl.MOE_TOPK, ids=ids[rows])
         assert_close(probs[rows], pf, 0.0, 1e-5, f"probs M={M}")
         rms = float(np.sqrt(np.mean(yf.astype(np.float64) ** 2)))
-        err = assert_close(y[rows], yf, 1e-3 * rms, 1e-2, f"moe out M={M}")
+        err = assert_close(y[rows], yf, moe_atol(rms, wl.MOE_TOPK, wl.MOE_I), 1e-2, f"moe out M={M}")
         print(f"M={M}: rms(out)={rms:.3e} max|err|={err:.2e} near-tie tokens={int((~clear).sum())}")
         for pid, pos in batch.probes.items():
             for p in pos:
@@ -123,24 +132,26 @@ def test_moe_zero_router_and_zero_down_projection(bi, moe):
     assert np.all(probs == np.float32(1.0 / 128.0))
     yo, _, _, _ = oracle.moe(batch.x[:4], np.zeros_like(w.w_router), None, w.w13, w.w2, 8)
     rms = float(np.sqrt(np.mean(yo.astype(np.float64) ** 2)))
-    assert_close(y[:4], yo, 1e-3 * rms, 1e-2, "zero-router outputs")
+    assert_close(y[:4], yo, moe_atol(rms, 8, wl.MOE_I), 1e-2, "zero-router outputs")
     banner("moe zero down projection")
     y2, _, _ = run_moe(bi, batch.x, dict(d, w2=torch.zeros_like(d["w2"])))
     assert np.all(y2 == 0.0)
 
 
-def test_moe_small_shape_full_oracle(bi):
-    # a small layer, every token checked, with a router bias and ragged M
-    w = wl.moe_weights(5, H=256, E=32, I=64)
-    b = (np.random.default_rng(9).standard_normal(32) * 0.05).astype(np.float32)
+@pytest.mark.parametrize("E,topk", [(32, 4), (256, 8), (1024, 6)])
+def test_moe_small_shape_full_oracle(bi, E, topk):
+    # a small layer, every token checked, with a router bias and ragged M;
+    # E spans the routing kernel's experts-per-lane variants
+    w = wl.moe_weights(5, H=256, E=E, I=64)
+    b = (np.random.default_rng(9).standard_normal(E) * 0.05).astype(np.float32)
     d = dict(wr=dev(w.w_router), w13=dev(w.w13), w2=dev(w.w2))
-    for M in (1, 5, 70):
-        banner(f"moe small H=256 E=32 I=64 topk=4 M={M}")
+    for M in (1, 5, 70, 200):
+        banner(f"moe small H=256 E={E} I=64 topk={topk} M={M}")
         x = wl.moe_batch(M, w).x
-        y, ids, probs = run_moe(bi, x, d, topk=4, b_router=dev(b))
+        y, ids, probs = run_moe(bi, x, d, topk=topk, b_router=dev(b))
         lg = host(bi.bi_linear_f32(dev(bf16_to_f32(x)), weight_t(d["wr"]), dev(b)))
-        np.testing.assert_array_equal(oracle.topk(lg, 4), ids)
-        yf, _, pf, _ = oracle.moe(x, w.w_router, b, w.w13, w.w2, 4, ids=ids)
+        np.testing.assert_array_equal(oracle.topk(lg, topk), ids)
+        yf, _, pf, _ = oracle.moe(x, w.w_router, b, w.w13, w.w2, topk, ids=ids)
         assert_close(probs, pf, 0.0, 1e-5, f"small probs M={M}")
         rms = float(np.sqrt(np.mean(yf.astype(np.float64) ** 2)))
-        assert_close(y, yf, 1e-3 * rms, 1e-2, f"small moe M={M}")
+        assert_close(y, yf, moe_atol(rms, topk, 64), 1e-2, f"small moe M={M}")
