@@ -151,15 +151,27 @@ __global__ __launch_bounds__(64) void k_decode_fold(LinearArgs a, int tiles_k,
 // One LDS stage holds KBS k blocks of BM rows of X and BN rows of W.  Each
 // thread moves whole 16-byte chunks: consecutive threads take consecutive
 // chunks of a row, so a row segment is read with coalesced 16-byte loads.
-// Rows are padded by 16 bytes in LDS, which spreads the 16 rows a fragment
-// read touches over distinct banks.
+// In LDS the chunks of a row are permuted by an XOR with a key taken from
+// the row (rows are not padded).  The LDS has 64 banks of 4 bytes, i.e. a
+// 256-byte bank window; the key spreads the 16 rows a fragment read touches
+// over distinct chunk positions of that window, which measured zero bank
+// conflicts on gfx950 (SQ_LDS_BANK_CONFLICT) for both the stage stores and
+// the fragment reads, against ~2 conflict cycles per instruction with
+// 16-byte row padding.
 template <typename E, int ROWS, int KS, int NT>
 struct Stager {
     static constexpr int kPer16 = 16 / (int)sizeof(E);
     static constexpr int kChunks = KS / kPer16;          // 16-byte chunks per row
-    static constexpr int kPitch = KS + kPer16;           // LDS row pitch, elements
+    static constexpr int kPitch = KS;                    // LDS row pitch, elements
+    static constexpr int kRowsPerWindow = kChunks >= 16 ? 1 : 16 / kChunks;
+    static constexpr int kKeyMask = (kChunks >= 16 ? 16 : kChunks) - 1;
     static constexpr int kTotal = ROWS * kChunks;
     static constexpr int kPerThread = (kTotal + NT - 1) / NT;
+
+    __device__ __forceinline__ static int key(int row) { return (row / kRowsPerWindow) & kKeyMask; }
+
+    // element offset of chunk c of row `row`
+    __device__ __forceinline__ static int at(int row, int c) { return row * kPitch + (c ^ key(row)) * kPer16; }
 
     // rows past rows_valid read the last valid row (never stored)
     __device__ __forceinline__ static void load(u32x4 (&v)[kPerThread], const E* __restrict__ g, int64_t ld,
@@ -183,7 +195,19 @@ struct Stager {
             if (kTotal % NT != 0 && i >= kTotal)
                 break;
             const int row = i / kChunks, c = i % kChunks;
-            *reinterpret_cast<u32x4*>(lds + row * kPitch + c * kPer16) = v[j];
+            *reinterpret_cast<u32x4*>(lds + at(row, c)) = v[j];
+        }
+    }
+    // one lane's slot of k block kbl: the eight elements kbl*32 + 8g .. +7
+    template <typename Op>
+    __device__ __forceinline__ static void frag(FragOf<Op>& f, const E* __restrict__ lds, int row, int kbl, int g)
+    {
+        if constexpr (sizeof(E) == 4) {
+            const int c = kbl * 8 + 2 * g;
+            f.lo = *reinterpret_cast<const f32x4*>(lds + at(row, c));
+            f.hi = *reinterpret_cast<const f32x4*>(lds + at(row, c + 1));
+        } else {
+            load_frag<Op>(f, lds + at(row, kbl * 4 + g));
         }
     }
 };
@@ -198,7 +222,7 @@ __device__ __forceinline__ int xcd_tile(int it, int tiles, int grid)
     return (it & 7) * (tiles >> 3) + (it >> 3);
 }
 
-template <typename OX, typename OW, int BM, int BN, int WM, int WN, int KBS>
+template <typename OX, typename OW, int BM, int BN, int WM, int WN, int KBS, int PD>
 __global__ __launch_bounds__(WM * WN * 64) void k_persistent(LinearArgs a, int kbpt, int tiles_m, int tiles_n)
 {
     using EX = typename OX::elem;
@@ -232,20 +256,10 @@ __global__ __launch_bounds__(WM * WN * 64) void k_persistent(LinearArgs a, int k
                 part[fm][fn] = acc[fm][fn];
             }
 
-        // prologue: stage 0 in LDS, stage 1 in flight in registers
-        u32x4 rx[SX::kPerThread], rw[SW::kPerThread];
-        SX::load(rx, xg, a.ldx, m0, a.M, 0, tid);
-        SW::load(rw, wg, a.ldw, n0, a.N, 0, tid);
-        SX::store(sx[0], rx, tid);
-        SW::store(sw[0], rw, tid);
-        if (nstages > 1) {
-            SX::load(rx, xg, a.ldx, m0, a.M, KS, tid);
-            SW::load(rw, wg, a.ldw, n0, a.N, KS, tid);
-        }
-        __syncthreads();
-
-        for (int st = 0; st < nstages; ++st) {
-            const int buf = st & 1;
+        // The k loop keeps two stages in flight in registers (two register
+        // sets, alternating by stage parity) while a third feeds the MFMAs
+        // from LDS: a stage is loaded two iterations before it is stored.
+        auto compute = [&](int buf, int st) {
 #pragma unroll
             for (int kbl = 0; kbl < KBS; ++kbl) {
                 const int kb = st * KBS + kbl;
@@ -260,12 +274,10 @@ __global__ __launch_bounds__(WM * WN * 64) void k_persistent(LinearArgs a, int k
                 FragOf<OW> wf[FN];
 #pragma unroll
                 for (int fm = 0; fm < FM; ++fm)
-                    load_frag<OX>(xf[fm], sx[buf] + (wm * FM * 16 + fm * 16 + r) * SX::kPitch + kbl * kKBlock +
-                                              kSlotLen * g);
+                    SX::template frag<OX>(xf[fm], sx[buf], wm * FM * 16 + fm * 16 + r, kbl, g);
 #pragma unroll
                 for (int fn = 0; fn < FN; ++fn)
-                    load_frag<OW>(wf[fn], sw[buf] + (wn * FN * 16 + fn * 16 + r) * SW::kPitch + kbl * kKBlock +
-                                              kSlotLen * g);
+                    SW::template frag<OW>(wf[fn], sw[buf], wn * FN * 16 + fn * 16 + r, kbl, g);
                 mfma_tiles<FM, FN>(xf, wf, part);
                 if (kb % kbpt == kbpt - 1) {
                     const bool first = kb < kbpt;
@@ -276,16 +288,74 @@ __global__ __launch_bounds__(WM * WN * 64) void k_persistent(LinearArgs a, int k
                             acc[fm][fn] = first ? part[fm][fn] : acc[fm][fn] + part[fm][fn];
                 }
             }
-            // the other buffer was last read before the previous barrier
+        };
+        if constexpr (PD == 2) {
+        u32x4 rx0[SX::kPerThread], rw0[SW::kPerThread], rx1[SX::kPerThread], rw1[SW::kPerThread];
+        SX::load(rx0, xg, a.ldx, m0, a.M, 0, tid);
+        SW::load(rw0, wg, a.ldw, n0, a.N, 0, tid);
+        if (nstages > 1) {
+            SX::load(rx1, xg, a.ldx, m0, a.M, KS, tid);
+            SW::load(rw1, wg, a.ldw, n0, a.N, KS, tid);
+        }
+        SX::store(sx[0], rx0, tid);
+        SW::store(sw[0], rw0, tid);
+        if (nstages > 2) {
+            SX::load(rx0, xg, a.ldx, m0, a.M, (int64_t)2 * KS, tid);
+            SW::load(rw0, wg, a.ldw, n0, a.N, (int64_t)2 * KS, tid);
+        }
+        __syncthreads();
+        for (int st = 0; st < nstages; st += 2) {
+            // even stage: set 1 holds stage st+1, set 0 holds stage st+2
+            compute(0, st);
             if (st + 1 < nstages) {
-                SX::store(sx[buf ^ 1], rx, tid);
-                SW::store(sw[buf ^ 1], rw, tid);
+                SX::store(sx[1], rx1, tid);
+                SW::store(sw[1], rw1, tid);
             }
-            if (st + 2 < nstages) {
-                SX::load(rx, xg, a.ldx, m0, a.M, (int64_t)(st + 2) * KS, tid);
-                SW::load(rw, wg, a.ldw, n0, a.N, (int64_t)(st + 2) * KS, tid);
+            if (st + 3 < nstages) {
+                SX::load(rx1, xg, a.ldx, m0, a.M, (int64_t)(st + 3) * KS, tid);
+                SW::load(rw1, wg, a.ldw, n0, a.N, (int64_t)(st + 3) * KS, tid);
             }
             __syncthreads();
+            if (st + 1 >= nstages)
+                break;
+            // odd stage: set 0 holds stage st+2, set 1 holds stage st+3
+            compute(1, st + 1);
+            if (st + 2 < nstages) {
+                SX::store(sx[0], rx0, tid);
+                SW::store(sw[0], rw0, tid);
+            }
+            if (st + 4 < nstages) {
+                SX::load(rx0, xg, a.ldx, m0, a.M, (int64_t)(st + 4) * KS, tid);
+                SW::load(rw0, wg, a.ldw, n0, a.N, (int64_t)(st + 4) * KS, tid);
+            }
+            __syncthreads();
+        }
+        } else {
+            // one stage in flight (shapes whose accumulators leave no room
+            // for a second register set)
+            u32x4 rx[SX::kPerThread], rw[SW::kPerThread];
+            SX::load(rx, xg, a.ldx, m0, a.M, 0, tid);
+            SW::load(rw, wg, a.ldw, n0, a.N, 0, tid);
+            SX::store(sx[0], rx, tid);
+            SW::store(sw[0], rw, tid);
+            if (nstages > 1) {
+                SX::load(rx, xg, a.ldx, m0, a.M, KS, tid);
+                SW::load(rw, wg, a.ldw, n0, a.N, KS, tid);
+            }
+            __syncthreads();
+            for (int st = 0; st < nstages; ++st) {
+                const int buf = st & 1;
+                compute(buf, st);
+                if (st + 1 < nstages) {
+                    SX::store(sx[buf ^ 1], rx, tid);
+                    SW::store(sw[buf ^ 1], rw, tid);
+                }
+                if (st + 2 < nstages) {
+                    SX::load(rx, xg, a.ldx, m0, a.M, (int64_t)(st + 2) * KS, tid);
+                    SW::load(rw, wg, a.ldw, n0, a.N, (int64_t)(st + 2) * KS, tid);
+                }
+                __syncthreads();
+            }
         }
 
 #pragma unroll
@@ -312,9 +382,19 @@ static hipError_t launch_decode_mt(const LinearArgs& a, const Plan& p, f32x4* pa
             ch = c;
             break;
         }
+    if constexpr (kMaxCH >= 16) {
+        if (ch == 16) {
+            k_decode<OX, OW, 16, MT><<<grid, 64, 0, s>>>(a, kbpt, p.tiles_k, p.mtiles, partials);
+            return hipGetLastError();
+        }
+    }
+    if constexpr (kMaxCH >= 8) {
+        if (ch == 8) {
+            k_decode<OX, OW, 8, MT><<<grid, 64, 0, s>>>(a, kbpt, p.tiles_k, p.mtiles, partials);
+            return hipGetLastError();
+        }
+    }
     switch (ch) {
-    case 16: k_decode<OX, OW, 16, MT><<<grid, 64, 0, s>>>(a, kbpt, p.tiles_k, p.mtiles, partials); break;
-    case 8:  k_decode<OX, OW, 8, MT><<<grid, 64, 0, s>>>(a, kbpt, p.tiles_k, p.mtiles, partials); break;
     case 4:  k_decode<OX, OW, 4, MT><<<grid, 64, 0, s>>>(a, kbpt, p.tiles_k, p.mtiles, partials); break;
     case 2:  k_decode<OX, OW, 2, MT><<<grid, 64, 0, s>>>(a, kbpt, p.tiles_k, p.mtiles, partials); break;
     default: k_decode<OX, OW, 1, MT><<<grid, 64, 0, s>>>(a, kbpt, p.tiles_k, p.mtiles, partials); break;
@@ -342,7 +422,7 @@ static hipError_t launch_decode(const LinearArgs& a, const Plan& p, void* ws, hi
     return hipGetLastError();
 }
 
-template <typename OX, typename OW, int BM, int BN, int WM, int WN, int KBS>
+template <typename OX, typename OW, int BM, int BN, int WM, int WN, int KBS, int PD = 2>
 static hipError_t launch_persistent_t(const LinearArgs& a, const Plan& p, hipStream_t s)
 {
     // the k loop walks whole stages: K must be a multiple of the stage width
@@ -352,7 +432,7 @@ static hipError_t launch_persistent_t(const LinearArgs& a, const Plan& p, hipStr
     const int tiles_n = (a.N + BN - 1) / BN;
     const int tiles = tiles_m * tiles_n;
     const int grid = min(tiles, device_cu_count() * 2);
-    k_persistent<OX, OW, BM, BN, WM, WN, KBS><<<grid, WM * WN * 64, 0, s>>>(a, p.kbpt, tiles_m, tiles_n);
+    k_persistent<OX, OW, BM, BN, WM, WN, KBS, PD><<<grid, WM * WN * 64, 0, s>>>(a, p.kbpt, tiles_m, tiles_n);
     return hipGetLastError();
 }
 
@@ -397,8 +477,8 @@ static hipError_t launch_persistent(const LinearArgs& a, const Plan& p, hipStrea
         case 11: return launch_persistent_t<OX, OW, 128, 128, 2, 2, 2>(a, p, s);
         case 12: return launch_persistent_t<OX, OW, 64, 64, 2, 2, 2>(a, p, s);
         case 13: return launch_persistent_t<OX, OW, 128, 128, 2, 2, 4>(a, p, s);
-        case 14: return launch_persistent_t<OX, OW, 256, 128, 4, 2, 2>(a, p, s);
-        case 15: return launch_persistent_t<OX, OW, 128, 256, 2, 4, 2>(a, p, s);
+        case 14: return launch_persistent_t<OX, OW, 256, 128, 4, 2, 2, 1>(a, p, s);
+        case 15: return launch_persistent_t<OX, OW, 128, 256, 2, 4, 2, 1>(a, p, s);
         case 16: return launch_persistent_t<OX, OW, 64, 128, 2, 2, 4>(a, p, s);
         default: return launch_persistent_t<OX, OW, 64, 64, 2, 2, 1>(a, p, s);
         }
