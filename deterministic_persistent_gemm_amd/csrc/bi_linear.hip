@@ -85,9 +85,11 @@ __global__ __launch_bounds__(64) void k_decode(LinearArgs a, int kbpt, int tiles
 #pragma unroll
     for (int m = 0; m < MT; ++m)
         P[m][0] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int c = 0; c < kbpt; c += CH) {
-        FragOf<OW> wf[CH][1];
-        FragOf<OX> xf[CH][MT];
+    // Chunks of CH k blocks; while one chunk feeds the chain the next one's
+    // loads are in flight (two fragment buffers, loop unrolled by two).
+    FragOf<OW> wf0[CH][1], wf1[CH][1];
+    FragOf<OX> xf0[CH][MT], xf1[CH][MT];
+    auto load_chunk = [&](FragOf<OW> (&wf)[CH][1], FragOf<OX> (&xf)[CH][MT], int c) {
 #pragma unroll
         for (int i = 0; i < CH; ++i)
             load_frag<OW>(wf[i][0], wp + (int64_t)(c + i) * kKBlock);
@@ -96,12 +98,25 @@ __global__ __launch_bounds__(64) void k_decode(LinearArgs a, int kbpt, int tiles
 #pragma unroll
             for (int i = 0; i < CH; ++i)
                 load_frag<OX>(xf[i][m], xp[m] + (int64_t)(c + i) * kKBlock);
-        // every load of the chunk is in flight before the first instruction
-        // of the chain waits on one (memory-level parallelism for streaming)
-        __builtin_amdgcn_sched_barrier(0);
+    };
+    auto run_chunk = [&](FragOf<OW> (&wf)[CH][1], FragOf<OX> (&xf)[CH][MT]) {
 #pragma unroll
         for (int i = 0; i < CH; ++i)
             mfma_tiles<MT, 1>(xf[i], wf[i], P);
+    };
+    load_chunk(wf0, xf0, 0);
+    for (int c = 0; c < kbpt; c += 2 * CH) {
+        if (c + CH < kbpt)
+            load_chunk(wf1, xf1, c + CH);
+        // every load issued so far is in flight before the chain waits on one
+        __builtin_amdgcn_sched_barrier(0);
+        run_chunk(wf0, xf0);
+        if (c + CH >= kbpt)
+            break;
+        if (c + 2 * CH < kbpt)
+            load_chunk(wf0, xf0, c + 2 * CH);
+        __builtin_amdgcn_sched_barrier(0);
+        run_chunk(wf1, xf1);
     }
 
     const int col = nt * 16 + acc_col(lane);
@@ -222,7 +237,9 @@ __device__ __forceinline__ int xcd_tile(int it, int tiles, int grid)
     return (it & 7) * (tiles >> 3) + (it >> 3);
 }
 
-template <typename OX, typename OW, int BM, int BN, int WM, int WN, int KBS, int PD>
+// CHAINED: the recipe has a single k tile (block_k == K), so the chain runs
+// straight into the accumulator and no partial registers are needed.
+template <typename OX, typename OW, int BM, int BN, int WM, int WN, int KBS, int PD, bool CHAINED>
 __global__ __launch_bounds__(WM * WN * 64) void k_persistent(LinearArgs a, int kbpt, int tiles_m, int tiles_n)
 {
     using EX = typename OX::elem;
@@ -262,6 +279,18 @@ __global__ __launch_bounds__(WM * WN * 64) void k_persistent(LinearArgs a, int k
         auto compute = [&](int buf, int st) {
 #pragma unroll
             for (int kbl = 0; kbl < KBS; ++kbl) {
+                if constexpr (CHAINED) {
+                    FragOf<OX> xf[FM];
+                    FragOf<OW> wf[FN];
+#pragma unroll
+                    for (int fm = 0; fm < FM; ++fm)
+                        SX::template frag<OX>(xf[fm], sx[buf], wm * FM * 16 + fm * 16 + r, kbl, g);
+#pragma unroll
+                    for (int fn = 0; fn < FN; ++fn)
+                        SW::template frag<OW>(wf[fn], sw[buf], wn * FN * 16 + fn * 16 + r, kbl, g);
+                    mfma_tiles<FM, FN>(xf, wf, acc);
+                    continue;
+                }
                 const int kb = st * KBS + kbl;
                 if (kb % kbpt == 0) {
 #pragma unroll
@@ -374,8 +403,9 @@ static hipError_t launch_decode_mt(const LinearArgs& a, const Plan& p, f32x4* pa
 {
     dim3 grid((unsigned)(p.ntiles * p.tiles_k), (unsigned)((p.mtiles + MT - 1) / MT));
     const int kbpt = p.kbpt;
-    // register budget per chunk of k blocks: W fragments plus MT X fragments
-    constexpr int kMaxCH = (OX::f32_frag ? 8 : 16) / (MT > 2 ? 2 : 1);
+    // register budget per chunk of k blocks (two buffers of W fragments plus
+    // MT X fragments)
+    constexpr int kMaxCH = (OX::f32_frag ? 4 : 8) / (MT > 2 ? 2 : 1);
     int ch = 1;
     for (int c = kMaxCH; c >= 1; c >>= 1)
         if (kbpt % c == 0) {
@@ -422,7 +452,7 @@ static hipError_t launch_decode(const LinearArgs& a, const Plan& p, void* ws, hi
     return hipGetLastError();
 }
 
-template <typename OX, typename OW, int BM, int BN, int WM, int WN, int KBS, int PD = 2>
+template <typename OX, typename OW, int BM, int BN, int WM, int WN, int KBS, int PD = 2, int PDC = PD>
 static hipError_t launch_persistent_t(const LinearArgs& a, const Plan& p, hipStream_t s)
 {
     // the k loop walks whole stages: K must be a multiple of the stage width
@@ -432,7 +462,17 @@ static hipError_t launch_persistent_t(const LinearArgs& a, const Plan& p, hipStr
     const int tiles_n = (a.N + BN - 1) / BN;
     const int tiles = tiles_m * tiles_n;
     const int grid = min(tiles, device_cu_count() * 2);
-    k_persistent<OX, OW, BM, BN, WM, WN, KBS, PD><<<grid, WM * WN * 64, 0, s>>>(a, p.kbpt, tiles_m, tiles_n);
+    if (p.tiles_k == 1) {
+        k_persistent<OX, OW, BM, BN, WM, WN, KBS, PDC, true><<<grid, WM * WN * 64, 0, s>>>(a, p.kbpt, tiles_m, tiles_n);
+    } else {
+        // the largest tiles exist only in the chained form (the dispatcher
+        // never selects them for a recipe with several k tiles)
+        if constexpr (BM * BN >= 256 * 256)
+            return hipErrorInvalidValue;
+        else
+            k_persistent<OX, OW, BM, BN, WM, WN, KBS, PD, false><<<grid, WM * WN * 64, 0, s>>>(a, p.kbpt, tiles_m,
+                                                                                              tiles_n);
+    }
     return hipGetLastError();
 }
 
@@ -473,12 +513,17 @@ static hipError_t launch_persistent(const LinearArgs& a, const Plan& p, hipStrea
             code = tiles(128, 256) >= cus ? 15 : 12;
         if (a.K % stage_k(code) != 0)
             code = 17;
+        // 256x256 tiles only fit the registers without tile partials
+        if ((code == 18 || code == 19) && p.tiles_k != 1)
+            code = 15;
         switch (code) {
         case 11: return launch_persistent_t<OX, OW, 128, 128, 2, 2, 2>(a, p, s);
         case 12: return launch_persistent_t<OX, OW, 64, 64, 2, 2, 2>(a, p, s);
         case 13: return launch_persistent_t<OX, OW, 128, 128, 2, 2, 4>(a, p, s);
-        case 14: return launch_persistent_t<OX, OW, 256, 128, 4, 2, 2, 1>(a, p, s);
-        case 15: return launch_persistent_t<OX, OW, 128, 256, 2, 4, 2, 1>(a, p, s);
+        case 14: return launch_persistent_t<OX, OW, 256, 128, 4, 2, 2, 1, 1>(a, p, s);
+        case 15: return launch_persistent_t<OX, OW, 128, 256, 2, 4, 2, 1, 1>(a, p, s);
+        case 18: return launch_persistent_t<OX, OW, 256, 256, 2, 4, 2, 1, 1>(a, p, s);
+        case 19: return launch_persistent_t<OX, OW, 256, 256, 4, 2, 2, 1, 1>(a, p, s);
         case 16: return launch_persistent_t<OX, OW, 64, 128, 2, 2, 4>(a, p, s);
         default: return launch_persistent_t<OX, OW, 64, 64, 2, 2, 1>(a, p, s);
         }

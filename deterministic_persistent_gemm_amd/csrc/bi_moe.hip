@@ -333,9 +333,11 @@ __global__ __launch_bounds__(TW * NW * 64) void k_grouped(GroupedArgs g)
             for (int b = 0; b < NB; ++b)
                 P[m][b] = f32x4{0.f, 0.f, 0.f, 0.f};
         const int64_t k0 = (int64_t)t * g.kbpt * kKBlock;
-        for (int c = 0; c < g.kbpt; c += CH) {
-            Frag<false> af[CH][MT];
-            Frag<false> bf[CH][NB];
+        // chunks of CH k blocks, the next chunk's loads in flight while the
+        // current one feeds the chains (two fragment buffers)
+        Frag<false> af0[CH][MT], af1[CH][MT];
+        Frag<false> bf0[CH][NB], bf1[CH][NB];
+        auto load_chunk = [&](Frag<false> (&af)[CH][MT], Frag<false> (&bf)[CH][NB], int c) {
 #pragma unroll
             for (int i = 0; i < CH; ++i) {
 #pragma unroll
@@ -345,10 +347,24 @@ __global__ __launch_bounds__(TW * NW * 64) void k_grouped(GroupedArgs g)
                 for (int m = 0; m < MT; ++m)
                     load_frag<BF16>(af[i][m], ap[m] + k0 + (int64_t)(c + i) * kKBlock);
             }
-            __builtin_amdgcn_sched_barrier(0);
+        };
+        auto run_chunk = [&](Frag<false> (&af)[CH][MT], Frag<false> (&bf)[CH][NB]) {
 #pragma unroll
             for (int i = 0; i < CH; ++i)
                 mfma_tiles<MT, NB>(af[i], bf[i], P);
+        };
+        load_chunk(af0, bf0, 0);
+        for (int c = 0; c < g.kbpt; c += 2 * CH) {
+            if (c + CH < g.kbpt)
+                load_chunk(af1, bf1, c + CH);
+            __builtin_amdgcn_sched_barrier(0);
+            run_chunk(af0, bf0);
+            if (c + CH >= g.kbpt)
+                break;
+            if (c + 2 * CH < g.kbpt)
+                load_chunk(af0, bf0, c + 2 * CH);
+            __builtin_amdgcn_sched_barrier(0);
+            run_chunk(af1, bf1);
         }
         if (TW == 1) {
 #pragma unroll
@@ -436,12 +452,14 @@ static hipError_t launch_grouped_tw(const GroupedArgs& g, int64_t max_units, hip
 {
     const int ntiles = (g.n_out / 16 + NW - 1) / NW;
     dim3 grid((unsigned)ntiles, (unsigned)max_units);
-    // register budget: CH k blocks of MT activation and NB weight fragments
+    // register budget: two buffers of CH k blocks of MT activation and NB
+    // weight fragments
     int ch = pick_ch(g.kbpt);
-    if (MT * (SWIGLU ? 2 : 1) > 2 && ch > 8)
+    if (ch > 8)
         ch = 8;
+    if (MT * (SWIGLU ? 2 : 1) > 2 && ch > 4)
+        ch = 4;
     switch (ch) {
-    case 16: k_grouped<TW, NW, MT, SWIGLU, 16><<<grid, TW * NW * 64, 0, s>>>(g); break;
     case 8:  k_grouped<TW, NW, MT, SWIGLU, 8><<<grid, TW * NW * 64, 0, s>>>(g); break;
     case 4:  k_grouped<TW, NW, MT, SWIGLU, 4><<<grid, TW * NW * 64, 0, s>>>(g); break;
     case 2:  k_grouped<TW, NW, MT, SWIGLU, 2><<<grid, TW * NW * 64, 0, s>>>(g); break;

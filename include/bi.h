@@ -160,7 +160,8 @@ const char* bi_status_str(bi_status_t status);
  * 128-k stages;
  * bf16: 11 = 128x128, 12 = 64x64, 13 = 128x128 with 128-k stages,
  * 14 = 256x128, 15 = 128x256, 16 = 64x128 with 128-k stages, 17 = 64x64
- * with 32-k stages).  Tile shapes never change the numerics. */
+ * with 32-k stages, 18 = 256x256 on 2x4 waves, 19 = 256x256 on 4x2 waves).
+ * Tile shapes never change the numerics. */
 enum { BI_PATH_AUTO = 0, BI_PATH_DECODE = 1, BI_PATH_PERSISTENT = 2 };
 
 /* The same linear layer with an explicit recipe and an explicit kernel path,

@@ -46,9 +46,11 @@ def test_recipe_is_a_function_of_the_key():
     assert r1 == r2
     assert r1["mfma"] == bi.BI_MFMA_F32_16X16X4_F32 and r1["block_k"] == 128 and r1["bias_last"] == 1
     rb = bi.bi_describe_recipe(bi.BI_BF16, 4096, 4096).as_dict()
-    assert rb["mfma"] == bi.BI_MFMA_F32_16X16X32_BF16 and 4096 % rb["block_k"] == 0
+    assert rb["mfma"] == bi.BI_MFMA_F32_16X16X32_BF16 and rb["block_k"] == 4096   # fully chained
     # keys whose K is not a multiple of the tile width fall back to one chain
     assert bi.bi_describe_recipe(bi.BI_BF16, 2048, 768).block_k == 768
+    # narrower bf16 keys (the MoE gate|up projection) use 512-k tile partials
+    assert bi.bi_describe_recipe(bi.BI_BF16, 1536, 2048).block_k == 512
     assert bi.bi_describe_recipe(bi.BI_F32, 32, 256).block_k == 128
 
 

@@ -102,13 +102,16 @@ def test_bf16_with_bias_and_ragged_m(bi):
         assert_bitwise(y[M - 1], solo, f"last row at M={M}")
 
 
-def test_every_bf16_tile_shape_gives_the_same_bits(bi):
+@pytest.mark.parametrize("K", [1024, 768])
+def test_every_bf16_tile_shape_gives_the_same_bits(bi, K):
+    # K=1024 keys use two 512-k tile partials; K=768 is fully chained, the
+    # only form the 256x256 shapes (codes 18, 19) exist in
     g = np.random.default_rng(47)
-    w = wl.normal_bf16(g, (320, 1024), 0.02)
-    x = dev(wl.normal_bf16(g, (300, 1024), 1.0))
+    w = wl.normal_bf16(g, (320, K), 0.02)
+    x = dev(wl.normal_bf16(g, (300, K), 1.0))
     wd = dev(w)
     ref = host(bi.bi_linear_bf16(x, weight_t(wd), None))
-    for code in range(11, 18):
-        banner(f"bf16 M=300 N=320 persistent tile code {code}")
+    for code in range(11, 20):
+        banner(f"bf16 M=300 N=320 K={K} persistent tile code {code}")
         y = host(bi.bi_lab_linear(x, weight_t(wd), None, path=bi.BI_PATH_PERSISTENT | (code << 8)))
         assert_bitwise(y, ref, f"bf16 tile code {code}")
