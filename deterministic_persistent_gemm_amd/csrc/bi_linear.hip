@@ -1,20 +1,24 @@
 // bi_linear.hip -- batch-invariant linear layer kernels for gfx950.
 //
-// Two kernel shapes carry out one recipe (bi_device.h) bit for bit:
+// Three kernel shapes carry out one recipe (bi_device.h) bit for bit:
 //
-//  * k_decode (small M): one wave per (16-row M tile, 16-column N tile, k tile
-//    partial).  The k tile partials of one output tile are computed on
-//    different compute units, so the weight streams through the whole chip
-//    and every weight element is fetched by exactly one wave (for M <= 16).
-//    The last wave to finish an output tile -- elected with a device-scope
-//    counter -- adds the partials in ascending tile order, adds the bias and
-//    stores.  The counter is reset by that wave, so the workspace stays clean.
+//  * k_decode + k_decode_fold (small M): one wave per (16-column N tile, k
+//    tile partial, group of 16-row M tiles).  The k tile partials of one
+//    output tile are computed on different compute units, so the weight
+//    streams through the whole chip and every weight element is fetched from
+//    HBM once.  A second launch adds the partials in ascending tile order,
+//    adds the bias and stores; the kernel boundary is the only
+//    synchronisation (no device-wide fences, no counters).
 //
-//  * k_persistent (large M): a grid of at most a few workgroups per compute
-//    unit loops over BM x BN output tiles.  Each k block of X and W is staged
-//    through LDS with coalesced 16-byte loads (rows padded by 16 bytes so the
-//    lanes' fragment reads spread over the banks); the tile partials are
-//    chained in registers and added in ascending order, exactly as above.
+//  * k_decode_wg (small M, short K): one workgroup per 16x16 output tile;
+//    its waves compute the tile partials and fold them through LDS in one
+//    launch.
+//
+//  * k_persistent (large M): a grid of at most two workgroups per compute
+//    unit loops over BM x BN output tiles.  Stages of k blocks of X and W go
+//    through LDS (16-byte loads along k, XOR-swizzled rows), the next stages
+//    are prefetched into registers, and the tile partials are chained in
+//    registers and added in ascending order, exactly as above.
 //
 // GateLinear page, section "Update: is the M=4096 cost avoidable?": decode is
 // latency-bound and wants many small pieces of work, while M=4096 wants few
@@ -160,6 +164,80 @@ __global__ __launch_bounds__(64) void k_decode_fold(LinearArgs a, int tiles_k,
             if (i < n)
                 acc = (u0 + i == 0) ? v[i] : acc + v[i];
     }
+    store_acc(a, row0, nt * 16 + acc_col(lane), acc);
+}
+
+// One workgroup per (16-row M tile, 16-column N tile), NW waves.  Wave w
+// computes the tile partials t = w, w + NW, w + 2 NW, ... (each a chain from
+// zero over its own k blocks) and leaves them in LDS; after one barrier wave 0
+// adds them in ascending tile order, adds the bias and stores.  The whole
+// reduction of an output tile stays inside one compute unit, so one launch
+// does the work of k_decode + k_decode_fold with no workspace.  A wave walks
+// its k blocks as one flattened sequence in chunks of CH (CH divides kbpt, so
+// no chunk straddles two partials) with the next chunk's loads in flight.
+template <typename OX, typename OW, int CH, int NW>
+__global__ __launch_bounds__(NW * 64) void k_decode_wg(LinearArgs a, int kbpt, int tiles_k)
+{
+    using EX = typename OX::elem;
+    using EW = typename OW::elem;
+    extern __shared__ f32x4 lds_part[];   // [tiles_k][64]
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int r = lane & 15, g = lane >> 4;
+    const int nt = blockIdx.x, mt = blockIdx.y;
+    const int nblk = (tiles_k > w ? (tiles_k - w + NW - 1) / NW : 0) * kbpt;
+
+    const EW* wp = reinterpret_cast<const EW*>(a.w) + (int64_t)(nt * 16 + r) * a.ldw + kSlotLen * g;
+    // rows past M read row M-1 (always valid); their results are never stored
+    const int xrow = min(mt * 16 + r, a.M - 1);
+    const EX* xp = reinterpret_cast<const EX*>(a.x) + (int64_t)xrow * a.ldx + kSlotLen * g;
+    // k offset of the c-th block of this wave's sequence
+    auto koff = [&](int c) {
+        const int j = c / kbpt;
+        return (int64_t)((w + j * NW) * kbpt + (c - j * kbpt)) * kKBlock;
+    };
+
+    f32x4 P[1][1];
+    FragOf<OW> wf0[CH][1], wf1[CH][1];
+    FragOf<OX> xf0[CH][1], xf1[CH][1];
+    auto load_chunk = [&](FragOf<OW> (&wf)[CH][1], FragOf<OX> (&xf)[CH][1], int c) {
+#pragma unroll
+        for (int i = 0; i < CH; ++i) {
+            const int64_t o = koff(c + i);
+            load_frag<OW>(wf[i][0], wp + o);
+            load_frag<OX>(xf[i][0], xp + o);
+        }
+    };
+    auto run_chunk = [&](FragOf<OW> (&wf)[CH][1], FragOf<OX> (&xf)[CH][1], int c) {
+        if (c % kbpt == 0)
+            P[0][0] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < CH; ++i)
+            mfma_tiles<1, 1>(xf[i], wf[i], P);
+        if ((c + CH) % kbpt == 0)
+            lds_part[(w + (c / kbpt) * NW) * 64 + lane] = P[0][0];
+    };
+    if (nblk > 0) {
+        load_chunk(wf0, xf0, 0);
+        for (int c = 0; c < nblk; c += 2 * CH) {
+            if (c + CH < nblk)
+                load_chunk(wf1, xf1, c + CH);
+            __builtin_amdgcn_sched_barrier(0);
+            run_chunk(wf0, xf0, c);
+            if (c + CH >= nblk)
+                break;
+            if (c + 2 * CH < nblk)
+                load_chunk(wf0, xf0, c + 2 * CH);
+            __builtin_amdgcn_sched_barrier(0);
+            run_chunk(wf1, xf1, c + CH);
+        }
+    }
+    __syncthreads();
+    if (w != 0)
+        return;
+    const int row0 = mt * 16 + acc_row(lane, 0);
+    f32x4 acc = lds_part[lane];
+    for (int t = 1; t < tiles_k; ++t)
+        acc = acc + lds_part[t * 64 + lane];
     store_acc(a, row0, nt * 16 + acc_col(lane), acc);
 }
 
@@ -452,6 +530,51 @@ static hipError_t launch_decode(const LinearArgs& a, const Plan& p, void* ws, hi
     return hipGetLastError();
 }
 
+template <typename OX, typename OW, int NW>
+static hipError_t launch_decode_wg_nw(const LinearArgs& a, const Plan& p, hipStream_t s)
+{
+    const dim3 grid((unsigned)p.ntiles, (unsigned)p.mtiles);
+    const size_t lds = (size_t)p.tiles_k * 64 * sizeof(f32x4);
+    // CH k blocks per chunk, two chunks in flight; CH must divide kbpt.  The
+    // register budget per wave shrinks as NW grows (NW / 4 waves per SIMD).
+    constexpr int kMaxCH = (OX::f32_frag ? 2 : 4) * (NW <= 4 ? 2 : 1);
+    int ch = 1;
+    for (int c = kMaxCH; c >= 1; c >>= 1)
+        if (p.kbpt % c == 0) {
+            ch = c;
+            break;
+        }
+    if constexpr (kMaxCH >= 8) {
+        if (ch == 8) {
+            k_decode_wg<OX, OW, 8, NW><<<grid, NW * 64, lds, s>>>(a, p.kbpt, p.tiles_k);
+            return hipGetLastError();
+        }
+    }
+    if constexpr (kMaxCH >= 4) {
+        if (ch == 4) {
+            k_decode_wg<OX, OW, 4, NW><<<grid, NW * 64, lds, s>>>(a, p.kbpt, p.tiles_k);
+            return hipGetLastError();
+        }
+    }
+    if (ch == 2)
+        k_decode_wg<OX, OW, 2, NW><<<grid, NW * 64, lds, s>>>(a, p.kbpt, p.tiles_k);
+    else
+        k_decode_wg<OX, OW, 1, NW><<<grid, NW * 64, lds, s>>>(a, p.kbpt, p.tiles_k);
+    return hipGetLastError();
+}
+
+template <typename OX, typename OW>
+static hipError_t launch_decode_wg(const LinearArgs& a, const Plan& p, hipStream_t s)
+{
+    if (p.tiles_k < 2 || p.tiles_k > kDecodeWgMaxTiles)
+        return hipErrorInvalidValue;
+    if (p.tiles_k >= 16)
+        return launch_decode_wg_nw<OX, OW, 16>(a, p, s);
+    if (p.tiles_k >= 8)
+        return launch_decode_wg_nw<OX, OW, 8>(a, p, s);
+    return launch_decode_wg_nw<OX, OW, 4>(a, p, s);
+}
+
 template <typename OX, typename OW, int BM, int BN, int WM, int WN, int KBS, int PD = 2, int PDC = PD>
 static hipError_t launch_persistent_t(const LinearArgs& a, const Plan& p, hipStream_t s)
 {
@@ -507,10 +630,14 @@ static hipError_t launch_persistent(const LinearArgs& a, const Plan& p, hipStrea
         default: return launch_persistent_t<OX, OW, 32, 32, 2, 2, 1>(a, p, s);
         }
     } else {
-        // measured on MI355X for the (bf16, 4096, 4096) GEMM: 128x256 on 8
-        // waves at M=4096 (169 us); 64x64 at M=256 (42 us)
-        if (code == 0)
-            code = tiles(128, 256) >= cus ? 15 : 12;
+        // measured on MI355X for the (bf16, 4096, 4096) GEMM: 256x256 on 4x2
+        // waves at M=4096 (127 us; 128x256: 159 us); 64x64 at M=256 (32 us)
+        if (code == 0) {
+            if (p.tiles_k == 1 && tiles(256, 256) >= cus)
+                code = 19;
+            else
+                code = tiles(128, 256) >= cus ? 15 : 12;
+        }
         if (a.K % stage_k(code) != 0)
             code = 17;
         // 256x256 tiles only fit the registers without tile partials
@@ -533,7 +660,9 @@ static hipError_t launch_persistent(const LinearArgs& a, const Plan& p, hipStrea
 template <typename OX, typename OW>
 static hipError_t launch_typed(const LinearArgs& a, const Plan& p, void* ws, hipStream_t s, bool fold)
 {
-    if (p.path == kPathDecode)
+    if (p.path == kPathDecodeWg && fold)
+        return launch_decode_wg<OX, OW>(a, p, s);
+    if (p.path == kPathDecode || p.path == kPathDecodeWg)
         return launch_decode<OX, OW>(a, p, ws, s, fold);
     return launch_persistent<OX, OW>(a, p, s);
 }

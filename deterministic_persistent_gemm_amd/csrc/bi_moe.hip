@@ -487,6 +487,17 @@ static hipError_t launch_grouped(const GroupedArgs& g, int unit_rows, int64_t ma
                            : launch_grouped_mt<1, SWIGLU>(g, max_units, s);
 }
 
+// The router's plan: the linear layer's own choice, except that at small M
+// the two-launch decode form is used and the routing kernel folds the
+// router's tile partials itself (saving the fold launch).
+static bi_status_t router_plan(const bi_recipe_t& r, int64_t M, int64_t E, int64_t H, Plan* p)
+{
+    bi_status_t st = make_plan(r, BI_PATH_AUTO, M, E, H, p);
+    if (st == BI_OK && p->path == kPathDecodeWg)
+        st = make_plan(r, BI_PATH_DECODE, M, E, H, p);
+    return st;
+}
+
 size_t moe_workspace_size(int64_t M, int64_t H, int64_t E, int64_t I, int64_t topk)
 {
     if (M <= 0 || H <= 0 || E <= 0 || I <= 0 || topk <= 0)
@@ -495,7 +506,7 @@ size_t moe_workspace_size(int64_t M, int64_t H, int64_t E, int64_t I, int64_t to
     if (recipe_for(BI_F32, E, H, &r) != BI_OK)
         return 0;
     Plan p;
-    if (make_plan(r, BI_PATH_AUTO, M, E, H, &p) != BI_OK)
+    if (router_plan(r, M, E, H, &p) != BI_OK)
         return 0;
     return moe_layout(M, H, E, I, topk, p.ws_bytes).total;
 }
@@ -528,7 +539,7 @@ bi_status_t moe_run(const uint16_t* x, const float* w_router, const float* b_rou
     if ((st = recipe_for(BI_BF16, H, I, &r_g2)) != BI_OK)
         return st;
     Plan pr;
-    if ((st = make_plan(r_router, BI_PATH_AUTO, M, E, H, &pr)) != BI_OK)
+    if ((st = router_plan(r_router, M, E, H, &pr)) != BI_OK)
         return st;
     const MoELayout L = moe_layout(M, H, E, I, topk, pr.ws_bytes);
     if (!ws || ws_bytes < L.total || !al16(ws))

@@ -126,12 +126,28 @@ bi_status_t make_plan(const bi_recipe_t& r, int32_t path_req, int64_t M, int64_t
     if (tile_code != 0 && (path_req != BI_PATH_PERSISTENT || !tile_code_valid(r.dtype, tile_code)))
         return BI_EINVAL;
     p.tile_code = tile_code;
+    const bool wg_ok = p.tiles_k >= 2 && p.tiles_k <= kDecodeWgMaxTiles;
     if (path_req == BI_PATH_DECODE)
         p.path = kPathDecode;
-    else if (path_req == BI_PATH_PERSISTENT)
+    else if (path_req == BI_PATH_DECODE_WG) {
+        if (!wg_ok)
+            return BI_EUNSUPPORTED;
+        p.path = kPathDecodeWg;
+    } else if (path_req == BI_PATH_PERSISTENT)
         p.path = kPathPersistent;
-    else if (path_req == BI_PATH_AUTO)
-        p.path = (M <= r.m_decode_max) ? kPathDecode : kPathPersistent;
+    else if (path_req == BI_PATH_AUTO) {
+        // The one-launch decode puts a whole output tile's k reduction on one
+        // compute unit, which then streams 16 rows x K of W by itself; a
+        // compute unit sustains only ~20 GB/s of such loads (measured on
+        // MI355X), so it pays only while that slab is small.  Measured per
+        // call, cold W: (bf16, 1536, 2048) M=1 6.9 vs 9.1 us two-launch;
+        // (fp32, 256, 4096) M=1 13.8 vs 9.6 us.
+        const int64_t slab = K * (r.dtype == BI_F32 ? 4 : 2);
+        if (M > r.m_decode_max)
+            p.path = kPathPersistent;
+        else
+            p.path = (wg_ok && slab <= 4096) ? kPathDecodeWg : kPathDecode;
+    }
     else
         return BI_EINVAL;
     p.ws_bytes = 0;

@@ -8,7 +8,10 @@
 
 namespace bi {
 
-enum Path { kPathDecode = 1, kPathPersistent = 2 };
+enum Path { kPathDecode = 1, kPathPersistent = 2, kPathDecodeWg = 3 };
+
+// Most tile partials the one-launch decode kernel keeps in LDS (64 KiB).
+constexpr int kDecodeWgMaxTiles = 64;
 
 // Persistent-kernel tiling: a workgroup computes a BM x BN output tile with
 // WM x WN waves.  Tiling never changes the numerics.

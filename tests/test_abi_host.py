@@ -89,16 +89,35 @@ def test_unsupported_shape_is_an_error_not_a_fallback():
     assert call_f32(K=4001, ldx=4096, ldw=4096) == bi.BI_EUNSUPPORTED
 
 
+def lab_call(path, ws=NULL, ws_bytes=0, M=1):
+    r = bi.bi_describe_recipe(bi.BI_F32, 256, 4096)
+    return L.bi_lab_linear(FAKE, 4096, FAKE, 4096, None, FAKE, bi.BI_F32, 256, M, 256, 4096,
+                           ctypes.byref(r), path, ws, ws_bytes, None)
+
+
+def lab_ws(path, M):
+    r = bi.bi_describe_recipe(bi.BI_F32, 256, 4096)
+    return L.bi_lab_workspace_size(ctypes.byref(r), path, M, 256, 4096)
+
+
 def test_workspace_required_and_sized():
-    need = L.bi_linear_workspace_size(bi.BI_F32, 1, 256, 4096)
-    assert need > 0
-    assert call_f32() == bi.BI_EWORKSPACE
-    assert call_f32(ws=FAKE, ws_bytes=need - 1) == bi.BI_EWORKSPACE
-    # the persistent path keeps its accumulators in registers: no workspace
+    # the two-launch decode path keeps its tile partials in the workspace
+    need = lab_ws(bi.BI_PATH_DECODE, 1)
+    assert need == 16 * 32 * 64 * 16          # N tiles x k tiles x 64 lanes x f32x4
+    assert lab_call(bi.BI_PATH_DECODE) == bi.BI_EWORKSPACE
+    assert lab_call(bi.BI_PATH_DECODE, ws=FAKE, ws_bytes=need - 1) == bi.BI_EWORKSPACE
+    # ... growing with M
+    sizes = [lab_ws(bi.BI_PATH_DECODE, m) for m in (1, 16, 17, 64, 128)]
+    assert sizes == sorted(sizes) and sizes[0] < sizes[-1]
+    # the one-launch decode path folds in LDS and the persistent path keeps
+    # its accumulators in registers: neither needs a workspace
+    assert lab_ws(bi.BI_PATH_DECODE_WG, 1) == 0 and lab_ws(bi.BI_PATH_PERSISTENT, 1) == 0
     assert L.bi_linear_workspace_size(bi.BI_F32, 4096, 256, 4096) == 0
-    # workspace grows with M on the decode path, never beyond the decode limit
-    sizes = [L.bi_linear_workspace_size(bi.BI_F32, m, 256, 4096) for m in (1, 16, 17, 64, 128)]
-    assert sizes == sorted(sizes)
+    # what the production entry asks for is what it checks
+    for m in (1, 17, 128, 129):
+        need = L.bi_linear_workspace_size(bi.BI_F32, m, 256, 4096)
+        if need:
+            assert call_f32(M=m, ws=FAKE, ws_bytes=need - 1) == bi.BI_EWORKSPACE
 
 
 def test_bf16_entry_validation():
@@ -119,6 +138,13 @@ def test_lab_recipe_validation():
     assert f(*args, ctypes.byref(r), bi.BI_PATH_AUTO, None, 0, None) == bi.BI_EUNSUPPORTED
     r = bi.bi_describe_recipe(bi.BI_F32, 256, 4096)
     assert f(*args, ctypes.byref(r), 9, None, 0, None) == bi.BI_EINVAL
+    # the one-launch decode keeps at most 64 tile partials in LDS, and needs two
+    r.block_k = 32                      # 128 tile partials
+    assert f(*args, ctypes.byref(r), bi.BI_PATH_DECODE_WG, None, 0, None) == bi.BI_EUNSUPPORTED
+    r.block_k = 4096                    # fully chained: nothing to fold
+    assert f(*args, ctypes.byref(r), bi.BI_PATH_DECODE_WG, None, 0, None) == bi.BI_EUNSUPPORTED
+    # tile shapes go with the persistent path only
+    assert f(*args, ctypes.byref(r), bi.BI_PATH_DECODE | (3 << 8), None, 0, None) == bi.BI_EINVAL
 
 
 def test_status_strings():

@@ -100,6 +100,11 @@ def test_bf16_with_bias_and_ragged_m(bi):
         assert_close(y, ref, 1e-5, 1e-4, f"bf16 fp32-out M={M}")
         solo = y[M - 1] if solo is None else solo
         assert_bitwise(y[M - 1], solo, f"last row at M={M}")
+        # every kernel path of this 512-k tile-partial key gives the same bits
+        xd = dev(x)
+        for path in (bi.BI_PATH_DECODE, bi.BI_PATH_DECODE_WG, bi.BI_PATH_PERSISTENT):
+            yp = host(bi.bi_lab_linear(xd, weight_t(wd), bd, path=path, out_dtype=torch.float32))
+            assert_bitwise(yp, y, f"bf16 path {path} at M={M}")
 
 
 @pytest.mark.parametrize("K", [1024, 768])

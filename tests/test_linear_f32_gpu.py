@@ -97,7 +97,31 @@ def test_both_kernel_paths_agree_bitwise(bi, router):
         x = dev(batch.x)
         a = host(bi.bi_lab_linear(x, weight_t(wd), bd, path=bi.BI_PATH_DECODE))
         b = host(bi.bi_lab_linear(x, weight_t(wd), bd, path=bi.BI_PATH_PERSISTENT))
+        c = host(bi.bi_lab_linear(x, weight_t(wd), bd, path=bi.BI_PATH_DECODE_WG))
         assert_bitwise(a, b, f"decode vs persistent at M={M}")
+        assert_bitwise(c, b, f"one-launch decode vs persistent at M={M}")
+
+
+@pytest.mark.parametrize("K,block_k", [(320, 32), (4096, 64), (2048, 128), (512, 256)])
+def test_one_launch_decode_uneven_tile_counts(bi, K, block_k):
+    # 10, 64, 16 and 2 tile partials: waves of the one-launch decode kernel
+    # take unequal numbers of partials, or one each, or the LDS maximum
+    g = np.random.default_rng(K + block_k)
+    N = 48
+    w = (g.standard_normal((N, K)) * 0.02).astype(np.float32)
+    b = (g.standard_normal(N) * 0.01).astype(np.float32)
+    r = bi.bi_describe_recipe(bi.BI_F32, N, K)
+    r.block_k = block_k
+    for M in (1, 19, 40):
+        banner(f"fp32 N={N} K={K} block_k={block_k} M={M} decode paths")
+        x = g.standard_normal((M, K)).astype(np.float32)
+        xd, wd, bd = dev(x), dev(w), dev(b)
+        a = host(bi.bi_lab_linear(xd, weight_t(wd), bd, recipe=r, path=bi.BI_PATH_DECODE))
+        c = host(bi.bi_lab_linear(xd, weight_t(wd), bd, recipe=r, path=bi.BI_PATH_DECODE_WG))
+        p = host(bi.bi_lab_linear(xd, weight_t(wd), bd, recipe=r, path=bi.BI_PATH_PERSISTENT))
+        assert_bitwise(c, a, "one-launch vs two-launch decode")
+        assert_bitwise(c, p, "one-launch decode vs persistent")
+        assert_close(c, oracle.linear_f32(x, w, b), F32_ATOL, F32_RTOL, "oracle")
 
 
 def test_every_persistent_tile_shape_gives_the_same_bits(bi, router):
@@ -285,6 +309,9 @@ def test_block_k_is_part_of_the_recipe(bi, router):
         dec = host(bi.bi_lab_linear(x, weight_t(wd), bd, recipe=r, path=bi.BI_PATH_DECODE))
         per = host(bi.bi_lab_linear(x, weight_t(wd), bd, recipe=r, path=bi.BI_PATH_PERSISTENT))
         assert_bitwise(dec, per, f"paths agree at block_k={bk}")
+        if bk < 4096:
+            wg = host(bi.bi_lab_linear(x, weight_t(wd), bd, recipe=r, path=bi.BI_PATH_DECODE_WG))
+            assert_bitwise(wg, per, f"one-launch decode agrees at block_k={bk}")
     assert not np.array_equal(outs[128].view(np.uint32), outs[256].view(np.uint32))
     assert not np.array_equal(outs[128].view(np.uint32), outs[4096].view(np.uint32))
 
