@@ -1,4 +1,4 @@
-"""CPU oracle for the batch-invariant linear and MoE paths.
+"""CPU oracle for the batch-invariant linear, MoE and indexer top-k paths.
 
 TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
 benchmark's ``cpu_baseline`` leg may import this package.  The HIP library
@@ -48,8 +48,10 @@ def _load():
         lib.oracle_topk.argtypes = [P, P, L, L, L]
         lib.oracle_moe.argtypes = [P, P, P, P, P, L, L, L, L, L, P, P, P, P, P]
         lib.oracle_f64_to_bf16.argtypes = [P, P, L]
+        lib.oracle_topk_rows.argtypes = [P, L, L, L, P, P, L, P, L]
         for f in (lib.oracle_linear_f32, lib.oracle_linear_bf16, lib.oracle_topk,
-                  lib.oracle_moe, lib.oracle_f64_to_bf16, lib.oracle_num_threads):
+                  lib.oracle_moe, lib.oracle_f64_to_bf16, lib.oracle_num_threads,
+                  lib.oracle_topk_rows):
             f.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -119,6 +121,25 @@ def topk(scores, k):
     if _load().oracle_topk(_ptr(s), _ptr(ids), M, E, k):
         raise ValueError("oracle_topk rejected its arguments (NaN score or bad k)")
     return ids
+
+
+def topk_rows(scores, topk, row_start=None, row_end=None):
+    """Indexer top-k per row (Sparse-MLA page, deterministic top-k notes).
+
+    ``scores`` is float32 [rows, cols] (any fp32 bit pattern); ``row_start`` /
+    ``row_end`` are int64 [rows] window bounds (clamped to [0, cols]; None means
+    0 / cols).  Returns int32 [rows, topk]: the selected row-local column
+    indices in ascending order, then -1."""
+    s = _c(scores, np.float32)
+    rows, cols = s.shape
+    rs = _c(row_start, np.int64)
+    re = _c(row_end, np.int64)
+    assert rs is None or rs.shape == (rows,)
+    assert re is None or re.shape == (rows,)
+    out = np.empty((rows, topk), np.int32)
+    if _load().oracle_topk_rows(_ptr(s), cols, rows, cols, _ptr(rs), _ptr(re), topk, _ptr(out), topk):
+        raise ValueError("oracle_topk_rows rejected its arguments")
+    return out
 
 
 def moe(x, w_router, b_router, w13, w2, topk, ids=None):

@@ -26,7 +26,11 @@
  *    review summary: gate|up half-split and a fixed slot-order reduction.
  *  - "[BI][DSv4] Pin sparse-MLA decode and prefill scheduling", commit notes
  *    of the deterministic per-row top-k: score descending, exact ties by
- *    ascending index, -0.0 treated as +0.0.
+ *    ascending index, -0.0 treated as +0.0; for the indexer's top-k, every
+ *    fp32 bit pattern is ranked by a monotone int32 key, lanes outside the
+ *    row's window rank below every lane inside it (validity first), and the
+ *    selection is emitted in ascending column order, row-local, with a -1
+ *    tail.
  */
 #include <math.h>
 #include <stdint.h>
@@ -205,6 +209,98 @@ int oracle_topk(const float* scores, int32_t* ids, long M, long E, long k)
     for (long m = 0; m < M; ++m)
         if (topk_row(scores + m * E, E, k, ids + m * k))
             bad = 1;
+    return bad ? -1 : 0;
+}
+
+/* ------------------------------------------------------- indexer top-k rows */
+
+/* The ranking key of an fp32 score (Sparse-MLA page, deterministic top-k
+ * commit notes): -0.0 is first replaced by +0.0, then the bit pattern b is
+ * read as a signed 32-bit integer and, when the sign bit is set, its 31 low
+ * bits are inverted.  Larger key = larger score for every non-NaN value; the
+ * key also orders every NaN pattern (positive NaNs above +inf, negative NaNs
+ * below -inf, 0xffffffff lowest at INT32_MIN). */
+static int32_t topk_key(float v)
+{
+    uint32_t b;
+    memcpy(&b, &v, 4);
+    if (b == 0x80000000u)
+        b = 0;
+    int32_t k;
+    memcpy(&k, &b, 4);
+    if (k < 0)
+        k = (int32_t)(b ^ 0x7fffffffu);
+    return k;
+}
+
+typedef struct {
+    int valid;
+    int32_t key;
+    long col;
+} topk_lane;
+
+/* Rank order: in-window lanes first, then larger key, then lower column. */
+static int topk_lane_cmp(const void* pa, const void* pb)
+{
+    const topk_lane* a = (const topk_lane*)pa;
+    const topk_lane* b = (const topk_lane*)pb;
+    if (a->valid != b->valid)
+        return a->valid ? -1 : 1;
+    if (a->key != b->key)
+        return a->key > b->key ? -1 : 1;
+    return a->col < b->col ? -1 : (a->col > b->col ? 1 : 0);
+}
+
+static long clamp_long(long v, long lo, long hi) { return v < lo ? lo : (v > hi ? hi : v); }
+
+/* Per-row top-k of an indexer score matrix.  Row r considers columns
+ * [0, cols); its window is [rs, re) with rs = clamp(row_start[r], 0, cols)
+ * and re = clamp(row_end[r], 0, cols) (0 and cols when the arrays are NULL).
+ * The first min(topk, re - rs) lanes of the rank order are selected and
+ * written to out[r, 0..] in ascending column order as row-local indices
+ * (column - rs); the remaining slots of the row hold -1. */
+int oracle_topk_rows(const float* scores, long ld, long rows, long cols,
+                     const int64_t* row_start, const int64_t* row_end, long topk,
+                     int32_t* out, long ld_out)
+{
+    if (rows < 0 || cols < 0 || topk <= 0 || ld < cols || ld_out < topk)
+        return -1;
+    if (rows == 0)
+        return 0;
+    if (!scores || !out)
+        return -1;
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic) reduction(| : bad)
+    for (long r = 0; r < rows; ++r) {
+        const long rs = row_start ? clamp_long((long)row_start[r], 0, cols) : 0;
+        const long re = row_end ? clamp_long((long)row_end[r], 0, cols) : cols;
+        topk_lane* lanes = (topk_lane*)malloc(sizeof(topk_lane) * (size_t)(cols > 0 ? cols : 1));
+        unsigned char* sel = (unsigned char*)calloc((size_t)(cols > 0 ? cols : 1), 1);
+        if (!lanes || !sel) {
+            bad = 1;
+            free(lanes);
+            free(sel);
+            continue;
+        }
+        for (long c = 0; c < cols; ++c) {
+            lanes[c].valid = (c >= rs && c < re);
+            lanes[c].key = topk_key(scores[r * ld + c]);
+            lanes[c].col = c;
+        }
+        qsort(lanes, (size_t)cols, sizeof(topk_lane), topk_lane_cmp);
+        const long nvalid = re > rs ? re - rs : 0;
+        const long take = topk < nvalid ? topk : nvalid;
+        for (long j = 0; j < take; ++j)
+            sel[lanes[j].col] = 1;
+        long o = 0;
+        for (long c = 0; c < cols; ++c)
+            if (sel[c])
+                out[r * ld_out + o++] = (int32_t)(c - rs);
+        for (; o < topk; ++o)
+            out[r * ld_out + o] = -1;
+        free(lanes);
+        free(sel);
+    }
     return bad ? -1 : 0;
 }
 

@@ -19,6 +19,9 @@ the GateLinear and fused-MoE pages; no public dataset is involved):
 * ``moe``      Qwen3-30B-A3B-shaped: hidden 2048, 128 experts, intermediate
                768, top-8; X ~ N(0,1) bf16, router W fp32 ~ N(0,0.02),
                expert weights bf16 ~ N(0,0.02).
+* ``indexer``  sparse-attention indexer top-k: scores relu(N(0,1)) rounded
+               to bf16 precision, [rows, 8192]; decode windows [0, context)
+               and packed causal prefill windows.
 """
 from __future__ import annotations
 
@@ -192,3 +195,59 @@ def moe_weights(seed: int = 0, H=MOE_H, E=MOE_E, I=MOE_I, n_probes: int = 3) -> 
 def moe_batch(M: int, wts: MoEWeights) -> Batch:
     filler = normal_bf16(filler_seed(M), (M, wts.w_router.shape[1]), 1.0)
     return plant(wts.probes, M, lambda pid: decode_positions(M, pid), filler)
+
+
+# ------------------------------------------------------------ indexer top-k
+
+# DeepSeek-V3.2-style sparse-attention indexer (Sparse-MLA page): per query
+# row, scores over up to 8192 key columns, top-k in {512, 1024, 2048}.  The
+# scores are relu-shaped (relu(q.k) makes exact 0.0 plateaus routine) and
+# rounded to bf16 precision, so equal values recur inside a row.
+INDEXER_COLS = 8192
+INDEXER_TOPK = (512, 1024, 2048)
+INDEXER_DECODE_ROWS = (1, 8, 64)
+INDEXER_PREFILL_ROWS = 4096
+
+
+@dataclass
+class IndexerBatch:
+    scores: np.ndarray          # float32 [rows, cols]
+    row_start: np.ndarray       # int64 [rows]
+    row_end: np.ndarray         # int64 [rows]
+
+
+def indexer_scores(seed: int, rows: int, cols: int) -> np.ndarray:
+    g = rng(seed)
+    s = np.maximum(g.standard_normal((rows, cols), dtype=np.float32), 0.0)
+    return bf16_bits_to_f32(f32_to_bf16_bits(s))
+
+
+def indexer_decode(rows: int, cols: int = INDEXER_COLS, seed: int = 0) -> IndexerBatch:
+    """Decode: one row per request, window [0, context length), context
+    lengths drawn in [cols/8, cols]; the last row always spans every column."""
+    g = rng(5000 + seed + rows)
+    re = g.integers(cols // 8, cols + 1, rows).astype(np.int64)
+    re[-1] = cols
+    return IndexerBatch(indexer_scores(6000 + seed + rows, rows, cols), np.zeros(rows, np.int64), re)
+
+
+def indexer_prefill(rows: int, cols: int = INDEXER_COLS, seed: int = 0, requests: int = 4) -> IndexerBatch:
+    """Prefill: `requests` causal requests packed along both axes.  Request r
+    has n_r query rows and a key segment [kv0_r, kv0_r + p_r + n_r) of cached
+    prefix p_r plus its own tokens; its query i sees [kv0_r, kv0_r + p_r + i + 1).
+    The segments tile [0, cols) (needs cols >= rows)."""
+    assert cols >= rows >= requests
+    g = rng(7000 + seed + rows)
+    n = np.diff([0, *np.sort(g.choice(np.arange(1, rows), requests - 1, replace=False)), rows])
+    p = np.diff([0, *np.sort(g.integers(0, cols - rows + 1, requests - 1)), cols - rows])
+    ks = np.zeros(rows, np.int64)
+    ke = np.zeros(rows, np.int64)
+    q0 = kv0 = 0
+    for nr, pr in zip(n, p):
+        i = np.arange(nr)
+        ks[q0:q0 + nr] = kv0
+        ke[q0:q0 + nr] = kv0 + pr + i + 1
+        q0 += nr
+        kv0 += pr + nr
+    assert kv0 == cols and q0 == rows
+    return IndexerBatch(indexer_scores(8000 + seed + rows, rows, cols), ks, ke)
