@@ -88,6 +88,7 @@ def main():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-bf16", action="store_true")
     ap.add_argument("--no-moe", action="store_true")
+    ap.add_argument("--no-topk", action="store_true")
     ap.add_argument("--mode", choices=("step", "copy"), default="step",
                     help="copy: one 512 MiB device-to-device copy, the known-size kernel that "
                          "scales the PMC byte counters")
@@ -176,6 +177,8 @@ def main():
         extra["dense_bf16"] = dense_bf16_leg(torch, np, bi, wl, dev)
     if not args.no_moe:
         extra["moe"] = moe_leg(torch, np, bi, wl, dev)
+    if not args.no_topk:
+        extra["indexer_topk"] = topk_leg(torch, np, bi, wl, dev)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -287,6 +290,31 @@ def moe_leg(torch, np, bi, wl, dev):
         res[str(M)] = {"us": round(us, 2), "distinct_experts": distinct,
                        "GBps": round(nbytes / us / 1e3, 1), "TFLOPs": round(flops / us / 1e6, 2),
                        "hbm_frac": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4)}
+    return res
+
+
+def topk_leg(torch, np, bi, wl, dev):
+    """Deterministic indexer top-k (8192 columns): decode batches of 1, 8 and
+    64 rows and a 4096-row packed causal prefill, top-k 2048.  Algorithmic
+    bytes: the in-window scores read once plus the int32 output written once;
+    8 rotating copies of the scores keep them out of L2."""
+    res = {}
+    cases = [(f"decode_{n}", wl.indexer_decode(n)) for n in wl.INDEXER_DECODE_ROWS]
+    cases.append((f"prefill_{wl.INDEXER_PREFILL_ROWS}", wl.indexer_prefill(wl.INDEXER_PREFILL_ROWS)))
+    topk = 2048
+    for name, b in cases:
+        rows = b.scores.shape[0]
+        s = torch.from_numpy(b.scores).to(dev)
+        copies = [s] + [s.clone() for _ in range(7)]
+        rs = torch.from_numpy(b.row_start).to(dev)
+        re = torch.from_numpy(b.row_end).to(dev)
+        out = torch.empty((rows, topk), dtype=torch.int32, device=dev)
+        us = time_calls(torch, np, lambda i: bi.bi_indexer_topk(copies[i % 8], topk, rs, re, out=out),
+                        10 if rows > 1024 else 30)
+        win = np.clip(b.row_end, 0, b.scores.shape[1]) - np.clip(b.row_start, 0, b.scores.shape[1])
+        nbytes = int(4 * np.maximum(win, 0).sum() + 4 * rows * topk + 16 * rows)
+        res[name] = {"us": round(us, 2), "rows": rows, "GBps": round(nbytes / us / 1e3, 1),
+                     "hbm_frac": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4)}
     return res
 
 

@@ -54,8 +54,9 @@ _lib.bi_lab_workspace_size.argtypes = [ctypes.POINTER(Recipe), _I32, _I64, _I64,
 _lib.bi_moe_workspace_size.argtypes = [_I64, _I64, _I64, _I64, _I64]
 _lib.bi_describe_recipe.argtypes = [_I32, _I64, _I64, ctypes.POINTER(Recipe)]
 _lib.bi_status_str.argtypes = [_I32]
+_lib.bi_indexer_topk.argtypes = [_P, _I64, _I64, _I64, _P, _P, _I64, _P, _I64, _P]
 for _f in (_lib.bi_linear_f32, _lib.bi_linear_bf16, _lib.bi_negctl_linear_f32, _lib.bi_lab_linear,
-           _lib.bi_moe_grouped_gemm, _lib.bi_describe_recipe):
+           _lib.bi_moe_grouped_gemm, _lib.bi_describe_recipe, _lib.bi_indexer_topk):
     _f.restype = _I32
 for _f in (_lib.bi_linear_workspace_size, _lib.bi_lab_workspace_size, _lib.bi_moe_workspace_size):
     _f.restype = _SZ
@@ -236,6 +237,26 @@ def bi_moe_grouped_gemm(x, w_router, b_router, w13, w2, topk: int):
                                     _ptr(ws), 0 if ws is None else ws.numel(), ctypes.c_void_p(s.cuda_stream)),
            "bi_moe_grouped_gemm")
     return y, ids, probs
+
+
+def bi_indexer_topk(scores, topk: int, row_start=None, row_end=None, out=None):
+    """Deterministic per-row top-k of fp32 indexer scores [rows, cols] (row pitch
+    may exceed cols).  row_start / row_end: int64 [rows] window bounds or None.
+    Returns int32 [rows, topk]: ascending window-relative indices, then -1."""
+    if scores.dtype != torch.float32 or scores.dim() != 2 or not scores.is_cuda or scores.stride(1) != 1:
+        raise ValueError("bi_indexer_topk: scores must be a 2-D float32 CUDA tensor with unit column stride")
+    rows, cols = scores.shape
+    for name, t in (("row_start", row_start), ("row_end", row_end)):
+        if t is not None and (t.dtype != torch.int64 or t.shape != (rows,) or not t.is_contiguous()
+                              or t.device != scores.device):
+            raise ValueError(f"bi_indexer_topk: {name} must be a contiguous int64 [rows] tensor on the same GPU")
+    if out is None:
+        out = torch.empty((rows, topk), dtype=torch.int32, device=scores.device)
+    s = _stream(scores.device)
+    _check(_lib.bi_indexer_topk(_ptr(scores), max(scores.stride(0), cols), rows, cols, _ptr(row_start),
+                                _ptr(row_end), topk, _ptr(out), out.stride(0),
+                                ctypes.c_void_p(s.cuda_stream)), "bi_indexer_topk")
+    return out
 
 
 def lib():

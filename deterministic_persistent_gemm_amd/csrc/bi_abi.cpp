@@ -12,6 +12,7 @@
 #include "bi_launch.h"
 #include "bi_moe.h"
 #include "bi_plan.h"
+#include "bi_topk.h"
 
 using namespace bi;
 
@@ -175,6 +176,26 @@ bi_status_t bi_moe_grouped_gemm(const uint16_t* x, const float* w_router, const 
 {
     return moe_run(x, w_router, b_router, w13, w2, M, H, E, I, topk, topk_ids, topk_probs, y, ws,
                    ws_bytes, stream);
+}
+
+bi_status_t bi_indexer_topk(const float* scores, int64_t ld, int64_t rows, int64_t cols,
+                            const int64_t* row_start, const int64_t* row_end, int64_t topk,
+                            int32_t* out, int64_t ld_out, hipStream_t stream)
+{
+    auto al = [](const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; };
+    if (rows < 0 || cols < 0 || topk <= 0 || ld < cols || ld_out < topk)
+        return BI_EINVAL;
+    if (rows == 0)
+        return BI_OK;
+    if (cols > kTopkMaxCols || rows > (int64_t(1) << 31) - 1 || topk > (int64_t(1) << 30))
+        return BI_EUNSUPPORTED;
+    if (!out || (cols > 0 && !scores))
+        return BI_EINVAL;
+    if (!al(scores, 4) || !al(out, 4) || !al(row_start, 8) || !al(row_end, 8))
+        return BI_EINVAL;
+    return launch_topk_rows(scores, ld, rows, cols, row_start, row_end, topk, out, ld_out, stream) == hipSuccess
+               ? BI_OK
+               : BI_EHIP;
 }
 
 }  // extern "C"

@@ -138,6 +138,27 @@ bi_status_t bi_moe_grouped_gemm(const uint16_t* x,
                                 int32_t* topk_ids, float* topk_probs, float* y,
                                 void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* Deterministic per-row top-k of indexer scores (sparse-attention indexer;
+ * "[BI][DSv4] Pin sparse-MLA decode and prefill scheduling under batch
+ * invariance", commit notes of the deterministic per-row top-k).
+ *   scores  [rows, cols] fp32, row pitch ld elements (ld >= cols); any fp32
+ *           bit pattern, NaNs included.
+ *   row_start, row_end  [rows] int64 or NULL (NULL: 0 and cols): row r's
+ *           window is [clamp(row_start[r], 0, cols), clamp(row_end[r], 0, cols)).
+ *   out     [rows, topk] int32, row pitch ld_out (>= topk).
+ * Ranking: -0.0 counts as +0.0; scores are ranked by the monotone 32-bit key
+ * of their bit pattern (positive NaNs above +inf, negative NaNs below -inf);
+ * exact ties go to the lower column; lanes outside the window are never
+ * selected and never take a tied slot.  Row r receives the min(topk, window
+ * length) best lanes as window-relative column indices in ascending order,
+ * followed by -1 in the remaining slots.  The result is a function of the
+ * row's own scores and window only.  Requires cols <= 8192 (BI_EUNSUPPORTED
+ * otherwise: there is no fallback).  Pointers are 4-byte (scores, out) and
+ * 8-byte (bounds) aligned device pointers; no workspace. */
+bi_status_t bi_indexer_topk(const float* scores, int64_t ld, int64_t rows, int64_t cols,
+                            const int64_t* row_start, const int64_t* row_end, int64_t topk,
+                            int32_t* out, int64_t ld_out, hipStream_t stream);
+
 /* Workspace bytes the calls above need for a given problem (0 if none). */
 size_t bi_linear_workspace_size(int32_t dtype, int64_t M, int64_t N, int64_t K);
 size_t bi_moe_workspace_size(int64_t M, int64_t H, int64_t E, int64_t I, int64_t topk);

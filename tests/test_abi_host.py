@@ -150,3 +150,18 @@ def test_lab_recipe_validation():
 def test_status_strings():
     for s in range(5):
         assert L.bi_status_str(s).startswith(b"BI_")
+
+
+def test_indexer_topk_validation():
+    f = L.bi_indexer_topk
+    args = dict(s=FAKE, ld=8192, rows=4, cols=8192, rs=None, re=None, k=2048, out=FAKE, ldo=2048)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return f(a["s"], a["ld"], a["rows"], a["cols"], a["rs"], a["re"], a["k"], a["out"], a["ldo"], None)
+
+    assert call(rows=0) == bi.BI_OK
+    assert call(cols=8193, ld=8193) == bi.BI_EUNSUPPORTED      # past the one-workgroup row envelope
+    for kw in (dict(k=0), dict(ld=100), dict(ldo=100), dict(rows=-1), dict(out=None),
+               dict(s=None), dict(s=ctypes.c_void_p(0x10002)), dict(rs=ctypes.c_void_p(0x10004))):
+        assert call(**kw) == bi.BI_EINVAL, kw
