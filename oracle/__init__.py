@@ -49,9 +49,11 @@ def _load():
         lib.oracle_moe.argtypes = [P, P, P, P, P, L, L, L, L, L, P, P, P, P, P]
         lib.oracle_f64_to_bf16.argtypes = [P, P, L]
         lib.oracle_topk_rows.argtypes = [P, L, L, L, P, P, L, P, L]
+        C = ctypes.c_int
+        lib.oracle_moe_ex.argtypes = [P, P, P, P, P, L, L, L, L, L, C, C, C, C, P, P, P, P, P]
         for f in (lib.oracle_linear_f32, lib.oracle_linear_bf16, lib.oracle_topk,
                   lib.oracle_moe, lib.oracle_f64_to_bf16, lib.oracle_num_threads,
-                  lib.oracle_topk_rows):
+                  lib.oracle_topk_rows, lib.oracle_moe_ex):
             f.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -169,6 +171,41 @@ def moe(x, w_router, b_router, w13, w2, topk, ids=None):
                             _ptr(probs), _ptr(y))
     if rc:
         raise ValueError("oracle_moe rejected its arguments")
+    return y, ids_out, probs, logits
+
+
+ACT_SWIGLU, ACT_SQRELU = 1, 2
+
+
+def moe_ex(x, w_router, b_router, w1, w2, topk, act=ACT_SWIGLU, probs_at_act=True, apply_weights=False,
+           acc_fp64=True, ids=None):
+    """MoE layer with the activation and combine options: act ACT_SWIGLU (w1
+    [E, 2I, H], gate rows first) or ACT_SQRELU (w1 [E, I, H]); the routing
+    probability applied at the activation and/or as a weight in the top-k
+    sum; the sum in binary64 or in fp32.  Same returns as moe()."""
+    x = _c(x, np.uint16)
+    w_router = _c(w_router, np.float32)
+    b_router = _c(b_router, np.float32)
+    w1 = _c(w1, np.uint16)
+    w2 = _c(w2, np.uint16)
+    M, H = x.shape
+    E, H2 = w_router.shape
+    E2, R1, H3 = w1.shape
+    E3, H4, I = w2.shape
+    assert H == H2 == H3 == H4 and E == E2 == E3 and R1 == (2 * I if act == ACT_SWIGLU else I)
+    ids_in = _c(ids, np.int32)
+    if ids_in is not None:
+        assert ids_in.shape == (M, topk)
+    y = np.empty((M, H), np.float32)
+    ids_out = np.empty((M, topk), np.int32)
+    probs = np.empty((M, topk), np.float64)
+    logits = np.empty((M, E), np.float32)
+    rc = _load().oracle_moe_ex(_ptr(x), _ptr(w_router), _ptr(b_router), _ptr(w1), _ptr(w2),
+                               M, H, E, I, topk, int(act), int(bool(probs_at_act)), int(bool(apply_weights)),
+                               int(bool(acc_fp64)), _ptr(ids_in), _ptr(logits), _ptr(ids_out),
+                               _ptr(probs), _ptr(y))
+    if rc:
+        raise ValueError("oracle_moe_ex rejected its arguments")
     return y, ids_out, probs, logits
 
 

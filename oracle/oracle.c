@@ -316,38 +316,54 @@ int oracle_topk_rows(const float* scores, long ld, long rows, long cols,
  *     caller's ids_in when given
  *  3. p[j] = exp(l[id_j] - max l) / sum_{e ascending} exp(l[e] - max l),
  *     the full-softmax probability of the chosen expert, not renormalised
- *  4. per slot j (expert e = ids[j]):  h[c] = RN_bf16( sum_h x[h]*w13[e,c,h] ),
- *     c in [0, 2I): the first I rows of w13[e] are the gate, the next I the up
- *     projection (gate|up half-split)
- *  5. a[i] = RN_bf16( ((g*s) * u) * p[j] ),  g = h[i], u = h[I+i],
- *     s = 1 / (1 + exp(-g)): SwiGLU with the routing probability applied at
- *     the activation, one rounding at the end
+ *  4. per slot j (expert e = ids[j]):  h[c] = RN_bf16( sum_h x[h]*w1[e,c,h] )
+ *     gated (SwiGLU): c in [0, 2I), the first I rows of w1[e] are the gate,
+ *     the next I the up projection (gate|up half-split);
+ *     squared-ReLU: c in [0, I)
+ *  5. a[i] = RN_bf16( act_i * q ), q = p[j] when the probability is applied
+ *     at the activation, else 1, computed in binary64 with one rounding:
+ *     SwiGLU act_i = (g*s) * u, g = h[i], u = h[I+i], s = 1 / (1 + exp(-g));
+ *     squared-ReLU act_i = max(h[i], 0)^2
  *  6. y_j[c] = sum_{i ascending} a[i] * w2[e,c,i]
- *  7. out[c] = RN_f32( sum_{j = 0..topk-1} y_j[c] ): unit-weight combine in
- *     binary64, slot order
+ *  7. combine in slot order j = 0..topk-1, with w_j = p[j] when the weights
+ *     are applied here, else 1:
+ *     acc_fp64:  out[c] = RN_f32( sum_j w_j * y_j[c] ) in binary64
+ *     fp32:      the slot partials are fp32 storage points and the sum is
+ *                fp32: acc = +0; acc = RN_f32(acc + t_j) with
+ *                t_j = RN_f32(RN_f32(p[j]) * RN_f32(y_j[c])) when weighted,
+ *                t_j = RN_f32(y_j[c]) otherwise
+ * The options (fused-MoE page: the gated activation with the probability at
+ * the activation and an unweighted fp64 combine; the squared-ReLU activation
+ * and the (apply_weights, acc_fp64) matrix of the top-k sum, whose (false,
+ * false) point must apply no weights) are independent switches here.
  */
-int oracle_moe(const uint16_t* x, const float* wr, const float* br,
-               const uint16_t* w13, const uint16_t* w2,
-               long M, long H, long E, long I, long topk,
-               const int32_t* ids_in, float* logits_out, int32_t* ids_out,
-               double* probs_out, float* y)
+int oracle_moe_ex(const uint16_t* x, const float* wr, const float* br,
+                  const uint16_t* w1, const uint16_t* w2,
+                  long M, long H, long E, long I, long topk,
+                  int act, int probs_at_act, int apply_weights, int acc_fp64,
+                  const int32_t* ids_in, float* logits_out, int32_t* ids_out,
+                  double* probs_out, float* y)
 {
     if (M < 0 || H <= 0 || E <= 0 || I <= 0 || topk <= 0 || topk > E)
         return -1;
+    if (act != 1 && act != 2)
+        return -1;
     if (M == 0)
         return 0;
-    if (!x || !wr || !w13 || !w2 || !ids_out || !probs_out || !y)
+    if (!x || !wr || !w1 || !w2 || !ids_out || !probs_out || !y)
         return -1;
+    const long rows1 = act == 1 ? 2 * I : I;     /* rows of one expert's first weight */
     int bad = 0;
 #pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
     for (long m = 0; m < M; ++m) {
         const uint16_t* xm = x + m * H;
         float* l = (float*)malloc(sizeof(float) * (size_t)E);
-        double* h = (double*)malloc(sizeof(double) * (size_t)(2 * I));
+        double* h = (double*)malloc(sizeof(double) * (size_t)rows1);
         double* a = (double*)malloc(sizeof(double) * (size_t)I);
         double* acc = (double*)calloc((size_t)H, sizeof(double));
+        float* acc32 = (float*)calloc((size_t)H, sizeof(float));
         int32_t* ids = ids_out + m * topk;
-        if (!l || !h || !a || !acc) {
+        if (!l || !h || !a || !acc || !acc32) {
             bad = 1;
             goto done;
         }
@@ -387,36 +403,63 @@ int oracle_moe(const uint16_t* x, const float* wr, const float* br,
             double p = exp((double)l[ids[j]] - mx) / den;
             probs_out[m * topk + j] = p;
             long e = ids[j];
-            /* 4. gate|up projection, bf16 storage point */
-            const uint16_t* w13e = w13 + e * (2 * I) * H;
-            for (long c = 0; c < 2 * I; ++c) {
+            /* 4. first projection, bf16 storage point */
+            const uint16_t* w1e = w1 + e * rows1 * H;
+            for (long c = 0; c < rows1; ++c) {
                 double s = 0.0;
                 for (long k = 0; k < H; ++k)
-                    s += bf16_to_f64(xm[k]) * bf16_to_f64(w13e[c * H + k]);
+                    s += bf16_to_f64(xm[k]) * bf16_to_f64(w1e[c * H + k]);
                 h[c] = bf16_to_f64(f64_to_bf16(s));
             }
-            /* 5. SwiGLU with the probability applied, bf16 storage point */
+            /* 5. activation (probability applied here or not), bf16 storage point */
+            const double q = probs_at_act ? p : 1.0;
             for (long i = 0; i < I; ++i) {
-                double g = h[i], u = h[I + i];
-                double sg = 1.0 / (1.0 + exp(-g));
-                a[i] = bf16_to_f64(f64_to_bf16(((g * sg) * u) * p));
+                double v;
+                if (act == 1) {
+                    double g = h[i], u = h[I + i];
+                    double sg = 1.0 / (1.0 + exp(-g));
+                    v = (g * sg) * u;
+                } else {
+                    double r = h[i] > 0.0 ? h[i] : 0.0;
+                    v = r * r;
+                }
+                a[i] = bf16_to_f64(f64_to_bf16(v * q));
             }
-            /* 6.+7. down projection, summed over slots in slot order */
+            /* 6.+7. down projection, combined over slots in slot order */
             const uint16_t* w2e = w2 + e * H * I;
             for (long c = 0; c < H; ++c) {
                 double s = 0.0;
                 for (long i = 0; i < I; ++i)
                     s += a[i] * bf16_to_f64(w2e[c * I + i]);
-                acc[c] += s;
+                if (acc_fp64) {
+                    acc[c] += apply_weights ? p * s : s;
+                } else {
+                    const double part = (double)f64_to_f32(s);
+                    const double t = apply_weights ? (double)f64_to_f32((double)f64_to_f32(p) * part) : part;
+                    acc32[c] = f64_to_f32((double)acc32[c] + t);
+                }
             }
         }
         for (long c = 0; c < H; ++c)
-            y[m * H + c] = f64_to_f32(acc[c]);
+            y[m * H + c] = acc_fp64 ? f64_to_f32(acc[c]) : acc32[c];
     done:
         free(l);
         free(h);
         free(a);
         free(acc);
+        free(acc32);
     }
     return bad ? -1 : 0;
+}
+
+/* The gated layer with the probability at the activation and an unweighted
+ * binary64 combine (the fused-MoE page's shipped configuration). */
+int oracle_moe(const uint16_t* x, const float* wr, const float* br,
+               const uint16_t* w13, const uint16_t* w2,
+               long M, long H, long E, long I, long topk,
+               const int32_t* ids_in, float* logits_out, int32_t* ids_out,
+               double* probs_out, float* y)
+{
+    return oracle_moe_ex(x, wr, br, w13, w2, M, H, E, I, topk, 1, 1, 0, 1, ids_in, logits_out, ids_out,
+                         probs_out, y);
 }
