@@ -290,6 +290,19 @@ def moe_leg(torch, np, bi, wl, dev):
         res[str(M)] = {"us": round(us, 2), "distinct_experts": distinct,
                        "GBps": round(nbytes / us / 1e3, 1), "TFLOPs": round(flops / us / 1e6, 2),
                        "hbm_frac": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4)}
+    # squared-ReLU experts (w1 = the gate half), weights applied in an fp32 top-k sum
+    w1 = w13[:, :I, :].contiguous()
+    for M in (16, 256):
+        x = torch.from_numpy(wl.moe_batch(M, w).x.view(np.int16)).view(torch.bfloat16).to(dev)
+        f = lambda i: bi.bi_moe_grouped_gemm_ex(x, wr, None, w1, w2, k, activation=bi.BI_ACT_SQRELU,
+                                                probs_at_activation=False, apply_weights=True, acc_fp64=False)
+        _, ids, _ = f(0)
+        distinct = int(torch.unique(ids).numel())
+        us = time_calls(torch, np, f, 20)
+        nbytes = (E * H * 4 + M * H * 2 + distinct * 2 * I * H * 2 + M * H * 4 + M * k * 8)
+        res[f"sqrelu_{M}"] = {"us": round(us, 2), "distinct_experts": distinct,
+                              "GBps": round(nbytes / us / 1e3, 1),
+                              "hbm_frac": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4)}
     return res
 
 

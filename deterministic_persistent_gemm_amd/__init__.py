@@ -55,8 +55,11 @@ _lib.bi_moe_workspace_size.argtypes = [_I64, _I64, _I64, _I64, _I64]
 _lib.bi_describe_recipe.argtypes = [_I32, _I64, _I64, ctypes.POINTER(Recipe)]
 _lib.bi_status_str.argtypes = [_I32]
 _lib.bi_indexer_topk.argtypes = [_P, _I64, _I64, _I64, _P, _P, _I64, _P, _I64, _P]
+_lib.bi_moe_grouped_gemm_ex.argtypes = [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _P, _P, _P, _P,
+                                        _P, _SZ, _P]
 for _f in (_lib.bi_linear_f32, _lib.bi_linear_bf16, _lib.bi_negctl_linear_f32, _lib.bi_lab_linear,
-           _lib.bi_moe_grouped_gemm, _lib.bi_describe_recipe, _lib.bi_indexer_topk):
+           _lib.bi_moe_grouped_gemm, _lib.bi_describe_recipe, _lib.bi_indexer_topk,
+           _lib.bi_moe_grouped_gemm_ex):
     _f.restype = _I32
 for _f in (_lib.bi_linear_workspace_size, _lib.bi_lab_workspace_size, _lib.bi_moe_workspace_size):
     _f.restype = _SZ
@@ -210,32 +213,59 @@ def bi_lab_linear(x, wt, bias=None, recipe: Recipe | None = None, path: int = BI
     return out
 
 
+class MoEOptions(ctypes.Structure):
+    """bi_moe_options_t."""
+    _fields_ = [("activation", ctypes.c_int32), ("probs_at_activation", ctypes.c_int32),
+                ("apply_weights", ctypes.c_int32), ("acc_fp64", ctypes.c_int32)]
+
+
+BI_ACT_SWIGLU, BI_ACT_SQRELU = 0, 1
+
+
 def bi_moe_grouped_gemm(x, w_router, b_router, w13, w2, topk: int):
     """Batch-invariant MoE layer.  Returns (y fp32 [M,H], topk_ids int32 [M,topk],
     topk_probs fp32 [M,topk]).  w13 [E, 2I, H] and w2 [E, H, I] are the experts'
     nn.Linear weights (their .t() views are what the GEMMs consume)."""
-    if x.dtype != torch.bfloat16 or w13.dtype != torch.bfloat16 or w2.dtype != torch.bfloat16:
-        raise TypeError("bi_moe_grouped_gemm: x, w13, w2 must be bfloat16")
+    return _moe(x, w_router, b_router, w13, w2, topk, None, "bi_moe_grouped_gemm")
+
+
+def bi_moe_grouped_gemm_ex(x, w_router, b_router, w1, w2, topk: int, activation: int = BI_ACT_SWIGLU,
+                           probs_at_activation: bool = True, apply_weights: bool = False,
+                           acc_fp64: bool = True):
+    """The MoE layer with explicit activation and top-k-sum options.  SwiGLU:
+    w1 [E, 2I, H]; squared-ReLU: w1 [E, I, H].  Same returns."""
+    opt = MoEOptions(int(activation), int(bool(probs_at_activation)), int(bool(apply_weights)),
+                     int(bool(acc_fp64)))
+    return _moe(x, w_router, b_router, w1, w2, topk, opt, "bi_moe_grouped_gemm_ex")
+
+
+def _moe(x, w_router, b_router, w1, w2, topk, opt, name):
+    if x.dtype != torch.bfloat16 or w1.dtype != torch.bfloat16 or w2.dtype != torch.bfloat16:
+        raise TypeError(f"{name}: x, w1, w2 must be bfloat16")
     if w_router.dtype != torch.float32:
-        raise TypeError("bi_moe_grouped_gemm: w_router must be float32")
-    for t in (x, w_router, w13, w2) + (() if b_router is None else (b_router,)):
+        raise TypeError(f"{name}: w_router must be float32")
+    for t in (x, w_router, w1, w2) + (() if b_router is None else (b_router,)):
         if not t.is_contiguous() or not t.is_cuda or t.device != x.device:
-            raise ValueError("bi_moe_grouped_gemm: tensors must be contiguous and on the same GPU")
+            raise ValueError(f"{name}: tensors must be contiguous and on the same GPU")
     M, H = x.shape
     E = w_router.shape[0]
     I = w2.shape[2]
-    if w_router.shape != (E, H) or w13.shape != (E, 2 * I, H) or w2.shape != (E, H, I):
-        raise ValueError("bi_moe_grouped_gemm: inconsistent shapes")
-    _check_bias(b_router, E, x.device, "bi_moe_grouped_gemm")
+    rows1 = I if (opt is not None and opt.activation == BI_ACT_SQRELU) else 2 * I
+    if w_router.shape != (E, H) or w1.shape != (E, rows1, H) or w2.shape != (E, H, I):
+        raise ValueError(f"{name}: inconsistent shapes")
+    _check_bias(b_router, E, x.device, name)
     y = torch.empty((M, H), dtype=torch.float32, device=x.device)
     ids = torch.empty((M, topk), dtype=torch.int32, device=x.device)
     probs = torch.empty((M, topk), dtype=torch.float32, device=x.device)
     s = _stream(x.device)
     ws = _workspace(_lib.bi_moe_workspace_size(M, H, E, I, topk), x.device, s)
-    _check(_lib.bi_moe_grouped_gemm(_ptr(x), _ptr(w_router), _ptr(b_router), _ptr(w13), _ptr(w2),
-                                    M, H, E, I, topk, _ptr(ids), _ptr(probs), _ptr(y),
-                                    _ptr(ws), 0 if ws is None else ws.numel(), ctypes.c_void_p(s.cuda_stream)),
-           "bi_moe_grouped_gemm")
+    common = (_ptr(x), _ptr(w_router), _ptr(b_router), _ptr(w1), _ptr(w2), M, H, E, I, topk)
+    tail = (_ptr(ids), _ptr(probs), _ptr(y), _ptr(ws), 0 if ws is None else ws.numel(),
+            ctypes.c_void_p(s.cuda_stream))
+    if opt is None:
+        _check(_lib.bi_moe_grouped_gemm(*common, *tail), name)
+    else:
+        _check(_lib.bi_moe_grouped_gemm_ex(*common, ctypes.byref(opt), *tail), name)
     return y, ids, probs
 
 

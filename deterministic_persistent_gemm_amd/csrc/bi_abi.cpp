@@ -174,7 +174,19 @@ bi_status_t bi_moe_grouped_gemm(const uint16_t* x, const float* w_router, const 
                                 float* topk_probs, float* y, void* ws, size_t ws_bytes,
                                 hipStream_t stream)
 {
-    return moe_run(x, w_router, b_router, w13, w2, M, H, E, I, topk, topk_ids, topk_probs, y, ws,
+    const bi_moe_options_t opt{BI_ACT_SWIGLU, 1, 0, 1};
+    return moe_run(x, w_router, b_router, w13, w2, M, H, E, I, topk, opt, topk_ids, topk_probs, y, ws,
+                   ws_bytes, stream);
+}
+
+bi_status_t bi_moe_grouped_gemm_ex(const uint16_t* x, const float* w_router, const float* b_router,
+                                   const uint16_t* w1, const uint16_t* w2, int64_t M, int64_t H, int64_t E,
+                                   int64_t I, int64_t topk, const bi_moe_options_t* options,
+                                   int32_t* topk_ids, float* topk_probs, float* y, void* ws, size_t ws_bytes,
+                                   hipStream_t stream)
+{
+    const bi_moe_options_t opt = options ? *options : bi_moe_options_t{BI_ACT_SWIGLU, 1, 0, 1};
+    return moe_run(x, w_router, b_router, w1, w2, M, H, E, I, topk, opt, topk_ids, topk_probs, y, ws,
                    ws_bytes, stream);
 }
 

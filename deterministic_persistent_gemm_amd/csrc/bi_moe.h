@@ -13,7 +13,7 @@ size_t moe_workspace_size(int64_t M, int64_t H, int64_t E, int64_t I, int64_t to
 
 bi_status_t moe_run(const uint16_t* x, const float* w_router, const float* b_router,
                     const uint16_t* w13, const uint16_t* w2, int64_t M, int64_t H, int64_t E,
-                    int64_t I, int64_t topk, int32_t* topk_ids, float* topk_probs, float* y,
+                    int64_t I, int64_t topk, const bi_moe_options_t& opt, int32_t* topk_ids, float* topk_probs, float* y,
                     void* ws, size_t ws_bytes, hipStream_t stream);
 
 }  // namespace bi

@@ -13,8 +13,10 @@
 //   dispatch stable counting sort of (token, slot) pairs by expert, and the
 //            list of 16-row work units                   one workgroup
 //   gemm1    act = bf16(silu(bf16(x.Wg^T)) * bf16(x.Wu^T) * p)   key (bf16, 2I, H)
+//            or, squared-ReLU, act = bf16(relu(bf16(x.W1^T))^2 [* p]) key (bf16, I, H)
 //   gemm2    part[pair] = act . W2^T (fp32)                       key (bf16, H, I)
-//   combine  y[m] = fp32(sum_j (double) part[m*topk + j])
+//   combine  y[m] = fp32(sum_j (double) part[m*topk + j]), or the weighted
+//            and/or fp32 forms of the top-k sum
 //
 // Every row of every GEMM is computed by the same per-element operation
 // sequence as the dense linear kernels for that key, so a token's bits do
@@ -31,6 +33,7 @@ namespace bi {
 namespace {
 
 constexpr int kTileRows = 16;     // rows of one MFMA output tile
+constexpr int kActNone = 0, kActSwiGLU = 1, kActSqReLU = 2;   // grouped-GEMM epilogues
 constexpr int kMaxExperts = 1024;
 constexpr int kMaxTopk = 32;
 
@@ -281,6 +284,7 @@ struct GroupedArgs {
     const int32_t* unit_row;
     const int32_t* nunits;
     const float* probs;       // [P] routing probabilities by pair
+    int act_probs;            // GEMM1: 1 = multiply the activation by the pair's probability
     int topk;
     uint16_t* act;            // GEMM1 output [P, I] by position
     float* part;              // GEMM2 output [P, H] by pair
@@ -290,12 +294,13 @@ struct GroupedArgs {
 // output tile (folded in ascending order through LDS), NW waves take NW
 // neighbouring 16-column tiles.  A work unit is MT tiles of 16 rows of one
 // expert; each wave runs MT x NB independent chains over one weight slab.
-// SWIGLU: each wave carries a gate block and the matching up block and
-// applies the activation in the epilogue.
-template <int TW, int NW, int MT, bool SWIGLU, int CH>
+// ACT (kActNone: GEMM2, fp32 partial per pair; kActSwiGLU: each wave carries
+// a gate block and the matching up block; kActSqReLU: one block) applies the
+// activation in the epilogue.
+template <int TW, int NW, int MT, int ACT, int CH>
 __global__ __launch_bounds__(TW * NW * 64) void k_grouped(GroupedArgs g)
 {
-    constexpr int NB = SWIGLU ? 2 : 1;                  // output blocks per wave
+    constexpr int NB = ACT == kActSwiGLU ? 2 : 1;       // output blocks per wave
     __shared__ f32x4 lds[(TW > 1) ? TW * NW * MT * NB * 64 : 1];
     const int u = blockIdx.y;
     if (u >= g.nunits[0])
@@ -321,7 +326,7 @@ __global__ __launch_bounds__(TW * NW * 64) void k_grouped(GroupedArgs g)
     const int ntc = nt_ok ? nt : 0;
     const uint16_t* wp[NB];
     wp[0] = we + (int64_t)(ntc * 16 + r) * g.ldw + kSlotLen * gslot;
-    if (SWIGLU)
+    if (ACT == kActSwiGLU)
         wp[NB - 1] = we + (int64_t)(g.up_offset + ntc * 16 + r) * g.ldw + kSlotLen * gslot;
 
     f32x4 acc[MT][NB];
@@ -405,14 +410,25 @@ __global__ __launch_bounds__(TW * NW * 64) void k_grouped(GroupedArgs g)
             const int p = row0 + m * kTileRows + acc_row(lane, q);
             if (p >= row_end)
                 continue;
-            if (SWIGLU) {
+            if (ACT == kActSwiGLU) {
                 // storage point of the gate/up projection, then the activation
-                // in fp32 with the routing probability, one rounding to bf16
+                // in fp32 (with the routing probability if asked), one
+                // rounding to bf16
                 const float hg = bf16_to_f32(f32_to_bf16_rne(acc[m][0][q]));
                 const float hu = bf16_to_f32(f32_to_bf16_rne(acc[m][NB - 1][q]));
-                const float prob = g.probs[g.sorted[p]];
                 const float sg = 1.0f / (1.0f + expf(-hg));
-                const float av = ((hg * sg) * hu) * prob;
+                float av = (hg * sg) * hu;
+                if (g.act_probs)
+                    av = av * g.probs[g.sorted[p]];
+                g.act[(int64_t)p * g.n_out + col] = f32_to_bf16_rne(av);
+            } else if (ACT == kActSqReLU) {
+                // squared ReLU of the bf16 storage point (exact in fp32: an
+                // 8-bit significand squared), then the optional probability
+                const float h = bf16_to_f32(f32_to_bf16_rne(acc[m][0][q]));
+                const float rl = h > 0.f ? h : 0.f;
+                float av = rl * rl;
+                if (g.act_probs)
+                    av = av * g.probs[g.sorted[p]];
                 g.act[(int64_t)p * g.n_out + col] = f32_to_bf16_rne(av);
             } else {
                 g.part[(int64_t)g.sorted[p] * g.n_out + col] = acc[m][0][q];
@@ -422,19 +438,35 @@ __global__ __launch_bounds__(TW * NW * 64) void k_grouped(GroupedArgs g)
 
 // ------------------------------------------------------------------- combine
 
-// y[m, c] = fp32( sum_{j = 0..topk-1} (double) part[m*topk + j, c] ), slot order.
-__global__ __launch_bounds__(256) void k_combine(const float* __restrict__ part, int M, int H, int topk,
-                                                 float* __restrict__ y)
+// Top-k sum in slot order j = 0..topk-1 (fused-MoE page: fixed slot order;
+// the (apply_weights, acc_fp64) options of the sum are honoured
+// independently, so the unweighted fp32 point applies no weights):
+//   acc_fp64:  y = fp32( sum_j w_j * (double) part_j ),  w_j = p_j or 1, in binary64
+//   fp32:      acc = +0; acc = acc + t_j,  t_j = p_j * part_j (fp32) or part_j
+template <bool APPLY, bool FP64>
+__global__ __launch_bounds__(256) void k_combine(const float* __restrict__ part, const float* __restrict__ probs,
+                                                 int M, int H, int topk, float* __restrict__ y)
 {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= (int64_t)M * H)
         return;
     const int64_t m = i / H, c = i % H;
     const float* p = part + (m * topk) * (int64_t)H + c;
-    double s = 0.0;
-    for (int j = 0; j < topk; ++j)
-        s += (double)p[(int64_t)j * H];
-    y[i] = (float)s;
+    if (FP64) {
+        double s = 0.0;
+        for (int j = 0; j < topk; ++j) {
+            const double v = (double)p[(int64_t)j * H];
+            s += APPLY ? (double)probs[m * topk + j] * v : v;
+        }
+        y[i] = (float)s;
+    } else {
+        float s = 0.0f;
+        for (int j = 0; j < topk; ++j) {
+            const float v = p[(int64_t)j * H];
+            s = s + (APPLY ? probs[m * topk + j] * v : v);
+        }
+        y[i] = s;
+    }
 }
 
 // ------------------------------------------------------------------ host side
@@ -447,7 +479,7 @@ static int pick_ch(int kbpt)
     return 1;
 }
 
-template <int TW, int NW, int MT, bool SWIGLU>
+template <int TW, int NW, int MT, int ACT>
 static hipError_t launch_grouped_tw(const GroupedArgs& g, int64_t max_units, hipStream_t s)
 {
     const int ntiles = (g.n_out / 16 + NW - 1) / NW;
@@ -457,34 +489,34 @@ static hipError_t launch_grouped_tw(const GroupedArgs& g, int64_t max_units, hip
     int ch = pick_ch(g.kbpt);
     if (ch > 8)
         ch = 8;
-    if (MT * (SWIGLU ? 2 : 1) > 2 && ch > 4)
+    if (MT * (ACT == kActSwiGLU ? 2 : 1) > 2 && ch > 4)
         ch = 4;
     switch (ch) {
-    case 8:  k_grouped<TW, NW, MT, SWIGLU, 8><<<grid, TW * NW * 64, 0, s>>>(g); break;
-    case 4:  k_grouped<TW, NW, MT, SWIGLU, 4><<<grid, TW * NW * 64, 0, s>>>(g); break;
-    case 2:  k_grouped<TW, NW, MT, SWIGLU, 2><<<grid, TW * NW * 64, 0, s>>>(g); break;
-    default: k_grouped<TW, NW, MT, SWIGLU, 1><<<grid, TW * NW * 64, 0, s>>>(g); break;
+    case 8:  k_grouped<TW, NW, MT, ACT, 8><<<grid, TW * NW * 64, 0, s>>>(g); break;
+    case 4:  k_grouped<TW, NW, MT, ACT, 4><<<grid, TW * NW * 64, 0, s>>>(g); break;
+    case 2:  k_grouped<TW, NW, MT, ACT, 2><<<grid, TW * NW * 64, 0, s>>>(g); break;
+    default: k_grouped<TW, NW, MT, ACT, 1><<<grid, TW * NW * 64, 0, s>>>(g); break;
     }
     return hipGetLastError();
 }
 
-template <int MT, bool SWIGLU>
+template <int MT, int ACT>
 static hipError_t launch_grouped_mt(const GroupedArgs& g, int64_t max_units, hipStream_t s)
 {
     // k tile partials of one output tile are spread over the workgroup's
     // waves when there are 2 or 4; otherwise the waves take more columns
     if (g.tiles_k == 4)
-        return launch_grouped_tw<4, 1, MT, SWIGLU>(g, max_units, s);
+        return launch_grouped_tw<4, 1, MT, ACT>(g, max_units, s);
     if (g.tiles_k == 2)
-        return launch_grouped_tw<2, 2, MT, SWIGLU>(g, max_units, s);
-    return launch_grouped_tw<1, 4, MT, SWIGLU>(g, max_units, s);
+        return launch_grouped_tw<2, 2, MT, ACT>(g, max_units, s);
+    return launch_grouped_tw<1, 4, MT, ACT>(g, max_units, s);
 }
 
-template <bool SWIGLU>
+template <int ACT>
 static hipError_t launch_grouped(const GroupedArgs& g, int unit_rows, int64_t max_units, hipStream_t s)
 {
-    return unit_rows == 32 ? launch_grouped_mt<2, SWIGLU>(g, max_units, s)
-                           : launch_grouped_mt<1, SWIGLU>(g, max_units, s);
+    return unit_rows == 32 ? launch_grouped_mt<2, ACT>(g, max_units, s)
+                           : launch_grouped_mt<1, ACT>(g, max_units, s);
 }
 
 // The router's plan: the linear layer's own choice, except that at small M
@@ -513,6 +545,7 @@ size_t moe_workspace_size(int64_t M, int64_t H, int64_t E, int64_t I, int64_t to
 
 bi_status_t moe_run(const uint16_t* x, const float* w_router, const float* b_router, const uint16_t* w13,
                     const uint16_t* w2, int64_t M, int64_t H, int64_t E, int64_t I, int64_t topk,
+                    const bi_moe_options_t& opt,
                     int32_t* topk_ids, float* topk_probs, float* y, void* ws, size_t ws_bytes,
                     hipStream_t stream)
 {
@@ -529,12 +562,22 @@ bi_status_t moe_run(const uint16_t* x, const float* w_router, const float* b_rou
         return BI_EUNSUPPORTED;
     if (H % 32 != 0 || I % 32 != 0 || E % 16 != 0)
         return BI_EUNSUPPORTED;
+    if (opt.activation != BI_ACT_SWIGLU && opt.activation != BI_ACT_SQRELU)
+        return BI_EINVAL;
+    if ((opt.probs_at_activation != 0 && opt.probs_at_activation != 1) ||
+        (opt.apply_weights != 0 && opt.apply_weights != 1) || (opt.acc_fp64 != 0 && opt.acc_fp64 != 1))
+        return BI_EINVAL;
+    // the probability applied at the activation and again as a weight of the
+    // top-k sum would count it twice
+    if (opt.probs_at_activation && opt.apply_weights)
+        return BI_EINVAL;
+    const bool gated = opt.activation == BI_ACT_SWIGLU;
 
     bi_recipe_t r_router, r_g1, r_g2;
     bi_status_t st;
     if ((st = recipe_for(BI_F32, E, H, &r_router)) != BI_OK)
         return st;
-    if ((st = recipe_for(BI_BF16, 2 * I, H, &r_g1)) != BI_OK)
+    if ((st = recipe_for(BI_BF16, gated ? 2 * I : I, H, &r_g1)) != BI_OK)
         return st;
     if ((st = recipe_for(BI_BF16, H, I, &r_g2)) != BI_OK)
         return st;
@@ -586,10 +629,10 @@ bi_status_t moe_run(const uint16_t* x, const float* w_router, const float* b_rou
     g1.lda = H;
     g1.a_by_token = 1;
     g1.w = w13;
-    g1.w_stride = 2 * I * H;
+    g1.w_stride = (gated ? 2 * I : I) * H;
     g1.ldw = H;
     g1.n_out = (int)I;
-    g1.up_offset = (int)I;
+    g1.up_offset = gated ? (int)I : 0;
     g1.K = (int)H;
     g1.kbpt = r_g1.block_k / 32;
     g1.tiles_k = (int)(H / r_g1.block_k);
@@ -599,9 +642,12 @@ bi_status_t moe_run(const uint16_t* x, const float* w_router, const float* b_rou
     g1.unit_row = unit_row;
     g1.nunits = nunits;
     g1.probs = topk_probs;
+    g1.act_probs = opt.probs_at_activation;
     g1.topk = (int)topk;
     g1.act = act;
-    if (launch_grouped<true>(g1, unit_rows, L.max_units, stream) != hipSuccess)
+    const hipError_t e1 = gated ? launch_grouped<kActSwiGLU>(g1, unit_rows, L.max_units, stream)
+                                : launch_grouped<kActSqReLU>(g1, unit_rows, L.max_units, stream);
+    if (e1 != hipSuccess)
         return BI_EHIP;
 
     GroupedArgs g2 = g1;
@@ -618,11 +664,20 @@ bi_status_t moe_run(const uint16_t* x, const float* w_router, const float* b_rou
     g2.tiles_k = (int)(I / r_g2.block_k);
     g2.act = nullptr;
     g2.part = part;
-    if (launch_grouped<false>(g2, unit_rows, L.max_units, stream) != hipSuccess)
+    g2.act_probs = 0;
+    if (launch_grouped<kActNone>(g2, unit_rows, L.max_units, stream) != hipSuccess)
         return BI_EHIP;
 
     const int64_t n = M * H;
-    k_combine<<<(unsigned)((n + 255) / 256), 256, 0, stream>>>(part, (int)M, (int)H, (int)topk, y);
+    const unsigned cgrid = (unsigned)((n + 255) / 256);
+    if (opt.apply_weights && opt.acc_fp64)
+        k_combine<true, true><<<cgrid, 256, 0, stream>>>(part, topk_probs, (int)M, (int)H, (int)topk, y);
+    else if (opt.apply_weights)
+        k_combine<true, false><<<cgrid, 256, 0, stream>>>(part, topk_probs, (int)M, (int)H, (int)topk, y);
+    else if (opt.acc_fp64)
+        k_combine<false, true><<<cgrid, 256, 0, stream>>>(part, topk_probs, (int)M, (int)H, (int)topk, y);
+    else
+        k_combine<false, false><<<cgrid, 256, 0, stream>>>(part, topk_probs, (int)M, (int)H, (int)topk, y);
     return hipGetLastError() == hipSuccess ? BI_OK : BI_EHIP;
 }
 

@@ -159,6 +159,39 @@ bi_status_t bi_indexer_topk(const float* scores, int64_t ld, int64_t rows, int64
                             const int64_t* row_start, const int64_t* row_end, int64_t topk,
                             int32_t* out, int64_t ld_out, hipStream_t stream);
 
+/* Activation and top-k-sum options of the MoE layer (fused-MoE page, "What's
+ * included" and the strict-review summary: the batch-invariant MoE first
+ * shipped a squared-ReLU activation; the top-k sum has an (apply_weights,
+ * acc_fp64) option matrix, and every point of it must do what it says --
+ * the unweighted fp32 point applies no weights). */
+typedef enum { BI_ACT_SWIGLU = 0, BI_ACT_SQRELU = 1 } bi_activation_t;
+
+typedef struct {
+    int32_t activation;           /* bi_activation_t                                  */
+    int32_t probs_at_activation;  /* 1: a = RN_bf16(act * p) (probability applied at
+                                     the activation); 0: a = RN_bf16(act)             */
+    int32_t apply_weights;        /* 1: the top-k sum weights slot j by p_j           */
+    int32_t acc_fp64;             /* 1: the top-k sum runs in binary64, one rounding
+                                     to fp32; 0: fp32 adds from +0 in slot order
+                                     (fp32 products when weighted)                   */
+} bi_moe_options_t;
+
+/* The MoE layer with explicit options.  SwiGLU: w1 is [E, 2I, H] (gate rows,
+ * then up rows), act = silu(g) * u; squared-ReLU: w1 is [E, I, H],
+ * act = max(h, 0)^2 of the bf16 storage point h.  options == NULL is the
+ * configuration of bi_moe_grouped_gemm (SwiGLU, probability at the
+ * activation, unweighted binary64 sum).  Setting both probs_at_activation and
+ * apply_weights would apply the probability twice and returns BI_EINVAL, as
+ * does any field outside its range.  Everything else as bi_moe_grouped_gemm;
+ * the workspace size does not depend on the options. */
+bi_status_t bi_moe_grouped_gemm_ex(const uint16_t* x,
+                                   const float* w_router, const float* b_router,
+                                   const uint16_t* w1, const uint16_t* w2,
+                                   int64_t M, int64_t H, int64_t E, int64_t I, int64_t topk,
+                                   const bi_moe_options_t* options,
+                                   int32_t* topk_ids, float* topk_probs, float* y,
+                                   void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* Workspace bytes the calls above need for a given problem (0 if none). */
 size_t bi_linear_workspace_size(int32_t dtype, int64_t M, int64_t N, int64_t K);
 size_t bi_moe_workspace_size(int64_t M, int64_t H, int64_t E, int64_t I, int64_t topk);

@@ -165,3 +165,15 @@ def test_indexer_topk_validation():
     for kw in (dict(k=0), dict(ld=100), dict(ldo=100), dict(rows=-1), dict(out=None),
                dict(s=None), dict(s=ctypes.c_void_p(0x10002)), dict(rs=ctypes.c_void_p(0x10004))):
         assert call(**kw) == bi.BI_EINVAL, kw
+
+
+def test_moe_options_validation():
+    f = L.bi_moe_grouped_gemm_ex
+    def call(opt):
+        return f(FAKE, FAKE, None, FAKE, FAKE, 4, 256, 32, 64, 4, ctypes.byref(opt), FAKE, FAKE, FAKE, FAKE,
+                 1 << 30, None)
+    O = bi.MoEOptions
+    assert call(O(0, 1, 1, 1)) == bi.BI_EINVAL        # probability applied twice
+    assert call(O(2, 1, 0, 1)) == bi.BI_EINVAL        # unknown activation
+    assert call(O(1, 0, 2, 1)) == bi.BI_EINVAL        # flags are 0 or 1
+    assert call(O(1, 0, 1, -1)) == bi.BI_EINVAL
