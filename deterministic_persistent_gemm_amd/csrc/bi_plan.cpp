@@ -20,7 +20,28 @@ namespace {
 // at HBM speed; the persistent kernel pays one fp32 add per 128 k.
 constexpr int kF32BlockK = 128;
 
+// Keys measured by the offline sweeper.  GateLinear page, "Perf" and "Update:
+// is the M=4096 cost avoidable?": the config of a key comes from a sweep in
+// the production weight.t() layout, keyed on (dtype, N, K) only.
+const KeyEntry kTable[] = {
+#include "bi_table.inc"
+    {-1, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0}   // end marker
+};
+constexpr int kTableSize = (int)(sizeof(kTable) / sizeof(kTable[0])) - 1;
+
 }  // namespace
+
+const KeyEntry* table_lookup(int32_t dtype, int64_t N, int64_t K)
+{
+    for (int i = 0; i < kTableSize; ++i)
+        if (kTable[i].dtype == dtype && kTable[i].N == N && kTable[i].K == K)
+            return &kTable[i];
+    return nullptr;
+}
+
+int table_size() { return kTableSize; }
+
+const KeyEntry* table_entry(int i) { return (i >= 0 && i < kTableSize) ? &kTable[i] : nullptr; }
 
 bi_status_t recipe_for(int32_t dtype, int64_t N, int64_t K, bi_recipe_t* out)
 {
@@ -53,6 +74,14 @@ bi_status_t recipe_for(int32_t dtype, int64_t N, int64_t K, bi_recipe_t* out)
         r.mfma = BI_MFMA_F32_16X16X32_BF16;
         r.block_k = (N >= 4096 || K % 512 != 0) ? (int32_t)K : 512;
         r.m_decode_max = 64;
+    }
+    // a measured entry replaces the rule's choices (its block_k must be one
+    // the kernels can carry out; an entry that is not is ignored)
+    if (const KeyEntry* e = table_lookup(dtype, N, K)) {
+        if (e->block_k > 0 && e->block_k % 32 == 0 && K % e->block_k == 0 && e->m_decode_max >= 0) {
+            r.block_k = e->block_k;
+            r.m_decode_max = e->m_decode_max;
+        }
     }
     *out = r;
     return BI_OK;
@@ -136,6 +165,7 @@ bi_status_t make_plan(const bi_recipe_t& r, int32_t path_req, int64_t M, int64_t
     } else if (path_req == BI_PATH_PERSISTENT)
         p.path = kPathPersistent;
     else if (path_req == BI_PATH_AUTO) {
+        const KeyEntry* e = table_lookup(r.dtype, N, K);
         // The one-launch decode puts a whole output tile's k reduction on one
         // compute unit, which then streams 16 rows x K of W by itself; a
         // compute unit sustains only ~20 GB/s of such loads (measured on
@@ -145,8 +175,17 @@ bi_status_t make_plan(const bi_recipe_t& r, int32_t path_req, int64_t M, int64_t
         const int64_t slab = K * (r.dtype == BI_F32 ? 4 : 2);
         if (M > r.m_decode_max)
             p.path = kPathPersistent;
+        else if (e && e->decode_path == BI_PATH_DECODE)
+            p.path = kPathDecode;
+        else if (e && e->decode_path == BI_PATH_DECODE_WG && wg_ok)
+            p.path = kPathDecodeWg;
         else
             p.path = (wg_ok && slab <= 4096) ? kPathDecodeWg : kPathDecode;
+        if (p.path == kPathPersistent && e) {
+            const int code = M <= e->m_a ? e->tile_a : (M <= e->m_b ? e->tile_b : e->tile_c);
+            if (tile_code_valid(r.dtype, code))
+                p.tile_code = code;
+        }
     }
     else
         return BI_EINVAL;

@@ -19,6 +19,30 @@ struct Tiling {
     int bm, bn, wm, wn;
 };
 
+// A measured entry of the key table (written by the offline sweeper,
+// deterministic_persistent_gemm_amd/sweep.py, into bi_table.inc).  block_k
+// is part of the recipe; every other field only picks kernel shapes.
+struct KeyEntry {
+    int32_t dtype;
+    int64_t N, K;
+    int32_t block_k;        // recipe: width of one k tile partial
+    int32_t m_decode_max;   // largest M on a decode kernel
+    int32_t decode_path;    // BI_PATH_DECODE or BI_PATH_DECODE_WG (0: automatic)
+    // persistent tile codes (0: automatic): tile_a for M <= m_a, tile_b for
+    // m_a < M <= m_b, tile_c above
+    int64_t m_a;
+    int32_t tile_a;
+    int64_t m_b;
+    int32_t tile_b, tile_c;
+};
+
+// The table entry of a key, or nullptr.
+const KeyEntry* table_lookup(int32_t dtype, int64_t N, int64_t K);
+
+// Number of entries in the compiled table and the i-th one (for checks).
+int table_size();
+const KeyEntry* table_entry(int i);
+
 struct Plan {
     bi_recipe_t recipe;
     int path;
@@ -27,7 +51,7 @@ struct Plan {
     int mtiles;      // 16-row tiles of M (decode path)
     int ntiles;      // 16-column tiles of N (decode path)
     Tiling tiling;   // persistent path
-    int tile_code;   // persistent tile shape, 0 = automatic
+    int tile_code;   // persistent tile shape, 0 = automatic (table entry or heuristic)
     size_t ws_bytes; // workspace the plan needs (decode tile partials)
 };
 
