@@ -78,15 +78,54 @@ constexpr int kRouteTokens = 16;   // tokens per routing workgroup, one wave eac
 // Ordering key of a logit for the expert choice: NaN ranks like -inf.
 __device__ __forceinline__ float rank_key(float v) { return (v != v) ? -INFINITY : v; }
 
+// Unsigned integer whose order is the order of the (non-NaN) float; -0.0
+// maps like +0.0.
+__device__ __forceinline__ uint32_t order_bits(float v)
+{
+    uint32_t b = __float_as_uint(v);
+    if (b == 0x80000000u)
+        b = 0u;
+    return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+// Maximum over the wave's 64 lanes (wave-uniform result): within each row of
+// 16 lanes by DPP exchanges (neighbours, pairs, half-row mirror, row mirror),
+// then over the four rows through lane reads.
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v)
+{
+    uint32_t hi = (uint32_t)(v >> 32), lo = (uint32_t)v;
+#define BI_DPP_MAX_STEP(CTRL)                                                                     \
+    {                                                                                             \
+        const uint32_t ohi = (uint32_t)__builtin_amdgcn_mov_dpp((int)hi, CTRL, 0xF, 0xF, false);   \
+        const uint32_t olo = (uint32_t)__builtin_amdgcn_mov_dpp((int)lo, CTRL, 0xF, 0xF, false);   \
+        const bool take = ohi > hi || (ohi == hi && olo > lo);                                    \
+        hi = take ? ohi : hi;                                                                     \
+        lo = take ? olo : lo;                                                                     \
+    }
+    BI_DPP_MAX_STEP(0xB1)     // quad_perm 1,0,3,2
+    BI_DPP_MAX_STEP(0x4E)     // quad_perm 2,3,0,1
+    BI_DPP_MAX_STEP(0x141)    // row_half_mirror
+    BI_DPP_MAX_STEP(0x140)    // row_mirror
+#undef BI_DPP_MAX_STEP
+    uint64_t best = 0;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const uint64_t c = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)hi, 16 * r) << 32) |
+                           (uint32_t)__builtin_amdgcn_readlane((int)lo, 16 * r);
+        best = c > best ? c : best;
+    }
+    return best;
+}
+
 // One workgroup per 16 tokens, one wave per token.
 //  1. Logits of the 16 tokens into LDS: either read from `logits` [M,E], or
 //     folded here from the router's k tile partials in ascending tile order
 //     (acc = P0; acc = acc + P1; ...; + bias) -- the linear fold, same bits.
 //  2. Softmax over all E: max (exact), exp, a sum in a fixed order (each
 //     lane ascending over its experts, then a fixed butterfly), p = e / sum.
-//  3. Top-k by rank: an expert's slot is the number of experts that beat it
-//     (larger logit, or equal logit and lower index; -0.0 == +0.0).  Ranks
-//     are distinct, so slot j receives exactly one expert.
+//  3. Top-k: slot j receives the j-th largest logit, equal logits in
+//     ascending expert order, -0.0 equal to +0.0 (repeated wave arg-max
+//     over unique keys).
 template <int kPer>   // experts per lane: E <= 64 * kPer
 __global__ __launch_bounds__(kRouteTokens * 64) void k_route(const float* __restrict__ logits,
                                                              const f32x4* __restrict__ partials,
@@ -103,9 +142,22 @@ __global__ __launch_bounds__(kRouteTokens * 64) void k_route(const float* __rest
         for (int pi = tid; pi < ntiles * 64; pi += kRouteTokens * 64) {
             const int nt = pi >> 6, ln = pi & 63;
             const f32x4* p = partials + ((int64_t)mt * ntiles + nt) * tiles_k * 64 + ln;
-            f32x4 acc = p[0];
-            for (int u = 1; u < tiles_k; ++u)
-                acc = acc + p[(int64_t)u * 64];
+            // up to 16 partials are requested before the first add, so the
+            // ordered fold costs one memory round trip per 16 k tiles
+            constexpr int kBatch = 16;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            for (int u0 = 0; u0 < tiles_k; u0 += kBatch) {
+                const int n = min(kBatch, tiles_k - u0);
+                f32x4 v[kBatch];
+#pragma unroll
+                for (int i = 0; i < kBatch; ++i)
+                    if (i < n)
+                        v[i] = p[(int64_t)(u0 + i) * 64];
+#pragma unroll
+                for (int i = 0; i < kBatch; ++i)
+                    if (i < n)
+                        acc = (u0 + i == 0) ? v[i] : acc + v[i];
+            }
             const int col = nt * 16 + acc_col(ln);
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
@@ -148,32 +200,29 @@ __global__ __launch_bounds__(kRouteTokens * 64) void k_route(const float* __rest
     for (int off = 1; off <= 32; off <<= 1)
         sum = sum + __shfl_xor(sum, off);
 
-    int rank[kPer];
-    float key[kPer];
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-        rank[i] = 0;
-        key[i] = rank_key(v[i]);
-    }
-    for (int e2 = 0; e2 < E; e2 += 4) {
-        const f32x4 o4 = *reinterpret_cast<const f32x4*>(l + e2);   // same address on every lane
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const float ok = rank_key(o4[j]);
-#pragma unroll
-            for (int i = 0; i < kPer; ++i) {
-                const int e = lane + 64 * i;
-                rank[i] += (ok > key[i] || (ok == key[i] && e2 + j < e)) ? 1 : 0;
-            }
-        }
-    }
+    // Top-k by repeated arg-max over unique 64-bit keys: high word the
+    // logit's order key (NaN as -inf, -0.0 as +0.0), low word ~e, so the
+    // larger logit wins and equal logits go to the lower expert index.
+    uint64_t key[kPer];
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
         const int e = lane + 64 * i;
-        if (e < E && rank[i] < topk) {
-            ids[(int64_t)m * topk + rank[i]] = e;
-            probs[(int64_t)m * topk + rank[i]] = ex[i] / sum;
-        }
+        key[i] = e < E ? ((uint64_t)order_bits(rank_key(v[i])) << 32) | (uint32_t)~(uint32_t)e : 0ull;
+    }
+    for (int j = 0; j < topk; ++j) {
+        uint64_t best = key[0];
+#pragma unroll
+        for (int i = 1; i < kPer; ++i)
+            best = key[i] > best ? key[i] : best;
+        best = wave_max_u64(best);
+#pragma unroll
+        for (int i = 0; i < kPer; ++i)
+            if (key[i] == best) {          // exactly one lane holds the winner
+                const int e = lane + 64 * i;
+                ids[(int64_t)m * topk + j] = e;
+                probs[(int64_t)m * topk + j] = ex[i] / sum;
+                key[i] = 0ull;
+            }
     }
 }
 
