@@ -610,7 +610,9 @@ static hipError_t launch_persistent(const LinearArgs& a, const Plan& p, hipStrea
     int code = p.tile_code;
     // stage width of each shape, in k: shapes whose stage does not divide K
     // fall back to the 32-k-stage shape of the same dtype
-    auto stage_k = [](int c) { return (c == 7 || c == 8 || c == 17) ? 32 : (c == 9 || c == 13 || c == 16) ? 128 : 64; };
+    auto stage_k = [](int c) {
+        return (c == 7 || c == 8 || c == 17) ? 32 : (c == 9 || c == 10 || c == 13 || c == 16) ? 128 : 64;
+    };
     if constexpr (OX::f32_frag) {
         // measured on MI355X for the (fp32, 256, 4096) router: 64x64 on 8
         // waves at M=4096 (99 us), 32x32 at M=1024 and 2048 (48 / 68 us)
@@ -627,6 +629,7 @@ static hipError_t launch_persistent(const LinearArgs& a, const Plan& p, hipStrea
         case 6: return launch_persistent_t<OX, OW, 64, 128, 2, 4, 2>(a, p, s);
         case 8: return launch_persistent_t<OX, OW, 64, 256, 2, 4, 1>(a, p, s);
         case 9: return launch_persistent_t<OX, OW, 32, 64, 2, 2, 4>(a, p, s);
+        case 10: return launch_persistent_t<OX, OW, 64, 64, 4, 2, 4>(a, p, s);
         default: return launch_persistent_t<OX, OW, 32, 32, 2, 2, 1>(a, p, s);
         }
     } else {

@@ -71,161 +71,6 @@ MoELayout moe_layout(int64_t M, int64_t H, int64_t E, int64_t I, int64_t topk, s
 
 }  // namespace
 
-// ------------------------------------------------------------------- routing
-
-constexpr int kRouteTokens = 16;   // tokens per routing workgroup, one wave each
-
-// Ordering key of a logit for the expert choice: NaN ranks like -inf.
-__device__ __forceinline__ float rank_key(float v) { return (v != v) ? -INFINITY : v; }
-
-// Unsigned integer whose order is the order of the (non-NaN) float; -0.0
-// maps like +0.0.
-__device__ __forceinline__ uint32_t order_bits(float v)
-{
-    uint32_t b = __float_as_uint(v);
-    if (b == 0x80000000u)
-        b = 0u;
-    return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
-}
-
-// Maximum over the wave's 64 lanes (wave-uniform result): within each row of
-// 16 lanes by DPP exchanges (neighbours, pairs, half-row mirror, row mirror),
-// then over the four rows through lane reads.
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v)
-{
-    uint32_t hi = (uint32_t)(v >> 32), lo = (uint32_t)v;
-#define BI_DPP_MAX_STEP(CTRL)                                                                     \
-    {                                                                                             \
-        const uint32_t ohi = (uint32_t)__builtin_amdgcn_mov_dpp((int)hi, CTRL, 0xF, 0xF, false);   \
-        const uint32_t olo = (uint32_t)__builtin_amdgcn_mov_dpp((int)lo, CTRL, 0xF, 0xF, false);   \
-        const bool take = ohi > hi || (ohi == hi && olo > lo);                                    \
-        hi = take ? ohi : hi;                                                                     \
-        lo = take ? olo : lo;                                                                     \
-    }
-    BI_DPP_MAX_STEP(0xB1)     // quad_perm 1,0,3,2
-    BI_DPP_MAX_STEP(0x4E)     // quad_perm 2,3,0,1
-    BI_DPP_MAX_STEP(0x141)    // row_half_mirror
-    BI_DPP_MAX_STEP(0x140)    // row_mirror
-#undef BI_DPP_MAX_STEP
-    uint64_t best = 0;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const uint64_t c = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)hi, 16 * r) << 32) |
-                           (uint32_t)__builtin_amdgcn_readlane((int)lo, 16 * r);
-        best = c > best ? c : best;
-    }
-    return best;
-}
-
-// One workgroup per 16 tokens, one wave per token.
-//  1. Logits of the 16 tokens into LDS: either read from `logits` [M,E], or
-//     folded here from the router's k tile partials in ascending tile order
-//     (acc = P0; acc = acc + P1; ...; + bias) -- the linear fold, same bits.
-//  2. Softmax over all E: max (exact), exp, a sum in a fixed order (each
-//     lane ascending over its experts, then a fixed butterfly), p = e / sum.
-//  3. Top-k: slot j receives the j-th largest logit, equal logits in
-//     ascending expert order, -0.0 equal to +0.0 (repeated wave arg-max
-//     over unique keys).
-template <int kPer>   // experts per lane: E <= 64 * kPer
-__global__ __launch_bounds__(kRouteTokens * 64) void k_route(const float* __restrict__ logits,
-                                                             const f32x4* __restrict__ partials,
-                                                             const float* __restrict__ bias, int tiles_k,
-                                                             int M, int E, int topk,
-                                                             int32_t* __restrict__ ids,
-                                                             float* __restrict__ probs)
-{
-    __shared__ float lg[kRouteTokens][kMaxExperts];
-    const int mt = blockIdx.x;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    if (partials) {
-        const int ntiles = E >> 4;
-        for (int pi = tid; pi < ntiles * 64; pi += kRouteTokens * 64) {
-            const int nt = pi >> 6, ln = pi & 63;
-            const f32x4* p = partials + ((int64_t)mt * ntiles + nt) * tiles_k * 64 + ln;
-            // up to 16 partials are requested before the first add, so the
-            // ordered fold costs one memory round trip per 16 k tiles
-            constexpr int kBatch = 16;
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            for (int u0 = 0; u0 < tiles_k; u0 += kBatch) {
-                const int n = min(kBatch, tiles_k - u0);
-                f32x4 v[kBatch];
-#pragma unroll
-                for (int i = 0; i < kBatch; ++i)
-                    if (i < n)
-                        v[i] = p[(int64_t)(u0 + i) * 64];
-#pragma unroll
-                for (int i = 0; i < kBatch; ++i)
-                    if (i < n)
-                        acc = (u0 + i == 0) ? v[i] : acc + v[i];
-            }
-            const int col = nt * 16 + acc_col(ln);
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                float v = acc[q];
-                if (bias)
-                    v = v + bias[col];
-                lg[acc_row(ln, q)][col] = v;
-            }
-        }
-    } else {
-        for (int i = tid; i < kRouteTokens * E; i += kRouteTokens * 64) {
-            const int r = i / E, e = i % E;
-            const int m = mt * kRouteTokens + r;
-            lg[r][e] = m < M ? logits[(int64_t)m * E + e] : 0.f;
-        }
-    }
-    __syncthreads();
-    const int m = mt * kRouteTokens + wave;
-    if (m >= M)
-        return;
-    const float* l = lg[wave];
-    float v[kPer];
-    float mx = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-        const int e = lane + 64 * i;
-        v[i] = e < E ? l[e] : -INFINITY;
-        mx = fmaxf(mx, v[i]);
-    }
-    for (int off = 32; off >= 1; off >>= 1)
-        mx = fmaxf(mx, __shfl_xor(mx, off));
-    float ex[kPer];
-    float sum = 0.f;
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-        const int e = lane + 64 * i;
-        ex[i] = e < E ? expf(v[i] - mx) : 0.f;
-        sum = sum + ex[i];
-    }
-    for (int off = 1; off <= 32; off <<= 1)
-        sum = sum + __shfl_xor(sum, off);
-
-    // Top-k by repeated arg-max over unique 64-bit keys: high word the
-    // logit's order key (NaN as -inf, -0.0 as +0.0), low word ~e, so the
-    // larger logit wins and equal logits go to the lower expert index.
-    uint64_t key[kPer];
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-        const int e = lane + 64 * i;
-        key[i] = e < E ? ((uint64_t)order_bits(rank_key(v[i])) << 32) | (uint32_t)~(uint32_t)e : 0ull;
-    }
-    for (int j = 0; j < topk; ++j) {
-        uint64_t best = key[0];
-#pragma unroll
-        for (int i = 1; i < kPer; ++i)
-            best = key[i] > best ? key[i] : best;
-        best = wave_max_u64(best);
-#pragma unroll
-        for (int i = 0; i < kPer; ++i)
-            if (key[i] == best) {          // exactly one lane holds the winner
-                const int e = lane + 64 * i;
-                ids[(int64_t)m * topk + j] = e;
-                probs[(int64_t)m * topk + j] = ex[i] / sum;
-                key[i] = 0ull;
-            }
-    }
-}
-
 // ------------------------------------------------------------------ dispatch
 
 // Stable counting sort of the M*topk (token, slot) pairs by expert, tokens
@@ -233,13 +78,10 @@ __global__ __launch_bounds__(kRouteTokens * 64) void k_route(const float* __rest
 // 1024 threads.  A token selects an expert at most once, so within a chunk
 // of 64 tokens a pair's rank among the expert's pairs is a popcount of the
 // chunk's per-expert token mask below it.
-__global__ __launch_bounds__(1024) void k_dispatch(const int32_t* __restrict__ ids, int M, int E, int topk,
-                                                   int unit_rows,
-                                                   int32_t* __restrict__ offsets,
-                                                   int32_t* __restrict__ sorted,
-                                                   int32_t* __restrict__ unit_expert,
-                                                   int32_t* __restrict__ unit_row,
-                                                   int32_t* __restrict__ nunits)
+__device__ __forceinline__ void dispatch_body(const int32_t* ids, int M, int E, int topk, int unit_rows,
+                                              int32_t* __restrict__ offsets, int32_t* __restrict__ sorted,
+                                              int32_t* __restrict__ unit_expert, int32_t* __restrict__ unit_row,
+                                              int32_t* __restrict__ nunits)
 {
     __shared__ int cnt[kMaxExperts];
     __shared__ int cursor[kMaxExperts];
@@ -315,6 +157,198 @@ __global__ __launch_bounds__(1024) void k_dispatch(const int32_t* __restrict__ i
         __syncthreads();
     }
 }
+
+__global__ __launch_bounds__(1024) void k_dispatch(const int32_t* __restrict__ ids, int M, int E, int topk,
+                                                   int unit_rows,
+                                                   int32_t* __restrict__ offsets,
+                                                   int32_t* __restrict__ sorted,
+                                                   int32_t* __restrict__ unit_expert,
+                                                   int32_t* __restrict__ unit_row,
+                                                   int32_t* __restrict__ nunits)
+{
+    dispatch_body(ids, M, E, topk, unit_rows, offsets, sorted, unit_expert, unit_row, nunits);
+}
+
+// ------------------------------------------------------------------- routing
+
+constexpr int kRouteTokens = 16;   // tokens per routing workgroup, one wave each
+
+// Outputs of the dispatch step when it runs inside the routing kernel.
+struct DispatchOut {
+    int unit_rows;
+    int32_t* offsets;
+    int32_t* sorted;
+    int32_t* unit_expert;
+    int32_t* unit_row;
+    int32_t* nunits;
+};
+
+// Ordering key of a logit for the expert choice: NaN ranks like -inf.
+__device__ __forceinline__ float rank_key(float v) { return (v != v) ? -INFINITY : v; }
+
+// Unsigned integer whose order is the order of the (non-NaN) float; -0.0
+// maps like +0.0.
+__device__ __forceinline__ uint32_t order_bits(float v)
+{
+    uint32_t b = __float_as_uint(v);
+    if (b == 0x80000000u)
+        b = 0u;
+    return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+// Maximum over the wave's 64 lanes (wave-uniform result): within each row of
+// 16 lanes by DPP exchanges (neighbours, pairs, half-row mirror, row mirror),
+// then over the four rows through lane reads.
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v)
+{
+    uint32_t hi = (uint32_t)(v >> 32), lo = (uint32_t)v;
+#define BI_DPP_MAX_STEP(CTRL)                                                                     \
+    {                                                                                             \
+        const uint32_t ohi = (uint32_t)__builtin_amdgcn_mov_dpp((int)hi, CTRL, 0xF, 0xF, false);   \
+        const uint32_t olo = (uint32_t)__builtin_amdgcn_mov_dpp((int)lo, CTRL, 0xF, 0xF, false);   \
+        const bool take = ohi > hi || (ohi == hi && olo > lo);                                    \
+        hi = take ? ohi : hi;                                                                     \
+        lo = take ? olo : lo;                                                                     \
+    }
+    BI_DPP_MAX_STEP(0xB1)     // quad_perm 1,0,3,2
+    BI_DPP_MAX_STEP(0x4E)     // quad_perm 2,3,0,1
+    BI_DPP_MAX_STEP(0x141)    // row_half_mirror
+    BI_DPP_MAX_STEP(0x140)    // row_mirror
+#undef BI_DPP_MAX_STEP
+    uint64_t best = 0;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const uint64_t c = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)hi, 16 * r) << 32) |
+                           (uint32_t)__builtin_amdgcn_readlane((int)lo, 16 * r);
+        best = c > best ? c : best;
+    }
+    return best;
+}
+
+// Softmax and top-k of one token (one wave): see k_route.
+template <int kPer, bool FUSE>
+__device__ __forceinline__ void route_token(const float* l, int lane, int m, int E, int topk,
+                                            int32_t* __restrict__ ids, float* __restrict__ probs, int32_t* sid)
+{
+    float v[kPer];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+        const int e = lane + 64 * i;
+        v[i] = e < E ? l[e] : -INFINITY;
+        mx = fmaxf(mx, v[i]);
+    }
+    for (int off = 32; off >= 1; off >>= 1)
+        mx = fmaxf(mx, __shfl_xor(mx, off));
+    float ex[kPer];
+    float sum = 0.f;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+        const int e = lane + 64 * i;
+        ex[i] = e < E ? expf(v[i] - mx) : 0.f;
+        sum = sum + ex[i];
+    }
+    for (int off = 1; off <= 32; off <<= 1)
+        sum = sum + __shfl_xor(sum, off);
+
+    // Top-k by repeated arg-max over unique 64-bit keys: high word the
+    // logit's order key (NaN as -inf, -0.0 as +0.0), low word ~e, so the
+    // larger logit wins and equal logits go to the lower expert index.
+    uint64_t key[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+        const int e = lane + 64 * i;
+        key[i] = e < E ? ((uint64_t)order_bits(rank_key(v[i])) << 32) | (uint32_t)~(uint32_t)e : 0ull;
+    }
+    for (int j = 0; j < topk; ++j) {
+        uint64_t best = key[0];
+#pragma unroll
+        for (int i = 1; i < kPer; ++i)
+            best = key[i] > best ? key[i] : best;
+        best = wave_max_u64(best);
+#pragma unroll
+        for (int i = 0; i < kPer; ++i)
+            if (key[i] == best) {          // exactly one lane holds the winner
+                const int e = lane + 64 * i;
+                ids[(int64_t)m * topk + j] = e;
+                probs[(int64_t)m * topk + j] = ex[i] / sum;
+                if (FUSE)
+                    sid[j] = e;
+                key[i] = 0ull;
+            }
+    }
+}
+
+// One workgroup per 16 tokens, one wave per token.
+//  1. Logits of the 16 tokens into LDS: either read from `logits` [M,E], or
+//     folded here from the router's k tile partials in ascending tile order
+//     (acc = P0; acc = acc + P1; ...; + bias) -- the linear fold, same bits.
+//  2. Softmax over all E: max (exact), exp, a sum in a fixed order (each
+//     lane ascending over its experts, then a fixed butterfly), p = e / sum.
+//  3. Top-k: slot j receives the j-th largest logit, equal logits in
+//     ascending expert order, -0.0 equal to +0.0 (repeated wave arg-max
+//     over unique keys).
+//  4. FUSE (a single workgroup, M <= 16): the dispatch of the next step runs
+//     in the same workgroup on the ids just chosen, saving a launch.
+template <int kPer, bool FUSE>   // experts per lane: E <= 64 * kPer
+__global__ __launch_bounds__(kRouteTokens * 64) void k_route(const float* __restrict__ logits,
+                                                             const f32x4* __restrict__ partials,
+                                                             const float* __restrict__ bias, int tiles_k,
+                                                             int M, int E, int topk,
+                                                             int32_t* __restrict__ ids,
+                                                             float* __restrict__ probs, DispatchOut d)
+{
+    __shared__ float lg[kRouteTokens][kMaxExperts];
+    __shared__ int32_t sids[FUSE ? kRouteTokens * kMaxTopk : 1];
+    const int mt = blockIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    if (partials) {
+        const int ntiles = E >> 4;
+        for (int pi = tid; pi < ntiles * 64; pi += kRouteTokens * 64) {
+            const int nt = pi >> 6, ln = pi & 63;
+            const f32x4* p = partials + ((int64_t)mt * ntiles + nt) * tiles_k * 64 + ln;
+            // up to 16 partials are requested before the first add, so the
+            // ordered fold costs one memory round trip per 16 k tiles
+            constexpr int kBatch = 16;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            for (int u0 = 0; u0 < tiles_k; u0 += kBatch) {
+                const int n = min(kBatch, tiles_k - u0);
+                f32x4 v[kBatch];
+#pragma unroll
+                for (int i = 0; i < kBatch; ++i)
+                    if (i < n)
+                        v[i] = p[(int64_t)(u0 + i) * 64];
+#pragma unroll
+                for (int i = 0; i < kBatch; ++i)
+                    if (i < n)
+                        acc = (u0 + i == 0) ? v[i] : acc + v[i];
+            }
+            const int col = nt * 16 + acc_col(ln);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                float v = acc[q];
+                if (bias)
+                    v = v + bias[col];
+                lg[acc_row(ln, q)][col] = v;
+            }
+        }
+    } else {
+        for (int i = tid; i < kRouteTokens * E; i += kRouteTokens * 64) {
+            const int r = i / E, e = i % E;
+            const int m = mt * kRouteTokens + r;
+            lg[r][e] = m < M ? logits[(int64_t)m * E + e] : 0.f;
+        }
+    }
+    __syncthreads();
+    const int m = mt * kRouteTokens + wave;
+    if (m < M)
+        route_token<kPer, FUSE>(lg[wave], lane, m, E, topk, ids, probs, sids + wave * topk);
+    if constexpr (FUSE) {
+        __syncthreads();
+        dispatch_body(sids, M, E, topk, d.unit_rows, d.offsets, d.sorted, d.unit_expert, d.unit_row, d.nunits);
+    }
+}
+
 
 // ------------------------------------------------------------ grouped GEMMs
 
@@ -655,21 +689,32 @@ bi_status_t moe_run(const uint16_t* x, const float* w_router, const float* b_rou
     const unsigned route_groups = (unsigned)((M + kRouteTokens - 1) / kRouteTokens);
     const float* lsrc = fused_fold ? nullptr : logits;
     const f32x4* psrc = fused_fold ? reinterpret_cast<const f32x4*>(base + L.router_ws) : nullptr;
-    if (E <= 128)
-        k_route<2><<<route_groups, kRouteTokens * 64, 0, stream>>>(lsrc, psrc, b_router, pr.tiles_k, (int)M,
-                                                                   (int)E, (int)topk, topk_ids, topk_probs);
-    else if (E <= 256)
-        k_route<4><<<route_groups, kRouteTokens * 64, 0, stream>>>(lsrc, psrc, b_router, pr.tiles_k, (int)M,
-                                                                   (int)E, (int)topk, topk_ids, topk_probs);
-    else if (E <= 512)
-        k_route<8><<<route_groups, kRouteTokens * 64, 0, stream>>>(lsrc, psrc, b_router, pr.tiles_k, (int)M,
-                                                                   (int)E, (int)topk, topk_ids, topk_probs);
-    else
-        k_route<16><<<route_groups, kRouteTokens * 64, 0, stream>>>(lsrc, psrc, b_router, pr.tiles_k, (int)M,
-                                                                    (int)E, (int)topk, topk_ids, topk_probs);
     const int unit_rows = unit_rows_for(M, E, topk);
-    k_dispatch<<<1, 1024, 0, stream>>>(topk_ids, (int)M, (int)E, (int)topk, unit_rows, offsets, sorted,
-                                       unit_expert, unit_row, nunits);
+    const DispatchOut dout{unit_rows, offsets, sorted, unit_expert, unit_row, nunits};
+    // one routing workgroup (M <= 16): the dispatch runs inside it
+    const bool fuse = route_groups == 1;
+#define BI_ROUTE(KPER)                                                                                      \
+    do {                                                                                                    \
+        if (fuse)                                                                                           \
+            k_route<KPER, true><<<1, kRouteTokens * 64, 0, stream>>>(lsrc, psrc, b_router, pr.tiles_k,      \
+                                                                     (int)M, (int)E, (int)topk, topk_ids,  \
+                                                                     topk_probs, dout);                    \
+        else                                                                                                \
+            k_route<KPER, false><<<route_groups, kRouteTokens * 64, 0, stream>>>(                           \
+                lsrc, psrc, b_router, pr.tiles_k, (int)M, (int)E, (int)topk, topk_ids, topk_probs, dout);   \
+    } while (0)
+    if (E <= 128)
+        BI_ROUTE(2);
+    else if (E <= 256)
+        BI_ROUTE(4);
+    else if (E <= 512)
+        BI_ROUTE(8);
+    else
+        BI_ROUTE(16);
+#undef BI_ROUTE
+    if (!fuse)
+        k_dispatch<<<1, 1024, 0, stream>>>(topk_ids, (int)M, (int)E, (int)topk, unit_rows, offsets, sorted,
+                                           unit_expert, unit_row, nunits);
     if (hipGetLastError() != hipSuccess)
         return BI_EHIP;
 

@@ -125,7 +125,7 @@ int device_cu_count()
 bool tile_code_valid(int dtype, int code)
 {
     if (dtype == BI_F32)
-        return (code >= 1 && code <= 9);
+        return (code >= 1 && code <= 10);
     return code >= 11 && code <= 19;
 }
 

@@ -51,7 +51,7 @@ DECODE_M = (1, 8, 16, 32, 64, 128)
 PREFILL_M = (256, 1024, 4096)
 TABLE_HEADER = ("// Measured key table, written by deterministic_persistent_gemm_amd/sweep.py.\n"
                 "// {dtype, N, K, block_k, m_decode_max, decode_path, m_a, tile_a, m_b, tile_b, tile_c}\n")
-F32_CODES = tuple(range(1, 10))
+F32_CODES = tuple(range(1, 11))
 BF16_CODES = tuple(range(11, 20))
 PATH_DECODE, PATH_PERSISTENT, PATH_DECODE_WG = 1, 2, 3
 
@@ -70,7 +70,7 @@ def parse_key(s: str, profile: str = "decode"):
 def stage_k(code: int) -> int:
     """k per LDS stage of a persistent tile shape (shapes whose stage does
     not divide K are served by the 32-k-stage shape of the dtype)."""
-    return 32 if code in (7, 8, 17) else 128 if code in (9, 13, 16) else 64
+    return 32 if code in (7, 8, 17) else 128 if code in (9, 10, 13, 16) else 64
 
 
 def tile_codes(dt: str, K: int, block_k: int):
