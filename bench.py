@@ -39,7 +39,7 @@ N_COPIES = 96
 # PMC runs: FETCH_SIZE scaled x2.0 and WRITE_SIZE x1.0 by a 512 MiB copy of known size (see
 # profiles/router_decode_hbm_bytes.md).  Valid only for the kernel sources with this digest; any
 # later change to them reports traffic as null until the counters are taken again.
-MEASURED_TRAFFIC = {"sources_sha256": "78eccd7d004dd8a7c14488f1042456af5a3550dc86bf3e0dd8ad44538a747b37", "bytes_per_call": 6834822}
+MEASURED_TRAFFIC = {"sources_sha256": "2b17dca953a49b059631408d10071518cfefaceeb07c04af8937da515755ae13", "bytes_per_call": 6819572}
 KERNEL_SOURCES = ("bi_device.h", "bi_launch.h", "bi_linear.hip", "bi_plan.cpp", "bi_plan.h")
 
 

@@ -23,7 +23,7 @@ LIB_PATH = os.path.join(_PKG, "libbi.so")
 
 BI_OK, BI_EINVAL, BI_EUNSUPPORTED, BI_EWORKSPACE, BI_EHIP = range(5)
 BI_F32, BI_BF16 = 0, 1
-BI_PATH_AUTO, BI_PATH_DECODE, BI_PATH_PERSISTENT, BI_PATH_DECODE_WG = 0, 1, 2, 3
+BI_PATH_AUTO, BI_PATH_DECODE, BI_PATH_PERSISTENT, BI_PATH_DECODE_WG, BI_PATH_DECODE_DMA = 0, 1, 2, 3, 4
 BI_R2_TILE_PARTIAL = 2
 BI_MFMA_F32_16X16X4_F32, BI_MFMA_F32_16X16X32_BF16 = 1, 2
 

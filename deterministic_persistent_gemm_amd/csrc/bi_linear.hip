@@ -241,6 +241,176 @@ __global__ __launch_bounds__(NW * 64) void k_decode_wg(LinearArgs a, int kbpt, i
     store_acc(a, row0, nt * 16 + acc_col(lane), acc);
 }
 
+// Decode for a fully chained bf16 recipe (one tile partial): one workgroup
+// per 16-column N tile and all M tiles (MT <= 4).  The chain itself is short
+// (one 16x16x32 instruction per 32 k per M tile), so the wave that runs it
+// would otherwise wait on its own loads; here kLoaders waves stream the
+// weight slab and the activation rows into an LDS ring with direct-to-LDS
+// loads (each k block of 16 rows lands as one 1 KiB chunk laid out exactly
+// as the fragment lanes read it), several phases ahead, and wave 0 only
+// reads LDS and issues the chain.  Phases are handed over with one barrier
+// each; a loader waits for its own loads of a phase before the barrier.
+constexpr int kDmaLoaders = 8;
+
+// One 16-byte direct-to-LDS load per lane: lane i's bytes land at LDS byte
+// address `lds` + 16 i (M0 holds the wave's base).  Written as inline
+// assembly so that the compiler does not order every such load after the
+// previous one (it would treat each as an aliasing LDS write and wait for
+// all earlier ones); the waits are explicit below instead.
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds)
+{
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(g), "s"(lds) : "memory", "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p)
+{
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// s_waitcnt with vmcnt <= N (N < 64), other counters untouched
+template <int N>
+__device__ __forceinline__ void wait_vm()
+{
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
+}
+
+// s_waitcnt lgkmcnt(0), other counters untouched
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xF | (0x7 << 4) | (0x3 << 14)); }
+
+// A workgroup barrier without the memory fence of __syncthreads (whose
+// release would wait for every outstanding load); the callers wait for
+// exactly what the other side needs first.
+__device__ __forceinline__ void bar() { asm volatile("s_barrier" : : : "memory"); }
+
+// vmcnt <= later * LW for a runtime later in [0, C]
+template <int LW, int C>
+__device__ __forceinline__ void wait_later(int later)
+{
+    if constexpr (C <= 0) {
+        wait_vm<0>();
+    } else {
+        if (later >= C)
+            wait_vm<C * LW>();
+        else
+            wait_later<LW, C - 1>(later);
+    }
+}
+
+// MT M tiles, PB k blocks per phase, a ring of R phases in LDS.
+// XR > 0 (MT = 1, M <= XR, K <= kDmaXMaxK): the first XR activation rows are
+// loaded once into LDS at the start (16-byte chunks, row-major), so the ring
+// holds the weight only and can run further ahead; rows past M are never
+// stored, so lanes of those rows read row M-1.  XR = 0: each k block's
+// activation tiles travel in the ring beside the weight.
+constexpr int kDmaXMaxK = 4096;
+
+template <int MT, int PB, int R, int XR>
+__global__ __launch_bounds__((kDmaLoaders + 1) * 64) void k_decode_dma(LinearArgs a)
+{
+    static_assert(XR == 0 || MT == 1, "activation rows in LDS for one M tile");
+    constexpr int IPB = XR ? 1 : 1 + MT;              // 1 KiB items per k block: W (then MT X tiles)
+    constexpr int IT = XR ? 16 : PB * IPB;            // items per phase (XR: one weight row each)
+    constexpr int LW = IT / kDmaLoaders;              // items per loader per phase
+    static_assert(IT % kDmaLoaders == 0, "items split evenly");
+    static_assert(R >= 2 && (R - 2) * LW < 64, "ring depth");
+    static_assert(!XR || PB * 4 == 64, "a weight row of a phase is one 1 KiB load");
+    // XR: row i of the 16-row weight slab at ring[.][i], its PB*32 k values
+    // contiguous (1 KiB, one load), rows 1040 bytes apart so that the 16 rows
+    // of a fragment read fall on different banks
+    constexpr int kRowPitch = XR ? 65 : 64;
+    __shared__ u32x4 ring[R][IT][kRowPitch];
+    __shared__ u32x4 xs[XR ? XR * kDmaXMaxK / 8 : 1];
+
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int r = lane & 15, g = lane >> 4;
+    const int nt = blockIdx.x;
+    const int nblk = a.K / kKBlock;
+    const int P = nblk / PB;
+    const int kc = a.K / 8;                           // 16-byte chunks per activation row
+    const uint16_t* xbase = reinterpret_cast<const uint16_t*>(a.x);
+
+    if (wave > 0) {
+        if constexpr (XR > 0) {
+            // the activation rows, once: chunk c of row c / kc, 64 chunks per load
+            const int nload = (XR * kc) / 64;
+            for (int d = wave - 1; d < nload; d += kDmaLoaders) {
+                const int c = d * 64 + lane;
+                const int row = min(c / kc, a.M - 1);
+                dma16(xbase + (int64_t)row * a.ldx + (c % kc) * 8,
+                      (uint32_t)__builtin_amdgcn_readfirstlane((int)lds_addr(&xs[d * 64])));
+            }
+        }
+        // loader: items i = (wave - 1) + kDmaLoaders * t of every phase
+        const uint16_t* wrow = reinterpret_cast<const uint16_t*>(a.w) + (int64_t)(nt * 16 + r) * a.ldw + kSlotLen * g;
+        const uint16_t* wslab = reinterpret_cast<const uint16_t*>(a.w) + (int64_t)(nt * 16) * a.ldw + 8 * lane;
+        auto issue = [&](int ph) {
+            if constexpr (XR > 0) {
+                // whole rows: lane l takes k = ph*PB*32 + 8l .. +7 of row i
+#pragma unroll
+                for (int t = 0; t < LW; ++t) {
+                    const int i = (wave - 1) + kDmaLoaders * t;
+                    dma16(wslab + (int64_t)i * a.ldw + (int64_t)ph * PB * kKBlock,
+                          (uint32_t)__builtin_amdgcn_readfirstlane((int)lds_addr(&ring[ph % R][i][0])));
+                }
+                return;
+            }
+#pragma unroll
+            for (int t = 0; t < LW; ++t) {
+                const int i = (wave - 1) + kDmaLoaders * t;
+                const int j = i / IPB, kind = i % IPB;      // kind 0: W, m + 1: X tile m
+                const int64_t k0 = (int64_t)(ph * PB + j) * kKBlock;
+                // rows past M read row M-1 (always valid); their results are never stored
+                const int xr = min((kind - 1) * 16 + r, a.M - 1);
+                const uint16_t* src =
+                    kind == 0 ? wrow + k0 : xbase + (int64_t)max(xr, 0) * a.ldx + kSlotLen * g + k0;
+                dma16(src, (uint32_t)__builtin_amdgcn_readfirstlane((int)lds_addr(&ring[ph % R][i][0])));
+            }
+        };
+        for (int ph = 0; ph < R - 1 && ph < P; ++ph)
+            issue(ph);
+        for (int ph = 0; ph < P; ++ph) {
+            // this loader's loads up to phase ph (the activation rows first)
+            // have landed once at most the later phases in flight,
+            // min(R - 2, P - 1 - ph), are outstanding
+            wait_later<LW, R - 2>(min(R - 2, P - 1 - ph));
+            bar();
+            if (ph + R - 1 < P)
+                issue(ph + R - 1);
+        }
+        return;
+    }
+
+    // wave 0: the chains
+    f32x4 acc[MT][1];
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+        acc[m][0] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int xrow = min(r, a.M - 1);
+    for (int ph = 0; ph < P; ++ph) {
+        wait_lgkm0();          // the previous phase's LDS reads are done before its slot is refilled
+        bar();
+        const u32x4(*slot)[kRowPitch] = ring[ph % R];
+#pragma unroll
+        for (int j = 0; j < PB; ++j) {
+            FragOf<BF16> wf[1], xf[MT];
+            if constexpr (XR > 0) {
+                wf[0].v = slot[r][j * 4 + g];
+                xf[0].v = xs[xrow * kc + (ph * PB + j) * 4 + g];
+            } else {
+                wf[0].v = slot[j * IPB][lane];
+#pragma unroll
+                for (int m = 0; m < MT; ++m)
+                    xf[m].v = slot[j * IPB + 1 + m][lane];
+            }
+            mfma_tiles<MT, 1>(xf, wf, acc);
+        }
+    }
+    const int col = nt * 16 + acc_col(lane);
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+        store_acc(a, m * 16 + acc_row(lane, 0), col, acc[m][0]);
+}
+
 // One LDS stage holds KBS k blocks of BM rows of X and BN rows of W.  Each
 // thread moves whole 16-byte chunks: consecutive threads take consecutive
 // chunks of a row, so a row segment is read with coalesced 16-byte loads.
@@ -563,6 +733,41 @@ static hipError_t launch_decode_wg_nw(const LinearArgs& a, const Plan& p, hipStr
     return hipGetLastError();
 }
 
+// The direct-to-LDS decode serves chained bf16 recipes with M <= 64 and K a
+// multiple of a phase (16 k blocks at MT = 1, 8 at MT = 2, 4 at MT = 4).
+// k blocks per phase for MT M tiles (a phase holds PB x (1 + MT) KiB)
+static int dma_phase_blocks(int mtiles) { return mtiles == 1 ? 16 : 8; }
+
+bool decode_dma_ok(const Plan& p, int64_t K)
+{
+    if (p.recipe.dtype != BI_BF16 || p.tiles_k != 1 || p.mtiles < 1 || p.mtiles > 4)
+        return false;
+    return K % (dma_phase_blocks(p.mtiles) * kKBlock) == 0;
+}
+
+static hipError_t launch_decode_dma(const LinearArgs& a, const Plan& p, hipStream_t s)
+{
+    if (!decode_dma_ok(p, a.K))
+        return hipErrorInvalidValue;
+    const dim3 grid((unsigned)p.ntiles);
+    const int threads = (kDmaLoaders + 1) * 64;
+    // LDS: ring R x PB x (items per block) KiB, plus XR activation rows of
+    // up to 8 KiB each
+    if (p.mtiles == 1 && a.K <= kDmaXMaxK && a.M == 1)
+        k_decode_dma<1, 16, 8, 1><<<grid, threads, 0, s>>>(a);      // 128 + 8 KiB
+    else if (p.mtiles == 1 && a.K <= kDmaXMaxK && a.M <= 4)
+        k_decode_dma<1, 16, 7, 4><<<grid, threads, 0, s>>>(a);      // 112 + 32 KiB
+    else if (p.mtiles == 1 && a.K <= kDmaXMaxK && a.M <= 8)
+        k_decode_dma<1, 16, 5, 8><<<grid, threads, 0, s>>>(a);      // 80 + 64 KiB
+    else if (p.mtiles == 1)
+        k_decode_dma<1, 16, 4, 0><<<grid, threads, 0, s>>>(a);      // 128 KiB, activation in the ring
+    else if (p.mtiles == 2)
+        k_decode_dma<2, 8, 4, 0><<<grid, threads, 0, s>>>(a);       // 96 KiB
+    else
+        k_decode_dma<4, 8, 3, 0><<<grid, threads, 0, s>>>(a);       // 120 KiB (3 M tiles read a clamped 4th)
+    return hipGetLastError();
+}
+
 template <typename OX, typename OW>
 static hipError_t launch_decode_wg(const LinearArgs& a, const Plan& p, hipStream_t s)
 {
@@ -665,6 +870,10 @@ static hipError_t launch_typed(const LinearArgs& a, const Plan& p, void* ws, hip
 {
     if (p.path == kPathDecodeWg && fold)
         return launch_decode_wg<OX, OW>(a, p, s);
+    if constexpr (!OX::f32_frag) {
+        if (p.path == kPathDecodeDma)
+            return launch_decode_dma(a, p, s);
+    }
     if (p.path == kPathDecode || p.path == kPathDecodeWg)
         return launch_decode<OX, OW>(a, p, ws, s, fold);
     return launch_persistent<OX, OW>(a, p, s);

@@ -162,6 +162,10 @@ bi_status_t make_plan(const bi_recipe_t& r, int32_t path_req, int64_t M, int64_t
         if (!wg_ok)
             return BI_EUNSUPPORTED;
         p.path = kPathDecodeWg;
+    } else if (path_req == BI_PATH_DECODE_DMA) {
+        if (!decode_dma_ok(p, K))
+            return BI_EUNSUPPORTED;
+        p.path = kPathDecodeDma;
     } else if (path_req == BI_PATH_PERSISTENT)
         p.path = kPathPersistent;
     else if (path_req == BI_PATH_AUTO) {
@@ -173,14 +177,20 @@ bi_status_t make_plan(const bi_recipe_t& r, int32_t path_req, int64_t M, int64_t
         // call, cold W: (bf16, 1536, 2048) M=1 6.9 vs 9.1 us two-launch;
         // (fp32, 256, 4096) M=1 13.8 vs 9.6 us.
         const int64_t slab = K * (r.dtype == BI_F32 ? 4 : 2);
+        // A fully chained bf16 recipe streams its weight through LDS with
+        // direct-to-LDS loads for one chain wave: (bf16, 4096, 4096) M=1
+        // 10.8 us against 14.1 us for one wave per N tile.
+        const bool dma_ok = decode_dma_ok(p, K);
         if (M > r.m_decode_max)
             p.path = kPathPersistent;
         else if (e && e->decode_path == BI_PATH_DECODE)
             p.path = kPathDecode;
         else if (e && e->decode_path == BI_PATH_DECODE_WG && wg_ok)
             p.path = kPathDecodeWg;
+        else if (e && e->decode_path == BI_PATH_DECODE_DMA && dma_ok)
+            p.path = kPathDecodeDma;
         else
-            p.path = (wg_ok && slab <= 4096) ? kPathDecodeWg : kPathDecode;
+            p.path = (wg_ok && slab <= 4096) ? kPathDecodeWg : dma_ok ? kPathDecodeDma : kPathDecode;
         if (p.path == kPathPersistent && e) {
             const int code = M <= e->m_a ? e->tile_a : (M <= e->m_b ? e->tile_b : e->tile_c);
             if (tile_code_valid(r.dtype, code))

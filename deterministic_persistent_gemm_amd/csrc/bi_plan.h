@@ -8,7 +8,7 @@
 
 namespace bi {
 
-enum Path { kPathDecode = 1, kPathPersistent = 2, kPathDecodeWg = 3 };
+enum Path { kPathDecode = 1, kPathPersistent = 2, kPathDecodeWg = 3, kPathDecodeDma = 4 };
 
 // Most tile partials the one-launch decode kernel keeps in LDS (64 KiB).
 constexpr int kDecodeWgMaxTiles = 64;
@@ -27,7 +27,7 @@ struct KeyEntry {
     int64_t N, K;
     int32_t block_k;        // recipe: width of one k tile partial
     int32_t m_decode_max;   // largest M on a decode kernel
-    int32_t decode_path;    // BI_PATH_DECODE or BI_PATH_DECODE_WG (0: automatic)
+    int32_t decode_path;    // BI_PATH_DECODE, _DECODE_WG or _DECODE_DMA (0: automatic)
     // persistent tile codes (0: automatic): tile_a for M <= m_a, tile_b for
     // m_a < M <= m_b, tile_c above
     int64_t m_a;
@@ -67,6 +67,9 @@ bi_status_t make_plan(const bi_recipe_t& r, int32_t path_req, int64_t M, int64_t
 
 // Persistent tile shapes selectable through the experiment entry point.
 bool tile_code_valid(int dtype, int code);
+
+// Whether the direct-to-LDS decode kernel serves this plan (bi_linear.hip).
+bool decode_dma_ok(const Plan& p, int64_t K);
 
 // Number of compute units of the current device (cached per device).
 int device_cu_count();

@@ -15,8 +15,9 @@ persistent kernel takes over, the persistent tile shape per M range) only
 picks kernel shapes.  For each candidate block_k of a key the sweeper times,
 with cold weights (rotating copies, beyond the Infinity Cache):
 
-  * both decode forms (two launches with a workspace fold, one launch with an
-    LDS fold) at M in DECODE_M;
+  * every decode form that serves the candidate (two launches with a
+    workspace fold, one launch with an LDS fold, direct-to-LDS streaming for
+    a chained bf16 recipe) at M in DECODE_M;
   * every persistent tile shape at M in PREFILL_M and at the decode sizes
     where the persistent kernel might take over;
 
@@ -53,7 +54,7 @@ TABLE_HEADER = ("// Measured key table, written by deterministic_persistent_gemm
                 "// {dtype, N, K, block_k, m_decode_max, decode_path, m_a, tile_a, m_b, tile_b, tile_c}\n")
 F32_CODES = tuple(range(1, 11))
 BF16_CODES = tuple(range(11, 20))
-PATH_DECODE, PATH_PERSISTENT, PATH_DECODE_WG = 1, 2, 3
+PATH_DECODE, PATH_PERSISTENT, PATH_DECODE_WG, PATH_DECODE_DMA = 1, 2, 3, 4
 
 
 def parse_key(s: str, profile: str = "decode"):
@@ -274,11 +275,11 @@ def sweep_key(dt: str, N: int, K: int, profile: str, tie: float = 0.03, log=prin
 
             if M in DECODE_M:
                 cand["decode"][M] = {}
-                for path in (PATH_DECODE, PATH_DECODE_WG):
+                for path in (PATH_DECODE, PATH_DECODE_WG, PATH_DECODE_DMA):
                     try:
                         run(path)
                     except bi.BIError:
-                        continue                       # the one-launch form needs 2..64 k tiles
+                        continue                       # a form that does not serve this recipe / M
                     check(f"decode path {path}")
                     cand["decode"][M][path] = _timeit(torch, [lambda w=w, p=path: run(p, w) for w in ws])
             cand["persistent"][M] = {}

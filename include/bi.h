@@ -211,7 +211,11 @@ const char* bi_status_str(bi_status_t status);
  * separate waves across the chip, folded by a second launch (workspace).
  * BI_PATH_DECODE_WG: one workgroup per 16x16 output tile whose waves share
  * the k tile partials through LDS, one launch, no workspace (recipes with 2
- * to 64 k tiles; BI_EUNSUPPORTED otherwise).  With BI_PATH_PERSISTENT, bits 8..15
+ * to 64 k tiles; BI_EUNSUPPORTED otherwise).  BI_PATH_DECODE_DMA: fully
+ * chained bf16 recipes at M <= 64, one workgroup per 16 columns whose loader
+ * waves stream W and X into LDS with direct-to-LDS loads for one chain wave
+ * (K a multiple of 512 at M <= 16, 256 at M <= 64;
+ * BI_EUNSUPPORTED otherwise).  With BI_PATH_PERSISTENT, bits 8..15
  * of `path` may name a persistent tile shape (0: automatic; fp32: 1 = 64x64,
  * 2 = 32x64, 3 = 32x32, 4 = 64x64 on 8 waves, 5 = 128x64, 6 = 64x128,
  * 7 = 32x32 with 32-k stages, 8 = 64x256 with 32-k stages, 9 = 32x64 with
@@ -220,7 +224,8 @@ const char* bi_status_str(bi_status_t status);
  * 14 = 256x128, 15 = 128x256, 16 = 64x128 with 128-k stages, 17 = 64x64
  * with 32-k stages, 18 = 256x256 on 2x4 waves, 19 = 256x256 on 4x2 waves).
  * Tile shapes never change the numerics. */
-enum { BI_PATH_AUTO = 0, BI_PATH_DECODE = 1, BI_PATH_PERSISTENT = 2, BI_PATH_DECODE_WG = 3 };
+enum { BI_PATH_AUTO = 0, BI_PATH_DECODE = 1, BI_PATH_PERSISTENT = 2, BI_PATH_DECODE_WG = 3,
+       BI_PATH_DECODE_DMA = 4 };
 
 /* The same linear layer with an explicit recipe and an explicit kernel path,
  * for A/B experiments (e.g. fully chained vs tile-partial, or one BLOCK_K

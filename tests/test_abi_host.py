@@ -177,3 +177,18 @@ def test_moe_options_validation():
     assert call(O(2, 1, 0, 1)) == bi.BI_EINVAL        # unknown activation
     assert call(O(1, 0, 2, 1)) == bi.BI_EINVAL        # flags are 0 or 1
     assert call(O(1, 0, 1, -1)) == bi.BI_EINVAL
+
+
+def test_direct_to_lds_decode_scope():
+    # chained bf16 recipes only, up to 64 rows, K a multiple of the phase
+    f = L.bi_lab_linear
+    def call(dtype, N, K, M, block_k=None):
+        r = bi.bi_describe_recipe(dtype, N, K)
+        if block_k:
+            r.block_k = block_k
+        return f(FAKE, K, FAKE, K, None, FAKE, bi.BI_F32, N, M, N, K, ctypes.byref(r), bi.BI_PATH_DECODE_DMA,
+                 None, 0, None)
+    assert call(bi.BI_F32, 256, 4096, 1, block_k=4096) == bi.BI_EUNSUPPORTED      # fp32
+    assert call(bi.BI_BF16, 1536, 2048, 1) == bi.BI_EUNSUPPORTED                  # 512-k tile partials
+    assert call(bi.BI_BF16, 4096, 4096, 65) == bi.BI_EUNSUPPORTED                 # more than 4 M tiles
+    assert call(bi.BI_BF16, 64, 480, 1, block_k=480) == bi.BI_EUNSUPPORTED        # K not a phase multiple

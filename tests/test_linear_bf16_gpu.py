@@ -120,3 +120,24 @@ def test_every_bf16_tile_shape_gives_the_same_bits(bi, K):
         banner(f"bf16 M=300 N=320 K={K} persistent tile code {code}")
         y = host(bi.bi_lab_linear(x, weight_t(wd), None, path=bi.BI_PATH_PERSISTENT | (code << 8)))
         assert_bitwise(y, ref, f"bf16 tile code {code}")
+
+
+@pytest.mark.parametrize("N,K", [(4096, 4096), (64, 512), (48, 1536)])
+def test_direct_to_lds_decode_matches_every_path(bi, N, K):
+    # the chained-recipe decode that streams W and X through LDS gives the
+    # bits of the register decode and of the persistent kernel, at every M it
+    # serves (1..64, ragged M tiles)
+    import torch
+    g = np.random.default_rng(N + K)
+    w = wl.normal_bf16(g, (N, K), 0.02)
+    wd = dev(w)
+    b = dev((g.standard_normal(N) * 0.01).astype(np.float32))
+    r = bi.bi_describe_recipe(bi.BI_BF16, N, K)
+    r.block_k = K                                   # fully chained
+    for M in (1, 3, 7, 8, 9, 16, 17, 32, 33, 48, 64):
+        banner(f"bf16 N={N} K={K} chained M={M} direct-to-LDS decode")
+        x = dev(wl.normal_bf16(g, (M, K), 1.0))
+        outs = [host(bi.bi_lab_linear(x, weight_t(wd), b, recipe=r, path=p, out_dtype=torch.float32))
+                for p in (bi.BI_PATH_DECODE_DMA, bi.BI_PATH_DECODE, bi.BI_PATH_PERSISTENT)]
+        assert_bitwise(outs[0], outs[1], f"dma vs register decode M={M}")
+        assert_bitwise(outs[0], outs[2], f"dma vs persistent M={M}")
