@@ -9,11 +9,16 @@ the next of 96 distinct copies of W (384 MiB in total, more than the 256 MB
 Infinity Cache), so HBM claims are not cache hits.  Inputs are synthetic
 (seeded normal draws, see workloads.py) and resident in HBM before timing.
 
-Timing: all launches of the timed region are queued behind a spin kernel, so
-the host's launch latency never shows; every launch is bracketed by HIP
-events on the stream it runs on.  `value` is whole-step throughput
-(algorithmic bytes of the step / step time); the roofline object reports the
-decode kernel's average launch duration against the 8 TB/s HBM peak.
+Timing: every timed call runs inside a HIP graph (torch.cuda.CUDAGraph),
+captured once after an eager pass, so neither the host's launch cost nor the
+device cost of per-call events (about 4.4 us for an event pair alone) enters
+the figures.  A step is one replay of a graph that holds the whole sweep;
+eight such graphs cycle through the W copies.  HIP events bracket only the K
+timed replays, queued behind a spin kernel on the same stream.  `value` is
+whole-step throughput (algorithmic bytes of the step / step time); the
+roofline object reports the decode call's average duration (step time / calls
+per step) against the 8 TB/s HBM peak.  Per-M, prefill, bf16, MoE and top-k
+figures are per-call averages over a replayed graph of many calls.
 The prefill leg (M = 1024, 4096) reports TFLOP/s against the fp32 MFMA peak.
 The CPU baseline times the fp64 oracle on the same decode sweep.
 
@@ -120,55 +125,51 @@ def main():
     bytes_step = sum(router_bytes(M) for M in sweep)
     calls_per_step = len(sweep)
 
-    state = {"i": 0}
+    stream = torch.cuda.Stream(dev)
+    n_graphs = 8
 
-    def one_call(M):
-        wd = copies[state["i"] % N_COPIES]
-        state["i"] += 1
-        bi.bi_linear_f32(xs[M], wd.t(), bias, out=outs[M])
+    def sweep_calls(j):
+        calls = []
+        for c, M in enumerate(sweep):
+            wd = copies[(j * calls_per_step + c) % N_COPIES]
+            calls.append(lambda M=M, wd=wd: bi.bi_linear_f32(xs[M], wd.t(), bias, out=outs[M]))
+        return calls
 
-    # warm-up (also allocates the workspace outside the timed region)
-    for _ in range(args.warmup):
-        for M in sweep:
-            one_call(M)
-    torch.cuda.synchronize()
+    graphs = [capture(torch, sweep_calls(j), stream) for j in range(n_graphs)]
 
     K = args.steps
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(K * calls_per_step)]
-    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    # the host needs ~30 us per call to enqueue; keep the GPU behind it
-    spin(torch, 5.0 + 0.05 * K * calls_per_step)
-    t0.record()
-    j = 0
-    for _ in range(K):
-        for M in sweep:
-            ev[j][0].record()
-            one_call(M)
-            ev[j][1].record()
-            j += 1
-    t1.record()
+    with torch.cuda.stream(stream):
+        for i in range(args.warmup):
+            graphs[i % n_graphs].replay()
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        spin(torch, 2.0)
+        t0.record()
+        for k in range(K):
+            graphs[k % n_graphs].replay()
+        t1.record()
     torch.cuda.synchronize()
     total_ms = t0.elapsed_time(t1)
-    per_call_us = np.array([a.elapsed_time(b) * 1e3 for a, b in ev]).reshape(K, calls_per_step)
     ms_per_step = total_ms / K
     value = bytes_step / (ms_per_step * 1e-3) / 1e9
+    del graphs
 
-    med_us = np.median(per_call_us, axis=0)
     per_m = {}
-    for i, M in enumerate(sweep):
-        t = med_us[i] * 1e-6
+    for M in sweep:
+        calls = [lambda M=M, wd=wd: bi.bi_linear_f32(xs[M], wd.t(), bias, out=outs[M]) for wd in copies]
+        us = time_graph_calls(torch, calls, stream)
+        t = us * 1e-6
         per_m[str(M)] = {
-            "us": round(float(med_us[i]), 3),
+            "us": round(us, 3),
             "GBps": round(router_bytes(M) / t / 1e9, 1),
             "TFLOPs": round(router_flops(M) / t / 1e12, 2),
             "hbm_frac": round(router_bytes(M) / t / 1e9 / HBM_PEAK_GBS, 4),
         }
-    mean_launch_us = float(np.mean(per_call_us))
-    achieved = bytes_step / calls_per_step / (mean_launch_us * 1e-6) / 1e9
+    achieved = bytes_step / (ms_per_step * 1e-3) / 1e9
 
     extra = {"decode_per_M": per_m, "weight": f"cold: {N_COPIES} rotating copies of W (384 MiB)",
-             "launch_timing": "HIP events around each launch, queued behind a spin kernel"}
+             "timing": "HIP graph replay; events bracket only the timed replays",
+             "event_pair_floor_us": round(event_pair_floor(torch, stream), 2)}
 
     if not args.no_prefill:
         extra["prefill"] = prefill_leg(torch, np, bi, wl, w, copies, bias, dev)
@@ -205,7 +206,7 @@ def main():
                      "traffic": (MEASURED_TRAFFIC["bytes_per_call"]
                                  if kernel_sources_digest() == MEASURED_TRAFFIC["sources_sha256"] else None),
                      "kernel": "decode call = k_decode (k-tile partials) + k_decode_fold, "
-                               "average over the sweep's launches"},
+                               "average over the sweep's calls (step time / calls per step)"},
         "cpu_baseline": cpu,
         "extra": extra,
     }
@@ -214,41 +215,70 @@ def main():
 
 def prefill_leg(torch, np, bi, wl, w, copies, bias, dev):
     res = {}
+    stream = torch.cuda.Stream(dev)
     for M in wl.ROUTER_PREFILL_M:
         x = torch.from_numpy(wl.router_batch(M, w).x).to(dev)
         out = torch.empty((M, 256), dtype=torch.float32, device=dev)
-        for i in range(3):
-            bi.bi_linear_f32(x, copies[i].t(), bias, out=out)
-        torch.cuda.synchronize()
-        n = 20
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
-        spin(torch, 2.0)
-        for i in range(n):
-            ev[i][0].record()
-            bi.bi_linear_f32(x, copies[i % len(copies)].t(), bias, out=out)
-            ev[i][1].record()
-        torch.cuda.synchronize()
-        us = float(np.median([a.elapsed_time(b) * 1e3 for a, b in ev]))
+        calls = [lambda wd=wd: bi.bi_linear_f32(x, wd.t(), bias, out=out) for wd in copies[:24]]
+        us = time_graph_calls(torch, calls, stream)
         tf = router_flops(M) / (us * 1e-6) / 1e12
         res[str(M)] = {"us": round(us, 2), "TFLOPs": round(tf, 2),
                        "mfma_frac": round(tf / FP32_MFMA_PEAK_TFLOPS, 4)}
     return res
 
 
-def time_calls(torch, np, fn, n, spin_ms=2.0):
-    """Median device time of fn() in microseconds: HIP events around each
-    call, all queued behind a spin kernel."""
-    for i in range(3):
-        fn(i)
+def capture(torch, calls, stream):
+    """One HIP graph of `calls`, captured on `stream` after an eager pass there
+    (which also sizes the library workspace outside the graph)."""
+    with torch.cuda.stream(stream):
+        for c in calls:
+            c()
     torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
-    spin(torch, spin_ms)
-    for i in range(n):
-        ev[i][0].record()
-        fn(i)
-        ev[i][1].record()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for c in calls:
+            c()
     torch.cuda.synchronize()
-    return float(np.median([a.elapsed_time(b) * 1e3 for a, b in ev]))
+    return g
+
+
+def time_graph_calls(torch, calls, stream, reps=3):
+    """Average device time of one call in microseconds: the calls are captured
+    into one graph, which is replayed `reps` times back to back behind a spin
+    kernel, with HIP events around the replays only."""
+    g = capture(torch, calls, stream)
+    with torch.cuda.stream(stream):
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        spin(torch, 1.0)
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+    torch.cuda.synchronize()
+    del g
+    return e0.elapsed_time(e1) * 1e3 / (reps * len(calls))
+
+
+def event_pair_floor(torch, stream, n=50):
+    """Device time between two HIP events recorded back to back (us)."""
+    import statistics
+    with torch.cuda.stream(stream):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        spin(torch, 1.0)
+        for a, b in ev:
+            a.record()
+            b.record()
+    torch.cuda.synchronize()
+    return statistics.median(a.elapsed_time(b) * 1e3 for a, b in ev)
+
+
+def time_calls(torch, np, fn, n):
+    """Average device time of fn(i) in microseconds over i = 0..n-1, from a
+    replayed graph of the n calls."""
+    stream = torch.cuda.Stream()
+    return time_graph_calls(torch, [lambda i=i: fn(i) for i in range(n)], stream)
 
 
 def dense_bf16_leg(torch, np, bi, wl, dev):

@@ -475,6 +475,32 @@ struct Stager {
     }
 };
 
+// Instruction order of one stage of the persistent kernel: the LDS reads of
+// k block kbl+1 are spread one by one between the MFMAs of block kbl (NR
+// reads and NM MFMAs per block), so each read has several MFMAs to land in.
+template <int NR, int NM, int KBS>
+__device__ __forceinline__ void interleave_stage()
+{
+    __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
+#pragma unroll
+    for (int kbl = 0; kbl < KBS; ++kbl) {
+        if (kbl + 1 < KBS) {
+            constexpr int pairs = NR < NM ? NR : NM;
+#pragma unroll
+            for (int i = 0; i < pairs; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+            if constexpr (NR > NM)
+                __builtin_amdgcn_sched_group_barrier(0x100, NR - NM, 0);
+            if constexpr (NM > NR)
+                __builtin_amdgcn_sched_group_barrier(0x008, NM - NR, 0);
+        } else {
+            __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);
+        }
+    }
+}
+
 // Tiles are taken in an order that gives each of the 8 XCDs (workgroup w
 // runs on XCD w % 8) a contiguous block of row-major tiles, so the N tiles
 // that share rows of X sit behind the same L2.
@@ -524,40 +550,59 @@ __global__ __launch_bounds__(WM * WN * 64) void k_persistent(LinearArgs a, int k
         // The k loop keeps two stages in flight in registers (two register
         // sets, alternating by stage parity) while a third feeds the MFMAs
         // from LDS: a stage is loaded two iterations before it is stored.
+        // Fragments of k block kbl+1 are read from LDS before the MFMAs of
+        // block kbl are issued, so their latency hides behind those MFMAs.
+        auto frags = [&](FragOf<OX> (&xf)[FM], FragOf<OW> (&wf)[FN], int buf, int kbl) {
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm)
+                SX::template frag<OX>(xf[fm], sx[buf], wm * FM * 16 + fm * 16 + r, kbl, g);
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn)
+                SW::template frag<OW>(wf[fn], sw[buf], wn * FN * 16 + fn * 16 + r, kbl, g);
+        };
+        // A stage never straddles a k tile (block_k is a whole number of
+        // stages), so the partial is cleared and folded only between stages
+        // and the unrolled k blocks of a stage form one straight-line block.
         auto compute = [&](int buf, int st) {
-#pragma unroll
-            for (int kbl = 0; kbl < KBS; ++kbl) {
-                if constexpr (CHAINED) {
-                    FragOf<OX> xf[FM];
-                    FragOf<OW> wf[FN];
-#pragma unroll
-                    for (int fm = 0; fm < FM; ++fm)
-                        SX::template frag<OX>(xf[fm], sx[buf], wm * FM * 16 + fm * 16 + r, kbl, g);
-#pragma unroll
-                    for (int fn = 0; fn < FN; ++fn)
-                        SW::template frag<OW>(wf[fn], sw[buf], wn * FN * 16 + fn * 16 + r, kbl, g);
-                    mfma_tiles<FM, FN>(xf, wf, acc);
-                    continue;
-                }
-                const int kb = st * KBS + kbl;
-                if (kb % kbpt == 0) {
+            // a second fragment set only where the registers allow it (the
+            // largest tiles would spill)
+            constexpr int kFragRegs = (FM + FN) * (OX::f32_frag ? 8 : 4);
+            constexpr bool kPrefetch = FM * FN * 4 * (CHAINED ? 1 : 2) + 2 * kFragRegs <= 160;
+            constexpr int kSets = kPrefetch ? 2 : 1;
+            FragOf<OX> xf[kSets][FM];
+            FragOf<OW> wf[kSets][FN];
+            if constexpr (kPrefetch)
+                frags(xf[0], wf[0], buf, 0);
+            if constexpr (!CHAINED) {
+                if ((st * KBS) % kbpt == 0) {
 #pragma unroll
                     for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
                         for (int fn = 0; fn < FN; ++fn)
                             part[fm][fn] = f32x4{0.f, 0.f, 0.f, 0.f};
                 }
-                FragOf<OX> xf[FM];
-                FragOf<OW> wf[FN];
+            }
 #pragma unroll
-                for (int fm = 0; fm < FM; ++fm)
-                    SX::template frag<OX>(xf[fm], sx[buf], wm * FM * 16 + fm * 16 + r, kbl, g);
-#pragma unroll
-                for (int fn = 0; fn < FN; ++fn)
-                    SW::template frag<OW>(wf[fn], sw[buf], wn * FN * 16 + fn * 16 + r, kbl, g);
-                mfma_tiles<FM, FN>(xf, wf, part);
-                if (kb % kbpt == kbpt - 1) {
-                    const bool first = kb < kbpt;
+            for (int kbl = 0; kbl < KBS; ++kbl) {
+                const int cur = kPrefetch ? (kbl & 1) : 0;
+                if constexpr (kPrefetch) {
+                    if (kbl + 1 < KBS)
+                        frags(xf[(kbl + 1) & 1], wf[(kbl + 1) & 1], buf, kbl + 1);
+                } else {
+                    frags(xf[0], wf[0], buf, kbl);
+                }
+                if constexpr (CHAINED)
+                    mfma_tiles<FM, FN>(xf[cur], wf[cur], acc);
+                else
+                    mfma_tiles<FM, FN>(xf[cur], wf[cur], part);
+            }
+            if constexpr (kPrefetch)
+                interleave_stage<(FM + FN) * (OX::f32_frag && !OX::widen ? 2 : 1),
+                                 FM * FN * (OX::f32_frag ? 8 : 1), KBS>();
+            if constexpr (!CHAINED) {
+                const int kb_end = (st + 1) * KBS;
+                if (kb_end % kbpt == 0) {
+                    const bool first = kb_end == kbpt;
 #pragma unroll
                     for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
@@ -790,6 +835,9 @@ static hipError_t launch_persistent_t(const LinearArgs& a, const Plan& p, hipStr
     const int tiles_n = (a.N + BN - 1) / BN;
     const int tiles = tiles_m * tiles_n;
     const int grid = min(tiles, device_cu_count() * 2);
+    // a k tile must hold whole stages (the kernel folds between stages)
+    if (p.tiles_k != 1 && p.kbpt % KBS != 0)
+        return hipErrorInvalidValue;
     if (p.tiles_k == 1) {
         k_persistent<OX, OW, BM, BN, WM, WN, KBS, PDC, true><<<grid, WM * WN * 64, 0, s>>>(a, p.kbpt, tiles_m, tiles_n);
     } else {
@@ -813,17 +861,22 @@ static hipError_t launch_persistent(const LinearArgs& a, const Plan& p, hipStrea
     const int cus = device_cu_count();
     auto tiles = [&](int bm, int bn) { return ((a.M + bm - 1) / bm) * ((a.N + bn - 1) / bn); };
     int code = p.tile_code;
-    // stage width of each shape, in k: shapes whose stage does not divide K
-    // fall back to the 32-k-stage shape of the same dtype
+    // stage width of each shape, in k: shapes whose stage does not fit fall
+    // back to the 32-k-stage shape of the same dtype
     auto stage_k = [](int c) {
         return (c == 7 || c == 8 || c == 17) ? 32 : (c == 9 || c == 10 || c == 13 || c == 16) ? 128 : 64;
+    };
+    // a stage must divide K and, with several k tiles, the k tile too
+    auto stage_fits = [&](int c) {
+        const int kbs = stage_k(c) / kKBlock;
+        return a.K % stage_k(c) == 0 && (p.tiles_k == 1 || p.kbpt % kbs == 0);
     };
     if constexpr (OX::f32_frag) {
         // measured on MI355X for the (fp32, 256, 4096) router: 64x64 on 8
         // waves at M=4096 (99 us), 32x32 at M=1024 and 2048 (48 / 68 us)
         if (code == 0)
             code = tiles(64, 64) >= cus ? 4 : 3;
-        if (a.K % stage_k(code) != 0)
+        if (!stage_fits(code))
             code = 7;
         switch (code) {
         case 1: return launch_persistent_t<OX, OW, 64, 64, 2, 2, 2>(a, p, s);
@@ -846,7 +899,7 @@ static hipError_t launch_persistent(const LinearArgs& a, const Plan& p, hipStrea
             else
                 code = tiles(128, 256) >= cus ? 15 : 12;
         }
-        if (a.K % stage_k(code) != 0)
+        if (!stage_fits(code))
             code = 17;
         // 256x256 tiles only fit the registers without tile partials
         if ((code == 18 || code == 19) && p.tiles_k != 1)

@@ -17,11 +17,13 @@ with cold weights (rotating copies, beyond the Infinity Cache):
 
   * every decode form that serves the candidate (two launches with a
     workspace fold, one launch with an LDS fold, direct-to-LDS streaming for
-    a chained bf16 recipe) at M in DECODE_M;
+    a chained bf16 recipe) at M in DECODE_M and at the prefill sizes up to
+    DECODE_PROBE_MAX (the decode limit may lie beyond the decode sizes);
   * every persistent tile shape at M in PREFILL_M and at the decode sizes
     where the persistent kernel might take over;
 
-checks that every path and tile shape of the candidate gives the same bits
+Times are per-call averages over a replayed HIP graph of the calls.  The
+sweeper then checks that every path and tile shape of the candidate gives the same bits
 (they carry out one recipe) and that a row computed alone equals the same
 row inside the batch, then picks the entry for the profile:
 
@@ -50,6 +52,7 @@ TABLE = os.path.join(PKG, "csrc", "bi_table.inc")
 
 DECODE_M = (1, 8, 16, 32, 64, 128)
 PREFILL_M = (256, 1024, 4096)
+DECODE_PROBE_MAX = 1024     # decode forms are also timed at the prefill sizes up to this M
 TABLE_HEADER = ("// Measured key table, written by deterministic_persistent_gemm_amd/sweep.py.\n"
                 "// {dtype, N, K, block_k, m_decode_max, decode_path, m_a, tile_a, m_b, tile_b, tile_c}\n")
 F32_CODES = tuple(range(1, 11))
@@ -215,24 +218,33 @@ def parse_table(text: str):
 # ------------------------------------------------------------------ measuring
 
 def _timeit(torch, fns, reps=3):
-    """Median device time (us) of one call, rotating over fns (cold weights)."""
-    import numpy as np
-    for f in fns[:3]:
-        f()
-    torch.cuda.synchronize()
-    ts = []
-    for _ in range(reps):
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in fns]
-        # the queue is held behind a spin long enough for the host to enqueue
-        # every call, so no call waits on the host
-        torch.cuda._sleep(2_000_000 + 40_000 * len(fns))
-        for (a, b), f in zip(ev, fns):
-            a.record()
+    """Average device time (us) of one call, rotating over fns (cold weights).
+
+    The calls are captured into one HIP graph on a side stream (after an
+    eager pass there, which also sizes the workspace) and the graph is
+    replayed back to back, so neither host launch cost nor per-call events
+    enter the figure."""
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        for f in fns:
             f()
-            b.record()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for f in fns:
+            f()
+    with torch.cuda.stream(stream):
+        g.replay()
         torch.cuda.synchronize()
-        ts += [a.elapsed_time(b) * 1e3 for a, b in ev]
-    return float(np.median(ts))
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(1_000_000)
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+    torch.cuda.synchronize()
+    del g
+    return e0.elapsed_time(e1) * 1e3 / (reps * len(fns))
 
 
 def sweep_key(dt: str, N: int, K: int, profile: str, tie: float = 0.03, log=print):
@@ -273,7 +285,7 @@ def sweep_key(dt: str, N: int, K: int, profile: str, tie: float = 0.03, log=prin
                     cand["bits_ok"] = False
                     log(f"  BITS DIFFER: {dt}:{N}:{K} block_k={bk} M={M} {tag}")
 
-            if M in DECODE_M:
+            if M in DECODE_M or M <= DECODE_PROBE_MAX:
                 cand["decode"][M] = {}
                 for path in (PATH_DECODE, PATH_DECODE_WG, PATH_DECODE_DMA):
                     try:
@@ -335,8 +347,9 @@ def main(argv=None):
     ap.add_argument("--from-json", action="append", default=[],
                     help="re-derive the entry of a saved report instead of measuring")
     ap.add_argument("--profile", choices=("decode", "prefill", "balanced"), default="decode")
-    ap.add_argument("--tie", type=float, default=0.03,
-                    help="relative objective difference treated as a tie (the served recipe is kept)")
+    ap.add_argument("--tie", type=float, default=None,
+                    help="relative objective difference treated as a tie (the served recipe is kept); "
+                         "default 0.03 when sweeping, the report's own with --from-json")
     ap.add_argument("--out", default=None, help="directory for the JSON reports")
     ap.add_argument("--write-table", action="store_true", help="merge the entries into csrc/bi_table.inc")
     args = ap.parse_args(argv)
@@ -345,12 +358,13 @@ def main(argv=None):
     for path in args.from_json:
         rep = json.load(open(path))
         dt, N, K = parse_key(rep["key"])[:3]
-        e = entry_from_report(rep)
+        e = entry_from_report(rep, tie=args.tie)
         lines[f"{'BI_F32' if dt == 'f32' else 'BI_BF16'},{N},{K}"] = table_line(dt, N, K, e)
         print(f"{rep['key']} ({rep['profile']}): {table_line(dt, N, K, e)}", flush=True)
     for dt, N, K, prof in keys:
         print(f"sweeping {dt}:{N}:{K} ({prof})", flush=True)
-        rep = sweep_key(dt, N, K, prof, tie=args.tie, log=lambda s: print(s, flush=True))
+        rep = sweep_key(dt, N, K, prof, tie=0.03 if args.tie is None else args.tie,
+                        log=lambda s: print(s, flush=True))
         print(f"  entry: {rep['table_line']}", flush=True)
         if args.out:
             os.makedirs(args.out, exist_ok=True)
