@@ -53,10 +53,11 @@ TABLE = os.path.join(PKG, "csrc", "bi_table.inc")
 DECODE_M = (1, 8, 16, 32, 64, 128)
 PREFILL_M = (256, 1024, 4096)
 DECODE_PROBE_MAX = 1024     # decode forms are also timed at the prefill sizes up to this M
+DECODE_MARGIN = 0.05        # the persistent kernel takes over once it is this much faster
 TABLE_HEADER = ("// Measured key table, written by deterministic_persistent_gemm_amd/sweep.py.\n"
                 "// {dtype, N, K, block_k, m_decode_max, decode_path, m_a, tile_a, m_b, tile_b, tile_c}\n")
 F32_CODES = tuple(range(1, 11))
-BF16_CODES = tuple(range(11, 20))
+BF16_CODES = tuple(range(11, 21))
 PATH_DECODE, PATH_PERSISTENT, PATH_DECODE_WG, PATH_DECODE_DMA = 1, 2, 3, 4
 
 
@@ -74,7 +75,7 @@ def parse_key(s: str, profile: str = "decode"):
 def stage_k(code: int) -> int:
     """k per LDS stage of a persistent tile shape (shapes whose stage does
     not divide K are served by the 32-k-stage shape of the dtype)."""
-    return 32 if code in (7, 8, 17) else 128 if code in (9, 10, 13, 16) else 64
+    return 32 if code in (7, 8, 17) else 128 if code in (9, 10, 13, 16) else 64   # 20: 64
 
 
 def tile_codes(dt: str, K: int, block_k: int):
@@ -101,10 +102,12 @@ def summarize(cand: dict) -> dict:
     best_dec_path = {M: min(v, key=v.get) for M, v in cand["decode"].items() if v}
     best_per = {M: min(v.values()) for M, v in cand["persistent"].items() if v}
     best_code = {M: min(v, key=v.get) for M, v in cand["persistent"].items() if v}
-    # decode serves M up to the last grid point before the persistent kernel wins
+    # decode serves M up to the last grid point before the persistent kernel
+    # wins by more than DECODE_MARGIN (near the crossing the two are within
+    # noise, and the grid is coarse: the decode form is kept there)
     m_dec = 0
     for M in sorted(best_dec):
-        if M in best_per and best_per[M] < best_dec[M]:
+        if M in best_per and best_per[M] < best_dec[M] * (1.0 - DECODE_MARGIN):
             break
         m_dec = M
     dec_ms = [M for M in sorted(best_dec) if M <= m_dec]

@@ -116,7 +116,7 @@ def test_every_bf16_tile_shape_gives_the_same_bits(bi, K):
     x = dev(wl.normal_bf16(g, (300, K), 1.0))
     wd = dev(w)
     ref = host(bi.bi_linear_bf16(x, weight_t(wd), None))
-    for code in range(11, 20):
+    for code in range(11, 21):
         banner(f"bf16 M=300 N=320 K={K} persistent tile code {code}")
         y = host(bi.bi_lab_linear(x, weight_t(wd), None, path=bi.BI_PATH_PERSISTENT | (code << 8)))
         assert_bitwise(y, ref, f"bf16 tile code {code}")
@@ -141,3 +141,32 @@ def test_direct_to_lds_decode_matches_every_path(bi, N, K):
                 for p in (bi.BI_PATH_DECODE_DMA, bi.BI_PATH_DECODE, bi.BI_PATH_PERSISTENT)]
         assert_bitwise(outs[0], outs[1], f"dma vs register decode M={M}")
         assert_bitwise(outs[0], outs[2], f"dma vs persistent M={M}")
+
+
+@pytest.mark.parametrize("M,N,K,chained", [(1, 64, 64, True), (65, 80, 128, True), (256, 4096, 4096, True),
+                                           (300, 320, 1024, False), (1000, 48, 2048, True),
+                                           (777, 1536, 2048, False)])
+def test_stream_ring_tiles(bi, M, N, K, chained):
+    # the 64x64 shape fed by a deep direct-to-LDS ring (tile code 20) gives
+    # the bits of the register-staged 64x64 shape (code 12): one to many
+    # stages, ragged M and N edges, chained and tile-partial recipes, bias,
+    # bf16 and fp32 output
+    import torch
+    g = np.random.default_rng(M * 7 + N + K)
+    w = wl.normal_bf16(g, (N, K), 0.02)
+    wd = dev(w)
+    x = dev(wl.normal_bf16(g, (M, K), 1.0))
+    b = dev((g.standard_normal(N) * 0.01).astype(np.float32))
+    r = bi.bi_describe_recipe(bi.BI_BF16, N, K)
+    r.block_k = K if chained else 512
+    for odt in (torch.bfloat16, torch.float32):
+        banner(f"bf16 M={M} N={N} K={K} block_k={r.block_k} tile code 20 vs 12 out={odt}")
+        y20 = host(bi.bi_lab_linear(x, weight_t(wd), b, recipe=r, path=bi.BI_PATH_PERSISTENT | (20 << 8),
+                                    out_dtype=odt))
+        y12 = host(bi.bi_lab_linear(x, weight_t(wd), b, recipe=r, path=bi.BI_PATH_PERSISTENT | (12 << 8),
+                                    out_dtype=odt))
+        assert_bitwise(y20, y12, f"code 20 vs 12 M={M} N={N} K={K}")
+    if M * N * K <= 64 * 1024 * 1024:
+        y = host(bi.bi_lab_linear(x, weight_t(wd), b, recipe=r, path=bi.BI_PATH_PERSISTENT | (20 << 8),
+                                  out_dtype=torch.float32))
+        assert_close(y, oracle.linear_bf16(host(x), w, host(b), out="f32"), 1e-5, 1e-4, "code 20 vs oracle")
