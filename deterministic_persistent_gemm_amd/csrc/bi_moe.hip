@@ -567,15 +567,17 @@ static hipError_t launch_grouped_tw(const GroupedArgs& g, int64_t max_units, hip
 {
     const int ntiles = (g.n_out / 16 + NW - 1) / NW;
     dim3 grid((unsigned)ntiles, (unsigned)max_units);
-    // register budget: two buffers of CH k blocks of MT activation and NB
-    // weight fragments
+    // two buffers of CH k blocks of MT activation and NB weight fragments.
+    // Short chunks keep the registers per wave low, and more waves per SIMD
+    // keep more weight bytes in flight than long chunks do (measured on
+    // MI355X, Qwen3-30B-A3B-shaped layer: CH 4 for 16-row units, 2 for 32-row
+    // units gave M=16 153.7 us (was 162.6 with CH 8), M=64 230.4 (253.7) and
+    // M=256 305.9 (366.7 with CH 4 / 8))
     int ch = pick_ch(g.kbpt);
-    if (ch > 8)
-        ch = 8;
-    if (MT * (ACT == kActSwiGLU ? 2 : 1) > 2 && ch > 4)
-        ch = 4;
+    const int ch_max = MT == 1 ? 4 : 2;
+    if (ch > ch_max)
+        ch = ch_max;
     switch (ch) {
-    case 8:  k_grouped<TW, NW, MT, ACT, 8><<<grid, TW * NW * 64, 0, s>>>(g); break;
     case 4:  k_grouped<TW, NW, MT, ACT, 4><<<grid, TW * NW * 64, 0, s>>>(g); break;
     case 2:  k_grouped<TW, NW, MT, ACT, 2><<<grid, TW * NW * 64, 0, s>>>(g); break;
     default: k_grouped<TW, NW, MT, ACT, 1><<<grid, TW * NW * 64, 0, s>>>(g); break;
