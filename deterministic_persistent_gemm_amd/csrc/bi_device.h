@@ -145,6 +145,22 @@ __device__ __forceinline__ void mfma_tiles(const Frag<false> (&xf)[FM], const Fr
             part[fm][fn] = mfma_block(xf[fm], wf[fn], part[fm][fn]);
 }
 
+// Inclusive prefix sum over the wave's lanes: a Hillis-Steele scan inside
+// each row of 16 lanes with DPP row shifts (lanes whose source falls outside
+// the row add 0), then the totals of the rows below are added.
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v, int lane)
+{
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, false);   // row_shr:1
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, false);   // row_shr:2
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, false);   // row_shr:4
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, false);   // row_shr:8
+    const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)v, 15);
+    const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)v, 31);
+    const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)v, 47);
+    const int row = lane >> 4;
+    return v + (row >= 1 ? r0 : 0u) + (row >= 2 ? r1 : 0u) + (row >= 3 ? r2 : 0u);
+}
+
 // fp32 -> bf16, round to nearest even; NaN stays a quiet NaN.
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f)
 {

@@ -169,6 +169,66 @@ __global__ __launch_bounds__(1024) void k_dispatch(const int32_t* __restrict__ i
     dispatch_body(ids, M, E, topk, unit_rows, offsets, sorted, unit_expert, unit_row, nunits);
 }
 
+// The same dispatch done by one wave, for the routing kernel when it serves
+// every token (M <= kRouteTokens, so a token set fits a 16-bit mask): the
+// per-expert counts and token masks by LDS atomics, the prefix sums of the
+// counts and of the unit counts by a wave scan over contiguous runs of
+// experts per lane, then the stable placement by popcount.  No barriers.
+
+__device__ __forceinline__ void dispatch_wave(const int32_t* sids, int M, int E, int topk, int unit_rows, int lane,
+                                              int32_t* __restrict__ offsets, int32_t* __restrict__ sorted,
+                                              int32_t* __restrict__ unit_expert, int32_t* __restrict__ unit_row,
+                                              int32_t* __restrict__ nunits)
+{
+    __shared__ int cnt[kMaxExperts];
+    __shared__ uint32_t tmask[kMaxExperts];
+    const int P = M * topk;
+    for (int e = lane; e < E; e += 64) {
+        cnt[e] = 0;
+        tmask[e] = 0u;
+    }
+    __builtin_amdgcn_wave_barrier();
+    for (int p = lane; p < P; p += 64) {
+        const int e = sids[p];
+        atomicAdd(&cnt[e], 1);
+        atomicOr(&tmask[e], 1u << (p / topk));
+    }
+    __builtin_amdgcn_wave_barrier();
+    // lane l owns experts l*per .. l*per + per - 1
+    const int per = (E + 63) / 64;
+    const int e0 = min(lane * per, E), e1 = min(e0 + per, E);
+    uint32_t c_run = 0, u_run = 0;
+    for (int e = e0; e < e1; ++e) {
+        const int c = cnt[e];
+        c_run += (uint32_t)c;
+        u_run += (uint32_t)((c + unit_rows - 1) / unit_rows);
+    }
+    const uint32_t c_incl = wave_incl_scan(c_run, lane), u_incl = wave_incl_scan(u_run, lane);
+    int start = (int)(c_incl - c_run), ustart = (int)(u_incl - u_run);
+    for (int e = e0; e < e1; ++e) {
+        const int c = cnt[e];
+        offsets[e] = start;
+        const int nu = (c + unit_rows - 1) / unit_rows;
+        for (int u = 0; u < nu; ++u) {
+            unit_expert[ustart + u] = e;
+            unit_row[ustart + u] = start + u * unit_rows;
+        }
+        cnt[e] = start;                  // from here on: the expert's first position
+        start += c;
+        ustart += nu;
+    }
+    if (lane == 63) {
+        offsets[E] = P;
+        nunits[0] = (int)u_incl;
+    }
+    __builtin_amdgcn_wave_barrier();
+    for (int p = lane; p < P; p += 64) {
+        const int e = sids[p];
+        const uint32_t below = (1u << (p / topk)) - 1u;
+        sorted[cnt[e] + __popc(tmask[e] & below)] = p;
+    }
+}
+
 // ------------------------------------------------------------------- routing
 
 constexpr int kRouteTokens = 16;   // tokens per routing workgroup, one wave each
@@ -225,6 +285,27 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v)
     return best;
 }
 
+// Butterfly over the wave with the partner order xor 1, 2, 4, 8, 16, 32
+// (at step k lane i combines its value with lane i ^ k's): DPP inside each
+// row of 16 lanes, lane reads across the four rows.  The half-row and row
+// mirrors pair a lane with another lane of the xor partner's group, whose
+// value is the same by then, and a + b == b + a exactly, so every lane ends
+// with the bits of the shuffle butterfly: ((r0 + r1) + (r2 + r3)) over the
+// row values r.
+template <typename Op>
+__device__ __forceinline__ float wave_butterfly(float v, Op op)
+{
+    v = op(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false)));   // xor 1
+    v = op(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false)));   // xor 2
+    v = op(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, false)));  // ~xor 4
+    v = op(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, false)));  // ~xor 8
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+    return op(op(r0, r1), op(r2, r3));
+}
+
 // Softmax and top-k of one token (one wave): see k_route.
 template <int kPer, bool FUSE>
 __device__ __forceinline__ void route_token(const float* l, int lane, int m, int E, int topk,
@@ -238,8 +319,7 @@ __device__ __forceinline__ void route_token(const float* l, int lane, int m, int
         v[i] = e < E ? l[e] : -INFINITY;
         mx = fmaxf(mx, v[i]);
     }
-    for (int off = 32; off >= 1; off >>= 1)
-        mx = fmaxf(mx, __shfl_xor(mx, off));
+    mx = wave_butterfly(mx, [](float a, float b) { return fmaxf(a, b); });
     float ex[kPer];
     float sum = 0.f;
 #pragma unroll
@@ -248,8 +328,7 @@ __device__ __forceinline__ void route_token(const float* l, int lane, int m, int
         ex[i] = e < E ? expf(v[i] - mx) : 0.f;
         sum = sum + ex[i];
     }
-    for (int off = 1; off <= 32; off <<= 1)
-        sum = sum + __shfl_xor(sum, off);
+    sum = wave_butterfly(sum, [](float a, float b) { return a + b; });
 
     // Top-k by repeated arg-max over unique 64-bit keys: high word the
     // logit's order key (NaN as -inf, -0.0 as +0.0), low word ~e, so the
@@ -289,7 +368,8 @@ __device__ __forceinline__ void route_token(const float* l, int lane, int m, int
 //     ascending expert order, -0.0 equal to +0.0 (repeated wave arg-max
 //     over unique keys).
 //  4. FUSE (a single workgroup, M <= 16): the dispatch of the next step runs
-//     in the same workgroup on the ids just chosen, saving a launch.
+//     in the same workgroup on the ids just chosen (one wave, no barriers),
+//     saving a launch.
 template <int kPer, bool FUSE>   // experts per lane: E <= 64 * kPer
 __global__ __launch_bounds__(kRouteTokens * 64) void k_route(const float* __restrict__ logits,
                                                              const f32x4* __restrict__ partials,
@@ -345,7 +425,9 @@ __global__ __launch_bounds__(kRouteTokens * 64) void k_route(const float* __rest
         route_token<kPer, FUSE>(lg[wave], lane, m, E, topk, ids, probs, sids + wave * topk);
     if constexpr (FUSE) {
         __syncthreads();
-        dispatch_body(sids, M, E, topk, d.unit_rows, d.offsets, d.sorted, d.unit_expert, d.unit_row, d.nunits);
+        if (wave == 0)
+            dispatch_wave(sids, M, E, topk, d.unit_rows, lane, d.offsets, d.sorted, d.unit_expert, d.unit_row,
+                          d.nunits);
     }
 }
 

@@ -34,6 +34,7 @@
 // page's fast path is gated to).
 #include <hip/hip_runtime.h>
 
+#include "bi_device.h"
 #include "bi_topk.h"
 
 namespace bi {
@@ -58,21 +59,6 @@ __device__ __forceinline__ uint32_t rank_bits(float v)
     return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
-// Inclusive prefix sum over the wave's lanes: a Hillis-Steele scan inside
-// each row of 16 lanes with DPP row shifts (lanes whose source falls outside
-// the row add 0), then the totals of the rows below are added.
-__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v, int lane)
-{
-    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, false);   // row_shr:1
-    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, false);   // row_shr:2
-    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, false);   // row_shr:4
-    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, false);   // row_shr:8
-    const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)v, 15);
-    const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)v, 31);
-    const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)v, 47);
-    const int row = lane >> 4;
-    return v + (row >= 1 ? r0 : 0u) + (row >= 2 ? r1 : 0u) + (row >= 3 ? r2 : 0u);
-}
 
 // Inclusive prefix sum over the workgroup's threads in thread order.
 __device__ __forceinline__ uint32_t block_incl_scan(uint32_t v, uint32_t* wsum, int lane, int wave)
