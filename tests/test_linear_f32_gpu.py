@@ -329,3 +329,24 @@ def test_bf16_roundtrip_control_fails_tolerance(bi, router):
     ratio = np.max(np.abs(y - ref) / (F32_ATOL + F32_RTOL * np.abs(ref)))
     print(f"bf16 round-trip error / fp32 tolerance = {ratio:.1f}x")
     assert ratio > 1.0
+
+
+@pytest.mark.parametrize("K,block_k", [(4096, 64), (4096, 128), (4096, 256), (4096, 1024), (3072, 1024), (384, 128)])
+def test_tile_partial_widths_agree_across_shapes(bi, K, block_k):
+    # for several tile-partial widths (an odd number of k tiles, 3072 / 1024,
+    # and a short K included) the 32x32 and 64x64 persistent shapes and the
+    # decode path give the same bits
+    g = np.random.default_rng(K + block_k)
+    N, M = 96, 200
+    w = g.standard_normal((N, K)).astype(np.float32) * 0.02
+    b = (g.standard_normal(N) * 0.01).astype(np.float32)
+    x = dev(g.standard_normal((M, K)).astype(np.float32))
+    wd, bd = dev(w), dev(b)
+    r = bi.bi_describe_recipe(bi.BI_F32, N, K)
+    r.block_k = block_k
+    banner(f"fp32 M={M} N={N} K={K} block_k={block_k} tile 3 vs 1")
+    y3 = host(bi.bi_lab_linear(x, weight_t(wd), bd, recipe=r, path=bi.BI_PATH_PERSISTENT | (3 << 8)))
+    y1 = host(bi.bi_lab_linear(x, weight_t(wd), bd, recipe=r, path=bi.BI_PATH_PERSISTENT | (1 << 8)))
+    assert_bitwise(y3, y1, f"32x32 vs 64x64 K={K} block_k={block_k}")
+    yd = host(bi.bi_lab_linear(x, weight_t(wd), bd, recipe=r, path=bi.BI_PATH_DECODE))
+    assert_bitwise(y3, yd, f"32x32 vs decode K={K} block_k={block_k}")
