@@ -501,20 +501,54 @@ __device__ __forceinline__ void interleave_stage()
     }
 }
 
-// Tiles are taken in an order that gives each of the 8 XCDs (workgroup w
-// runs on XCD w % 8) a contiguous block of row-major tiles, so the N tiles
-// that share rows of X sit behind the same L2.
-__device__ __forceinline__ int xcd_tile(int it, int tiles, int grid)
+// Workgroup w runs on XCD w % 8, and with a grid that is a multiple of 8 so
+// does every tile index it = w + r * grid it walks.  XCD x = it % 8 therefore
+// owns the tiles it, it + 8, ...; they are mapped onto one xbm x xbn block of
+// the tile grid (row-major inside the block), so the tiles that share rows
+// of X or of W sit behind the same L2.  xbm == 0 keeps the row-major order.
+__device__ __forceinline__ int xcd_tile(int it, int tiles_n, int xbm, int xbn)
 {
-    if (grid != tiles || (tiles & 7) != 0)
+    if (xbm == 0)
         return it;
-    return (it & 7) * (tiles >> 3) + (it >> 3);
+    const int x = it & 7, j = it >> 3;
+    const int bx = tiles_n / xbn;
+    const int m = (x / bx) * xbm + j / xbn;
+    const int n = (x % bx) * xbn + j % xbn;
+    return m * tiles_n + n;
+}
+
+// The block shape of xcd_tile: of the xbm x xbn blocks that split the
+// tiles_m x tiles_n grid into eight, the one whose L2 fetches the fewest
+// operand rows (xbm * BM rows of X, xbn * BN rows of W); {0, 0} when the
+// grid or the tile count is not a multiple of 8.
+struct XcdBlock {
+    int xbm, xbn;
+};
+
+static XcdBlock xcd_block(int tiles_m, int tiles_n, int BM, int BN, int grid)
+{
+    const int tiles = tiles_m * tiles_n;
+    XcdBlock best{0, 0};
+    if (grid % 8 != 0 || tiles % 8 != 0)
+        return best;
+    const int per = tiles / 8;
+    long best_rows = 0;
+    for (int bm = 1; bm <= tiles_m; ++bm) {
+        if (tiles_m % bm != 0 || per % bm != 0 || tiles_n % (per / bm) != 0)
+            continue;
+        const long rows = (long)bm * BM + (long)(per / bm) * BN;
+        if (best.xbm == 0 || rows < best_rows) {
+            best = {bm, per / bm};
+            best_rows = rows;
+        }
+    }
+    return best;
 }
 
 // CHAINED: the recipe has a single k tile (block_k == K), so the chain runs
 // straight into the accumulator and no partial registers are needed.
 template <typename OX, typename OW, int BM, int BN, int WM, int WN, int KBS, int PD, bool CHAINED>
-__global__ __launch_bounds__(WM * WN * 64) void k_persistent(LinearArgs a, int kbpt, int tiles_m, int tiles_n)
+__global__ __launch_bounds__(WM * WN * 64) void k_persistent(LinearArgs a, int kbpt, int tiles_m, int tiles_n, int xbm, int xbn)
 {
     using EX = typename OX::elem;
     using EW = typename OW::elem;
@@ -535,7 +569,7 @@ __global__ __launch_bounds__(WM * WN * 64) void k_persistent(LinearArgs a, int k
     const EW* wg = reinterpret_cast<const EW*>(a.w);
 
     for (int it = blockIdx.x; it < tiles; it += gridDim.x) {
-        const int tile = xcd_tile(it, tiles, gridDim.x);
+        const int tile = xcd_tile(it, tiles_n, xbm, xbn);
         const int tm = tile / tiles_n, tn = tile % tiles_n;
         const int m0 = tm * BM, n0 = tn * BN;
         f32x4 acc[FM][FN], part[FM][FN];
@@ -716,7 +750,7 @@ constexpr int kStreamHalf = kStreamTile * kStreamRowBytes;               // 8 Ki
 constexpr int kStreamStage = 2 * kStreamHalf;                            // 16 KiB
 
 template <bool CHAINED>
-__global__ __launch_bounds__(256) void k_stream_bf16(LinearArgs a, int kbpt, int tiles_m, int tiles_n)
+__global__ __launch_bounds__(256) void k_stream_bf16(LinearArgs a, int kbpt, int tiles_m, int tiles_n, int xbm, int xbn)
 {
     __shared__ __attribute__((aligned(16))) unsigned char ring[kStreamRing * kStreamStage];
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -729,7 +763,7 @@ __global__ __launch_bounds__(256) void k_stream_bf16(LinearArgs a, int kbpt, int
     const uint32_t lds0 = lds_addr(ring);
 
     for (int it = blockIdx.x; it < tiles; it += gridDim.x) {
-        const int tile = xcd_tile(it, tiles, gridDim.x);
+        const int tile = xcd_tile(it, tiles_n, xbm, xbn);
         const int m0 = (tile / tiles_n) * kStreamTile, n0 = (tile % tiles_n) * kStreamTile;
         // wave w loads rows 16 w .. 16 w + 15 of the X and W tiles, 8 per load;
         // rows past M (N) read row M-1 (N-1), whose results are never stored
@@ -855,10 +889,11 @@ static hipError_t launch_stream_bf16(const LinearArgs& a, const Plan& p, hipStre
     const int tiles_m = (a.M + kStreamTile - 1) / kStreamTile;
     const int tiles_n = (a.N + kStreamTile - 1) / kStreamTile;
     const int grid = min(tiles_m * tiles_n, device_cu_count());
+    const XcdBlock xb = xcd_block(tiles_m, tiles_n, kStreamTile, kStreamTile, grid);
     if (p.tiles_k == 1)
-        k_stream_bf16<true><<<grid, 256, 0, s>>>(a, p.kbpt, tiles_m, tiles_n);
+        k_stream_bf16<true><<<grid, 256, 0, s>>>(a, p.kbpt, tiles_m, tiles_n, xb.xbm, xb.xbn);
     else
-        k_stream_bf16<false><<<grid, 256, 0, s>>>(a, p.kbpt, tiles_m, tiles_n);
+        k_stream_bf16<false><<<grid, 256, 0, s>>>(a, p.kbpt, tiles_m, tiles_n, xb.xbm, xb.xbn);
     return hipGetLastError();
 }
 
@@ -1008,11 +1043,13 @@ static hipError_t launch_persistent_t(const LinearArgs& a, const Plan& p, hipStr
     const int tiles_n = (a.N + BN - 1) / BN;
     const int tiles = tiles_m * tiles_n;
     const int grid = min(tiles, device_cu_count() * 2);
+    const XcdBlock xb = xcd_block(tiles_m, tiles_n, BM, BN, grid);
     // a k tile must hold whole stages (the kernel folds between stages)
     if (p.tiles_k != 1 && p.kbpt % KBS != 0)
         return hipErrorInvalidValue;
     if (p.tiles_k == 1) {
-        k_persistent<OX, OW, BM, BN, WM, WN, KBS, PDC, true><<<grid, WM * WN * 64, 0, s>>>(a, p.kbpt, tiles_m, tiles_n);
+        k_persistent<OX, OW, BM, BN, WM, WN, KBS, PDC, true><<<grid, WM * WN * 64, 0, s>>>(a, p.kbpt, tiles_m, tiles_n,
+                                                                                           xb.xbm, xb.xbn);
     } else {
         // the largest tiles exist only in the chained form (the dispatcher
         // never selects them for a recipe with several k tiles)
@@ -1020,7 +1057,7 @@ static hipError_t launch_persistent_t(const LinearArgs& a, const Plan& p, hipStr
             return hipErrorInvalidValue;
         else
             k_persistent<OX, OW, BM, BN, WM, WN, KBS, PD, false><<<grid, WM * WN * 64, 0, s>>>(a, p.kbpt, tiles_m,
-                                                                                              tiles_n);
+                                                                                              tiles_n, xb.xbm, xb.xbn);
     }
     return hipGetLastError();
 }
