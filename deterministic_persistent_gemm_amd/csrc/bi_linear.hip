@@ -938,12 +938,14 @@ static hipError_t launch_decode(const LinearArgs& a, const Plan& p, void* ws, hi
 {
     f32x4* partials = reinterpret_cast<f32x4*>(ws);
     hipError_t e;
-    // M tiles per wave: keep >= ~1024 waves in flight while reusing each
-    // wave's W fragments across as many M tiles as that allows
+    // M tiles per wave: a wave's W fragments serve 2 M tiles from 4 M tiles
+    // on and 4 from 12 on, while at least ~1000 waves remain (measured for
+    // the fp32 router: M=64 11.0 -> 10.4 us, M=96 13.5 -> 12.2, M=192 18.5
+    // -> 17.6; below 4 M tiles one M tile per wave is as fast)
     const int waves1 = p.ntiles * p.tiles_k * p.mtiles;
-    if (p.mtiles >= 4 && waves1 >= 4 * 2048)
+    if (p.mtiles >= 12 && waves1 >= 6144)
         e = launch_decode_mt<OX, OW, 4>(a, p, partials, s);
-    else if (p.mtiles >= 2 && waves1 >= 2 * 2048)
+    else if (p.mtiles >= 4 && waves1 >= 2048)
         e = launch_decode_mt<OX, OW, 2>(a, p, partials, s);
     else
         e = launch_decode_mt<OX, OW, 1>(a, p, partials, s);
