@@ -1,6 +1,6 @@
 // bi_linear.hip -- batch-invariant linear layer kernels for gfx950.
 //
-// Three kernel shapes carry out one recipe (bi_device.h) bit for bit:
+// Five kernel shapes carry out one recipe (bi_device.h) bit for bit:
 //
 //  * k_decode + k_decode_fold (small M): one wave per (16-column N tile, k
 //    tile partial, group of 16-row M tiles).  The k tile partials of one
@@ -14,12 +14,20 @@
 //    its waves compute the tile partials and fold them through LDS in one
 //    launch.
 //
+//  * k_decode_dma (small M, fully chained bf16 recipes): loader waves stream
+//    a 16-column weight slab into an LDS ring with direct-to-LDS loads for
+//    one wave that runs the chains.
+//
 //  * k_persistent (large M): a grid of at most two workgroups per compute
 //    unit loops over BM x BN output tiles.  Stages of k blocks of X and W go
 //    through LDS (16-byte loads along k, XOR-swizzled rows), the next stages
 //    are prefetched into registers, and the tile partials are chained in
 //    registers and added in ascending order, exactly as above.
 //
+//  * k_stream_bf16 (bf16, mid M): 64x64 tiles fed by a deep ring of LDS
+//    stages written by direct-to-LDS loads.
+//
+// The persistent kernels hand each XCD one block of the tile grid (xcd_tile).
 // GateLinear page, section "Update: is the M=4096 cost avoidable?": decode is
 // latency-bound and wants many small pieces of work, while M=4096 wants few
 // wide tiles so that X is not re-read once per N tile.  Keeping the recipe
