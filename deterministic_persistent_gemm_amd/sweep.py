@@ -21,6 +21,8 @@ with cold weights (rotating copies, beyond the Infinity Cache):
     DECODE_PROBE_MAX (the decode limit may lie beyond the decode sizes);
   * every persistent tile shape at M in PREFILL_M and at the decode sizes
     where the persistent kernel might take over;
+  * both at CROSS_M, which only places the decode limit between the
+    prefill sizes (it counts in neither total);
 
 Times are per-call averages over a replayed HIP graph of the calls.  The
 sweeper then checks that every path and tile shape of the candidate gives the same bits
@@ -52,6 +54,7 @@ TABLE = os.path.join(PKG, "csrc", "bi_table.inc")
 
 DECODE_M = (1, 8, 16, 32, 64, 128)
 PREFILL_M = (256, 1024, 4096)
+CROSS_M = (512,)            # timed on both sides to place the decode limit, not in either total
 DECODE_PROBE_MAX = 1024     # decode forms are also timed at the prefill sizes up to this M
 DECODE_MARGIN = 0.05        # the persistent kernel takes over once it is this much faster
 TABLE_HEADER = ("// Measured key table, written by deterministic_persistent_gemm_amd/sweep.py.\n"
@@ -263,7 +266,8 @@ def sweep_key(dt: str, N: int, K: int, profile: str, tie: float = 0.03, log=prin
     ncopies = max(2, min(128, math.ceil((512 << 20) / wbytes)))
     w0 = (torch.randn(N, K, generator=g) * 0.02).to(tdt)
     ws = [w0.to(dev)] + [w0.to(dev).clone() for _ in range(ncopies - 1)]
-    xs = {M: torch.randn(M, K, generator=g).to(tdt).to(dev) for M in sorted(set(DECODE_M + PREFILL_M))}
+    grid = sorted(set(DECODE_M + PREFILL_M + CROSS_M))
+    xs = {M: torch.randn(M, K, generator=g).to(tdt).to(dev) for M in grid}
     odt = torch.float32
     served = bi.bi_describe_recipe(bi.BI_F32 if dt == "f32" else bi.BI_BF16, N, K).block_k
     cands, summaries = [], []
@@ -271,7 +275,7 @@ def sweep_key(dt: str, N: int, K: int, profile: str, tie: float = 0.03, log=prin
         r = bi.bi_describe_recipe(bi.BI_F32 if dt == "f32" else bi.BI_BF16, N, K)
         r.block_k = bk
         cand = {"block_k": bk, "decode": {}, "persistent": {}, "bits_ok": True}
-        for M in sorted(set(DECODE_M + PREFILL_M)):
+        for M in grid:
             x = xs[M]
             out = torch.empty(M, N, dtype=odt, device=dev)
             ref = None
