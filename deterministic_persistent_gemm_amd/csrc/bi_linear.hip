@@ -24,8 +24,8 @@
 //    are prefetched into registers, and the tile partials are chained in
 //    registers and added in ascending order, exactly as above.
 //
-//  * k_stream_bf16 (bf16, mid M): 64x64 tiles fed by a deep ring of LDS
-//    stages written by direct-to-LDS loads.
+//  * k_stream_bf16 (bf16, mid M): 64x64 tiles on eight waves fed by a deep
+//    ring of LDS stages written by direct-to-LDS loads.
 //
 // The persistent kernels hand each XCD one block of the tile grid (xcd_tile).
 // GateLinear page, section "Update: is the M=4096 cost avoidable?": decode is
@@ -743,15 +743,18 @@ __global__ __launch_bounds__(WM * WN * 64) void k_persistent(LinearArgs a, int k
 // bf16 recipes at mid-size M, where the work is bound by how fast each
 // compute unit can stream its operand rows in (a register-staged kernel keeps
 // too few bytes in flight per CU to cover the memory latency): one 64x64
-// output tile per workgroup of four waves (each a 32x32 quarter), X and W
-// streamed into a ring of kStreamRing LDS stages of 64 k by direct-to-LDS
-// loads issued kStreamRing - 1 stages ahead, i.e. about 112 KiB in flight
-// per compute unit.  One barrier per stage; the next stage's fragments are
-// read while the current stage's MFMAs issue.  The chains are the recipe's
-// (one v_mfma_f32_16x16x32_bf16 per k block in ascending order, the usual
-// lane slots; with several k tiles the partials are cleared and added in
-// ascending order at tile boundaries, which fall between stages), so the bits
-// equal every other path's.
+// output tile per workgroup of eight waves (each a 16x32 slice, two waves
+// per SIMD), X and W streamed into a ring of kStreamRing LDS stages of 64 k
+// by direct-to-LDS loads issued kStreamRing - 1 stages ahead, i.e. about
+// 112 KiB in flight per compute unit.  Direct-to-LDS loads issue at a rate
+// per wave, so eight issuing waves stream faster than four (dense bf16
+// M=256: 24.2 us against 26.1; deeper rings of 9 or 10 stages were slower).
+// One barrier per stage; the next stage's fragments are read while the
+// current stage's MFMAs issue.  The chains are the recipe's (one
+// v_mfma_f32_16x16x32_bf16 per k block in ascending order, the usual lane
+// slots; with several k tiles the partials are cleared and added in ascending
+// order at tile boundaries, which fall between stages), so the bits equal
+// every other path's.
 //
 // Stage layout: X rows 0..63 then W rows 0..63, 128 bytes (64 k) per row,
 // chunk c of row q at position c ^ ((q / 2) & 7) -- the Stager layout for
@@ -760,16 +763,18 @@ __global__ __launch_bounds__(WM * WN * 64) void k_persistent(LinearArgs a, int k
 // fetches chunk (i % 8) ^ key(row) of its row.
 constexpr int kStreamTile = 64;
 constexpr int kStreamRing = 8;
+constexpr int kStreamWaves = 8;
 constexpr int kStreamRowBytes = 2 * kKBlock * 2;                         // 64 k of bf16
 constexpr int kStreamHalf = kStreamTile * kStreamRowBytes;               // 8 KiB
 constexpr int kStreamStage = 2 * kStreamHalf;                            // 16 KiB
 
 template <bool CHAINED>
-__global__ __launch_bounds__(256) void k_stream_bf16(LinearArgs a, int kbpt, int tiles_m, int tiles_n, int xbm, int xbn)
+__global__ __launch_bounds__(kStreamWaves * 64) void k_stream_bf16(LinearArgs a, int kbpt, int tiles_m, int tiles_n,
+                                                                  int xbm, int xbn)
 {
     __shared__ __attribute__((aligned(16))) unsigned char ring[kStreamRing * kStreamStage];
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const int wm = w >> 1, wn = w & 1;
+    const int wm = w >> 1, wn = w & 1;                                   // rows 16 wm.., columns 32 wn..
     const int r = lane & 15, g = lane >> 4;
     const int ns = a.K / (2 * kKBlock);                                  // stages
     const int tiles = tiles_m * tiles_n;
@@ -780,77 +785,65 @@ __global__ __launch_bounds__(256) void k_stream_bf16(LinearArgs a, int kbpt, int
     for (int it = blockIdx.x; it < tiles; it += gridDim.x) {
         const int tile = xcd_tile(it, tiles_n, xbm, xbn);
         const int m0 = (tile / tiles_n) * kStreamTile, n0 = (tile % tiles_n) * kStreamTile;
-        // wave w loads rows 16 w .. 16 w + 15 of the X and W tiles, 8 per load;
-        // rows past M (N) read row M-1 (N-1), whose results are never stored
-        const uint16_t* src[4];
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            const int row = 16 * w + 8 * t + (lane >> 3);
-            const int chunk = (lane & 7) ^ ((row >> 1) & 7);
-            src[t] = xg + (int64_t)min(m0 + row, a.M - 1) * a.ldx + chunk * 8;
-            src[2 + t] = wg + (int64_t)min(n0 + row, a.N - 1) * a.ldw + chunk * 8;
-        }
+        // wave w loads rows 8 w .. 8 w + 7 of the X and of the W tile, one
+        // load each; rows past M (N) read row M-1 (N-1), whose results are
+        // never stored
+        const int lrow = 8 * w + (lane >> 3);
+        const int lchunk = (lane & 7) ^ ((lrow >> 1) & 7);
+        const uint16_t* src[2] = {xg + (int64_t)min(m0 + lrow, a.M - 1) * a.ldx + lchunk * 8,
+                                  wg + (int64_t)min(n0 + lrow, a.N - 1) * a.ldw + lchunk * 8};
         auto issue = [&](int s) {
-            const uint32_t base = lds0 + (uint32_t)(s % kStreamRing) * kStreamStage + (16 * w) * kStreamRowBytes;
+            const uint32_t base = lds0 + (uint32_t)(s % kStreamRing) * kStreamStage + (8 * w) * kStreamRowBytes;
 #pragma unroll
-            for (int t = 0; t < 4; ++t)
+            for (int t = 0; t < 2; ++t)
                 dma16(src[t] + (int64_t)s * 2 * kKBlock,
-                      (uint32_t)__builtin_amdgcn_readfirstlane(
-                          (int)(base + (t >> 1) * kStreamHalf + (t & 1) * 8 * kStreamRowBytes)));
+                      (uint32_t)__builtin_amdgcn_readfirstlane((int)(base + t * kStreamHalf)));
         };
-        // fragment of k block b (0, 1) of stage s: X rows wm*32 + 16 i + r,
-        // W rows wn*32 + 16 i + r; chunk 4 b + g of the row
+        // fragment of k block b (0, 1) of stage s: X row wm*16 + r, W rows
+        // wn*32 + 16 n + r; chunk 4 b + g of the row
         auto frag = [&](int s, int half, int row, int b) {
             const unsigned char* p = ring + (s % kStreamRing) * kStreamStage + half * kStreamHalf;
             return *reinterpret_cast<const u32x4*>(p + row * kStreamRowBytes + (((4 * b + g) ^ ((row >> 1) & 7)) << 4));
         };
-        auto frags = [&](u32x4 (&x)[2][2], u32x4 (&wf)[2][2], int s) {
+        auto frags = [&](u32x4 (&x)[2], u32x4 (&wf)[2][2], int s) {
 #pragma unroll
-            for (int b = 0; b < 2; ++b)
+            for (int b = 0; b < 2; ++b) {
+                x[b] = frag(s, 0, wm * 16 + r, b);
 #pragma unroll
-                for (int i = 0; i < 2; ++i) {
-                    x[b][i] = frag(s, 0, wm * 32 + 16 * i + r, b);
-                    wf[b][i] = frag(s, 1, wn * 32 + 16 * i + r, b);
-                }
+                for (int n = 0; n < 2; ++n)
+                    wf[b][n] = frag(s, 1, wn * 32 + 16 * n + r, b);
+            }
         };
 
-        f32x4 acc[2][2], part[2][2];
+        f32x4 acc[2], part[2];
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int n = 0; n < 2; ++n) {
-                acc[i][n] = f32x4{0.f, 0.f, 0.f, 0.f};
-                part[i][n] = acc[i][n];
-            }
-        auto mfmas = [&](const u32x4 (&x)[2][2], const u32x4 (&wf)[2][2], int s) {
+        for (int n = 0; n < 2; ++n) {
+            acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+            part[n] = acc[n];
+        }
+        auto mfmas = [&](const u32x4 (&x)[2], const u32x4 (&wf)[2][2], int s) {
 #pragma unroll
             for (int b = 0; b < 2; ++b) {
                 const int kb = 2 * s + b;
                 if constexpr (!CHAINED) {
                     if (kb % kbpt == 0) {
 #pragma unroll
-                        for (int i = 0; i < 2; ++i)
-#pragma unroll
-                            for (int n = 0; n < 2; ++n)
-                                part[i][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+                        for (int n = 0; n < 2; ++n)
+                            part[n] = f32x4{0.f, 0.f, 0.f, 0.f};
                     }
                 }
 #pragma unroll
-                for (int i = 0; i < 2; ++i)
-#pragma unroll
-                    for (int n = 0; n < 2; ++n) {
-                        f32x4& c = CHAINED ? acc[i][n] : part[i][n];
-                        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, x[b][i]),
-                                                                    __builtin_bit_cast(bf16x8, wf[b][n]), c, 0, 0, 0);
-                    }
+                for (int n = 0; n < 2; ++n) {
+                    f32x4& c = CHAINED ? acc[n] : part[n];
+                    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, x[b]),
+                                                                __builtin_bit_cast(bf16x8, wf[b][n]), c, 0, 0, 0);
+                }
                 if constexpr (!CHAINED) {
                     if (kb % kbpt == kbpt - 1) {
                         const bool first = kb < kbpt;
 #pragma unroll
-                        for (int i = 0; i < 2; ++i)
-#pragma unroll
-                            for (int n = 0; n < 2; ++n)
-                                acc[i][n] = first ? part[i][n] : acc[i][n] + part[i][n];
+                        for (int n = 0; n < 2; ++n)
+                            acc[n] = first ? part[n] : acc[n] + part[n];
                     }
                 }
             }
@@ -862,18 +855,17 @@ __global__ __launch_bounds__(256) void k_stream_bf16(LinearArgs a, int kbpt, int
         bar();
         for (int s = 0; s < kStreamRing - 1 && s < ns; ++s)
             issue(s);
-        wait_later<4, kStreamRing - 2>(min(kStreamRing - 2, ns - 1));
+        wait_later<2, kStreamRing - 2>(min(kStreamRing - 2, ns - 1));
         bar();
-        u32x4 xa[2][2], wa[2][2], xb[2][2], wb[2][2];
+        u32x4 xa[2], wa[2][2], xb[2], wb[2][2];
         frags(xa, wa, 0);
         // stage s: make stage s+1 visible (this wave's loads of it waited
         // for, then the barrier, which also tells that every wave is done
         // with stage s-1, whose slot the load issued next refills), read its
         // fragments, then the MFMAs of stage s
-        auto step = [&](int s, const u32x4 (&xc)[2][2], const u32x4 (&wc)[2][2], u32x4 (&xn)[2][2],
-                        u32x4 (&wnx)[2][2]) {
+        auto step = [&](int s, const u32x4 (&xc)[2], const u32x4 (&wc)[2][2], u32x4 (&xn)[2], u32x4 (&wnx)[2][2]) {
             if (s + 1 < ns) {
-                wait_later<4, kStreamRing - 3>(min(kStreamRing - 3, ns - 2 - s));
+                wait_later<2, kStreamRing - 3>(min(kStreamRing - 3, ns - 2 - s));
                 bar();
                 if (s + kStreamRing - 1 < ns)
                     issue(s + kStreamRing - 1);
@@ -888,11 +880,8 @@ __global__ __launch_bounds__(256) void k_stream_bf16(LinearArgs a, int kbpt, int
         }
 
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int n = 0; n < 2; ++n)
-                store_acc(a, m0 + wm * 32 + i * 16 + acc_row(lane, 0), n0 + wn * 32 + n * 16 + acc_col(lane),
-                          acc[i][n]);
+        for (int n = 0; n < 2; ++n)
+            store_acc(a, m0 + wm * 16 + acc_row(lane, 0), n0 + wn * 32 + n * 16 + acc_col(lane), acc[n]);
     }
 }
 
@@ -906,9 +895,9 @@ static hipError_t launch_stream_bf16(const LinearArgs& a, const Plan& p, hipStre
     const int grid = min(tiles_m * tiles_n, device_cu_count());
     const XcdBlock xb = xcd_block(tiles_m, tiles_n, kStreamTile, kStreamTile, grid);
     if (p.tiles_k == 1)
-        k_stream_bf16<true><<<grid, 256, 0, s>>>(a, p.kbpt, tiles_m, tiles_n, xb.xbm, xb.xbn);
+        k_stream_bf16<true><<<grid, kStreamWaves * 64, 0, s>>>(a, p.kbpt, tiles_m, tiles_n, xb.xbm, xb.xbn);
     else
-        k_stream_bf16<false><<<grid, 256, 0, s>>>(a, p.kbpt, tiles_m, tiles_n, xb.xbm, xb.xbn);
+        k_stream_bf16<false><<<grid, kStreamWaves * 64, 0, s>>>(a, p.kbpt, tiles_m, tiles_n, xb.xbm, xb.xbn);
     return hipGetLastError();
 }
 

@@ -223,7 +223,7 @@ const char* bi_status_str(bi_status_t status);
  * bf16: 11 = 128x128, 12 = 64x64, 13 = 128x128 with 128-k stages,
  * 14 = 256x128, 15 = 128x256, 16 = 64x128 with 128-k stages, 17 = 64x64
  * with 32-k stages, 18 = 256x256 on 2x4 waves, 19 = 256x256 on 4x2 waves,
- * 20 = 64x64 on 2x2 waves fed by a ring of eight 64-k LDS stages through
+ * 20 = 64x64 on 4x2 waves fed by a ring of eight 64-k LDS stages through
  * direct-to-LDS loads; 18 and 19 serve fully chained recipes only, 20 needs
  * K a multiple of 64; a shape that cannot serve falls back to another).
  * Tile shapes never change the numerics. */
