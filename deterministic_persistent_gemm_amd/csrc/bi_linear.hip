@@ -262,9 +262,10 @@ __global__ __launch_bounds__(NW * 64) void k_decode_wg(LinearArgs a, int kbpt, i
 // would otherwise wait on its own loads; here kLoaders waves stream the
 // weight slab and the activation rows into an LDS ring with direct-to-LDS
 // loads (each k block of 16 rows lands as one 1 KiB chunk laid out exactly
-// as the fragment lanes read it), several phases ahead, and wave 0 only
-// reads LDS and issues the chain.  Phases are handed over with one barrier
-// each; a loader waits for its own loads of a phase before the barrier.
+// as the fragment lanes read it), several phases ahead, and MT chain waves
+// only read LDS and issue the chains, one M tile each.  Phases are handed
+// over with one barrier each; a loader waits for its own loads of a phase
+// before the barrier.
 constexpr int kDmaLoaders = 8;
 
 // One 16-byte direct-to-LDS load per lane: lane i's bytes land at LDS byte
@@ -320,7 +321,7 @@ __device__ __forceinline__ void wait_later(int later)
 constexpr int kDmaXMaxK = 4096;
 
 template <int MT, int PB, int R, int XR>
-__global__ __launch_bounds__((kDmaLoaders + 1) * 64) void k_decode_dma(LinearArgs a)
+__global__ __launch_bounds__((kDmaLoaders + MT) * 64) void k_decode_dma(LinearArgs a)
 {
     static_assert(XR == 0 || MT == 1, "activation rows in LDS for one M tile");
     constexpr int IPB = XR ? 1 : 1 + MT;              // 1 KiB items per k block: W (then MT X tiles)
@@ -344,18 +345,19 @@ __global__ __launch_bounds__((kDmaLoaders + 1) * 64) void k_decode_dma(LinearArg
     const int kc = a.K / 8;                           // 16-byte chunks per activation row
     const uint16_t* xbase = reinterpret_cast<const uint16_t*>(a.x);
 
-    if (wave > 0) {
+    if (wave >= MT) {
+        const int ld = wave - MT;                     // loader index
         if constexpr (XR > 0) {
             // the activation rows, once: chunk c of row c / kc, 64 chunks per load
             const int nload = (XR * kc) / 64;
-            for (int d = wave - 1; d < nload; d += kDmaLoaders) {
+            for (int d = ld; d < nload; d += kDmaLoaders) {
                 const int c = d * 64 + lane;
                 const int row = min(c / kc, a.M - 1);
                 dma16(xbase + (int64_t)row * a.ldx + (c % kc) * 8,
                       (uint32_t)__builtin_amdgcn_readfirstlane((int)lds_addr(&xs[d * 64])));
             }
         }
-        // loader: items i = (wave - 1) + kDmaLoaders * t of every phase
+        // loader: items i = ld + kDmaLoaders * t of every phase
         const uint16_t* wrow = reinterpret_cast<const uint16_t*>(a.w) + (int64_t)(nt * 16 + r) * a.ldw + kSlotLen * g;
         const uint16_t* wslab = reinterpret_cast<const uint16_t*>(a.w) + (int64_t)(nt * 16) * a.ldw + 8 * lane;
         auto issue = [&](int ph) {
@@ -363,7 +365,7 @@ __global__ __launch_bounds__((kDmaLoaders + 1) * 64) void k_decode_dma(LinearArg
                 // whole rows: lane l takes k = ph*PB*32 + 8l .. +7 of row i
 #pragma unroll
                 for (int t = 0; t < LW; ++t) {
-                    const int i = (wave - 1) + kDmaLoaders * t;
+                    const int i = ld + kDmaLoaders * t;
                     dma16(wslab + (int64_t)i * a.ldw + (int64_t)ph * PB * kKBlock,
                           (uint32_t)__builtin_amdgcn_readfirstlane((int)lds_addr(&ring[ph % R][i][0])));
                 }
@@ -371,7 +373,7 @@ __global__ __launch_bounds__((kDmaLoaders + 1) * 64) void k_decode_dma(LinearArg
             }
 #pragma unroll
             for (int t = 0; t < LW; ++t) {
-                const int i = (wave - 1) + kDmaLoaders * t;
+                const int i = ld + kDmaLoaders * t;
                 const int j = i / IPB, kind = i % IPB;      // kind 0: W, m + 1: X tile m
                 const int64_t k0 = (int64_t)(ph * PB + j) * kKBlock;
                 // rows past M read row M-1 (always valid); their results are never stored
@@ -395,11 +397,11 @@ __global__ __launch_bounds__((kDmaLoaders + 1) * 64) void k_decode_dma(LinearArg
         return;
     }
 
-    // wave 0: the chains
-    f32x4 acc[MT][1];
-#pragma unroll
-    for (int m = 0; m < MT; ++m)
-        acc[m][0] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // waves 0 .. MT-1: the chains, wave m the chain of M tile m (the weight
+    // fragment of each k block is read by every chain wave; the chains run
+    // on MT SIMDs side by side instead of one after another in one wave)
+    const int m = wave;
+    f32x4 acc[1][1] = {{f32x4{0.f, 0.f, 0.f, 0.f}}};
     const int xrow = min(r, a.M - 1);
     for (int ph = 0; ph < P; ++ph) {
         wait_lgkm0();          // the previous phase's LDS reads are done before its slot is refilled
@@ -407,23 +409,18 @@ __global__ __launch_bounds__((kDmaLoaders + 1) * 64) void k_decode_dma(LinearArg
         const u32x4(*slot)[kRowPitch] = ring[ph % R];
 #pragma unroll
         for (int j = 0; j < PB; ++j) {
-            FragOf<BF16> wf[1], xf[MT];
+            FragOf<BF16> wf[1], xf[1];
             if constexpr (XR > 0) {
                 wf[0].v = slot[r][j * 4 + g];
                 xf[0].v = xs[xrow * kc + (ph * PB + j) * 4 + g];
             } else {
                 wf[0].v = slot[j * IPB][lane];
-#pragma unroll
-                for (int m = 0; m < MT; ++m)
-                    xf[m].v = slot[j * IPB + 1 + m][lane];
+                xf[0].v = slot[j * IPB + 1 + m][lane];
             }
-            mfma_tiles<MT, 1>(xf, wf, acc);
+            mfma_tiles<1, 1>(xf, wf, acc);
         }
     }
-    const int col = nt * 16 + acc_col(lane);
-#pragma unroll
-    for (int m = 0; m < MT; ++m)
-        store_acc(a, m * 16 + acc_row(lane, 0), col, acc[m][0]);
+    store_acc(a, m * 16 + acc_row(lane, 0), nt * 16 + acc_col(lane), acc[0][0]);
 }
 
 // One LDS stage holds KBS k blocks of BM rows of X and BN rows of W.  Each
@@ -1009,21 +1006,22 @@ static hipError_t launch_decode_dma(const LinearArgs& a, const Plan& p, hipStrea
     if (!decode_dma_ok(p, a.K))
         return hipErrorInvalidValue;
     const dim3 grid((unsigned)p.ntiles);
-    const int threads = (kDmaLoaders + 1) * 64;
+    // MT chain waves, then the loaders
+    auto threads = [](int mt) { return (kDmaLoaders + mt) * 64; };
     // LDS: ring R x PB x (items per block) KiB, plus XR activation rows of
     // up to 8 KiB each
     if (p.mtiles == 1 && a.K <= kDmaXMaxK && a.M == 1)
-        k_decode_dma<1, 16, 8, 1><<<grid, threads, 0, s>>>(a);      // 128 + 8 KiB
+        k_decode_dma<1, 16, 8, 1><<<grid, threads(1), 0, s>>>(a);      // 128 + 8 KiB
     else if (p.mtiles == 1 && a.K <= kDmaXMaxK && a.M <= 4)
-        k_decode_dma<1, 16, 7, 4><<<grid, threads, 0, s>>>(a);      // 112 + 32 KiB
+        k_decode_dma<1, 16, 7, 4><<<grid, threads(1), 0, s>>>(a);      // 112 + 32 KiB
     else if (p.mtiles == 1 && a.K <= kDmaXMaxK && a.M <= 8)
-        k_decode_dma<1, 16, 5, 8><<<grid, threads, 0, s>>>(a);      // 80 + 64 KiB
+        k_decode_dma<1, 16, 5, 8><<<grid, threads(1), 0, s>>>(a);      // 80 + 64 KiB
     else if (p.mtiles == 1)
-        k_decode_dma<1, 16, 4, 0><<<grid, threads, 0, s>>>(a);      // 128 KiB, activation in the ring
+        k_decode_dma<1, 16, 4, 0><<<grid, threads(1), 0, s>>>(a);      // 128 KiB, activation in the ring
     else if (p.mtiles == 2)
-        k_decode_dma<2, 8, 4, 0><<<grid, threads, 0, s>>>(a);       // 96 KiB
+        k_decode_dma<2, 8, 4, 0><<<grid, threads(2), 0, s>>>(a);       // 96 KiB
     else
-        k_decode_dma<4, 8, 3, 0><<<grid, threads, 0, s>>>(a);       // 120 KiB (3 M tiles read a clamped 4th)
+        k_decode_dma<4, 8, 3, 0><<<grid, threads(4), 0, s>>>(a);       // 120 KiB (3 M tiles read a clamped 4th)
     return hipGetLastError();
 }
 
