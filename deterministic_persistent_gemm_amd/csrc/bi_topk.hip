@@ -19,19 +19,22 @@
 //    where the running rank lands.  Histogram bins are integer counts, so the
 //    order in which the LDS atomics land cannot change T (the page's concern
 //    is atomics that decide WHICH tied lane wins; here none does).  Each bin
-//    has 4 (last pass: 2) copies, picked by lane, so a plateau of equal
-//    scores does not serialise a wave's increments on one address.  The three
-//    histograms (72 KiB) are cleared once while the row's loads are in
-//    flight, and 72 KiB leaves room for two rows per compute unit.
+//    has several copies, picked by lane, so a plateau of equal scores does
+//    not serialise a wave's increments on one address.  The three histograms
+//    are cleared once while the row's loads are in flight.
 //  * Emission: every lane with key > T and the first `budget` lanes (in
 //    column order) with key == T, where budget = k_eff - #(key > T).  A
 //    lane's output slot is #(key > T before it) + min(#(key == T before it),
 //    budget), from one exclusive scan, so the output is ascending in column
 //    and row-local (column - rs); slots k_eff .. topk-1 get -1.
 //
-// One workgroup of 1024 threads per row; thread t owns the 8 consecutive
-// columns [8t, 8t + 8), which bounds a row at 8192 columns (the envelope the
-// page's fast path is gated to).
+// One workgroup per row; thread t owns PT consecutive columns [PT t, PT t +
+// PT), NT x PT = 8192 columns (the envelope the page's fast path is gated
+// to).  Two forms carry out the same selection: 1024 threads with 8 columns
+// each and 4/4/2 histogram copies (72 KiB of LDS, two rows per compute unit:
+// the shortest time per row, for decode batches), and 512 threads with 16
+// columns each and 2/2/1 copies (36 KiB, four rows per compute unit: more
+// rows in flight, for prefill batches).
 #include <hip/hip_runtime.h>
 
 #include "bi_device.h"
@@ -41,15 +44,20 @@ namespace bi {
 
 namespace {
 
-constexpr int kThreads = 1024;
-constexpr int kPerThread = 8;
-constexpr int kWaves = kThreads / 64;
-static_assert(kThreads * kPerThread == kTopkMaxCols, "row envelope");
+template <int NT>
+struct TopkCfg;
+template <>
+struct TopkCfg<1024> {
+    static constexpr int kC0 = 4, kC1 = 4, kC2 = 2;
+};
+template <>
+struct TopkCfg<512> {
+    static constexpr int kC0 = 2, kC1 = 2, kC2 = 1;
+};
 
-// Radix digits (most significant first) and LDS copies of each histogram.
-constexpr int kShift0 = 21, kBins0 = 2048, kCopies0 = 4;   // key bits 31..21
-constexpr int kShift1 = 10, kBins1 = 2048, kCopies1 = 4;   // key bits 20..10
-constexpr int kShift2 = 0, kBins2 = 1024, kCopies2 = 2;    // key bits 9..0
+constexpr int kShift0 = 21, kBins0 = 2048;   // key bits 31..21
+constexpr int kShift1 = 10, kBins1 = 2048;   // key bits 20..10
+constexpr int kShift2 = 0, kBins2 = 1024;    // key bits 9..0
 
 __device__ __forceinline__ uint32_t rank_bits(float v)
 {
@@ -59,10 +67,12 @@ __device__ __forceinline__ uint32_t rank_bits(float v)
     return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
-
-// Inclusive prefix sum over the workgroup's threads in thread order.
+// Inclusive scan over the workgroup: the wave scan (wave_incl_scan), then the
+// wave totals of the lower waves added from LDS.
+template <int NT>
 __device__ __forceinline__ uint32_t block_incl_scan(uint32_t v, uint32_t* wsum, int lane, int wave)
 {
+    constexpr int kWaves = NT / 64;
     v = wave_incl_scan(v, lane);
     if (lane == 63)
         wsum[wave] = v;
@@ -81,72 +91,84 @@ __device__ __forceinline__ uint32_t block_incl_scan(uint32_t v, uint32_t* wsum, 
 template <int COPIES>
 __device__ __forceinline__ uint32_t bin_count(const uint32_t* hist, int bin)
 {
-    if constexpr (COPIES == 8) {
-        const uint4 a = reinterpret_cast<const uint4*>(hist)[2 * bin];
-        const uint4 b = reinterpret_cast<const uint4*>(hist)[2 * bin + 1];
-        return a.x + a.y + a.z + a.w + b.x + b.y + b.z + b.w;
-    } else if constexpr (COPIES == 4) {
+    if constexpr (COPIES == 4) {
         const uint4 h = reinterpret_cast<const uint4*>(hist)[bin];
         return h.x + h.y + h.z + h.w;
-    } else {
+    } else if constexpr (COPIES == 2) {
         const uint2 h = reinterpret_cast<const uint2*>(hist)[bin];
         return h.x + h.y;
+    } else {
+        return hist[bin];
     }
 }
 
 // One radix pass.  Counts the digit (key >> SHIFT) % BINS of the active lanes
 // into `hist` (COPIES copies per bin, by lane), finds the digit d holding the
 // rem-th largest active key (#(digit > d) < rem <= #(digit >= d)) with one
-// block-wide scan over the bins in descending order, and returns the updated
-// prefix and rank through LDS.
-template <int SHIFT, int BINS, int COPIES>
-__device__ __forceinline__ void radix_pass(uint32_t* hist, uint32_t* wsum, uint32_t* sel,
-                                           const uint32_t (&key)[kPerThread], uint32_t& active, uint32_t& prefix,
-                                           uint32_t& rem, int tid, int lane, int wave)
+// block-wide scan over the bins in descending order (thread t holds the
+// BINS/NT bins just below BINS - BINS/NT * t), and returns the updated prefix
+// and rank through LDS.
+template <int NT, int PT, int SHIFT, int BINS, int COPIES>
+__device__ __forceinline__ void radix_pass(uint32_t* hist, uint32_t* wsum, uint32_t* sel, const uint32_t (&key)[PT],
+                                           uint32_t& active, uint32_t& prefix, uint32_t& rem, int tid, int lane,
+                                           int wave)
 {
     constexpr uint32_t kMask = BINS - 1;
-    constexpr int kPer = BINS / kThreads;     // bins per thread in the scan: 1 or 2
-    static_assert(kPer == 1 || kPer == 2, "bins per thread");
+    constexpr int kPer = BINS / NT;           // bins per thread in the scan
+    static_assert(kPer >= 1 && kPer * NT == BINS, "bins per thread");
     const int copy = lane & (COPIES - 1);
 #pragma unroll
-    for (int j = 0; j < kPerThread; ++j)
+    for (int j = 0; j < PT; ++j)
         if ((active >> j) & 1u)
             atomicAdd(&hist[((key[j] >> SHIFT) & kMask) * COPIES + copy], 1u);
     __syncthreads();
-    // descending digit order: thread t holds bins BINS-1-kPer*t ... (high first)
-    const int bh = BINS - 1 - kPer * tid;
-    const uint32_t ch = bin_count<COPIES>(hist, bh);
-    const uint32_t cl = kPer == 2 ? bin_count<COPIES>(hist, bh - 1) : 0u;
-    const uint32_t ge_l = block_incl_scan(ch + cl, wsum, lane, wave);   // #(digit >= lowest bin held)
-    const uint32_t ge_h = ge_l - cl;                                     // #(digit >= bh)
-    if (ge_h - ch < rem && rem <= ge_h) {
-        sel[0] = prefix | ((uint32_t)bh << SHIFT);
-        sel[1] = rem - (ge_h - ch);
-    } else if (kPer == 2 && ge_h < rem && rem <= ge_l) {
-        sel[0] = prefix | ((uint32_t)(bh - 1) << SHIFT);
-        sel[1] = rem - ge_h;
+    const int bh = BINS - 1 - kPer * tid;     // highest bin held, then bh-1, ...
+    uint32_t c[kPer], total = 0;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+        c[i] = bin_count<COPIES>(hist, bh - i);
+        total += c[i];
+    }
+    // #(digit >= bh - i) = #(digit > bh) + c[0] + ... + c[i]
+    uint32_t ge = block_incl_scan<NT>(total, wsum, lane, wave) - total;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+        const uint32_t ge_i = ge + c[i];
+        if (ge < rem && rem <= ge_i) {
+            sel[0] = prefix | ((uint32_t)(bh - i) << SHIFT);
+            sel[1] = rem - ge;
+        }
+        ge = ge_i;
     }
     __syncthreads();
     prefix = sel[0];
     rem = sel[1];
     const uint32_t dsel = (prefix >> SHIFT) & kMask;
 #pragma unroll
-    for (int j = 0; j < kPerThread; ++j)
+    for (int j = 0; j < PT; ++j)
         if (((key[j] >> SHIFT) & kMask) != dsel)
             active &= ~(1u << j);
 }
 
-__global__ __launch_bounds__(kThreads) void k_topk_rows(const float* __restrict__ scores, int64_t ld, int cols,
-                                                        int vec_ok, const int64_t* __restrict__ row_start,
-                                                        const int64_t* __restrict__ row_end, int topk,
-                                                        int32_t* __restrict__ out, int64_t ld_out)
+template <int NT>
+__global__ __launch_bounds__(NT) void k_topk_rows(const float* __restrict__ scores, int64_t ld, int cols, int vec_ok,
+                                                  const int64_t* __restrict__ row_start,
+                                                  const int64_t* __restrict__ row_end, int topk,
+                                                  int32_t* __restrict__ out, int64_t ld_out)
 {
-    // one histogram per pass, all cleared once while the row is in flight
-    __shared__ __attribute__((aligned(16))) uint32_t hist0[kBins0 * kCopies0];
-    __shared__ __attribute__((aligned(16))) uint32_t hist1[kBins1 * kCopies1];
-    __shared__ __attribute__((aligned(16))) uint32_t hist2[kBins2 * kCopies2];
-    __shared__ __attribute__((aligned(16))) uint32_t wsum[4][kWaves];
+    constexpr int PT = kTopkMaxCols / NT;     // columns per thread
+    constexpr int C0 = TopkCfg<NT>::kC0, C1 = TopkCfg<NT>::kC1, C2 = TopkCfg<NT>::kC2;
+    static_assert(NT * PT == kTopkMaxCols && PT <= 16 && PT % 4 == 0, "row envelope");
+    // one histogram per pass, all cleared once while the row is in flight;
+    // the first two are one array, which later stages the selection
+    constexpr int kH0 = kBins0 * C0, kH1 = kBins1 * C1, kH2 = kBins2 * C2;
+    static_assert(kH0 + kH1 >= kTopkMaxCols, "staging fits the first two histograms");
+    __shared__ __attribute__((aligned(16))) uint32_t hist01[kH0 + kH1];
+    __shared__ __attribute__((aligned(16))) uint32_t hist2[kH2];
+    __shared__ __attribute__((aligned(16))) uint32_t wsum[4][NT / 64];
     __shared__ uint32_t sel[2];
+    uint32_t* hist0 = hist01;
+    uint32_t* hist1 = hist01 + kH0;
 
     const int r = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -157,23 +179,24 @@ __global__ __launch_bounds__(kThreads) void k_topk_rows(const float* __restrict_
     const int keff = min(topk, max(re - rs, 0));
     int32_t* orow = out + (int64_t)r * ld_out;
 
-    // this thread's window columns [lo, hi) within [c0, c0 + 8)
-    const int c0 = tid * kPerThread;
-    const int lo = max(c0, rs), hi = min(c0 + kPerThread, re);
-    float v[kPerThread];
+    // this thread's window columns [lo, hi) within [c0, c0 + PT)
+    const int c0 = tid * PT;
+    const int lo = max(c0, rs), hi = min(c0 + PT, re);
+    float v[PT];
 #pragma unroll
-    for (int j = 0; j < kPerThread; ++j)
+    for (int j = 0; j < PT; ++j)
         v[j] = 0.f;
     if (lo < hi) {
         const float* p = scores + (int64_t)r * ld + c0;
-        if (vec_ok && c0 + kPerThread <= cols) {
-            const float4 a = reinterpret_cast<const float4*>(p)[0];
-            const float4 b = reinterpret_cast<const float4*>(p)[1];
-            v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-            v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+        if (vec_ok && c0 + PT <= cols) {
+#pragma unroll
+            for (int q = 0; q < PT / 4; ++q) {
+                const float4 a = reinterpret_cast<const float4*>(p)[q];
+                v[4 * q] = a.x; v[4 * q + 1] = a.y; v[4 * q + 2] = a.z; v[4 * q + 3] = a.w;
+            }
         } else {
 #pragma unroll
-            for (int j = 0; j < kPerThread; ++j)
+            for (int j = 0; j < PT; ++j)
                 if (c0 + j >= lo && c0 + j < hi)
                     v[j] = p[j];
         }
@@ -182,48 +205,43 @@ __global__ __launch_bounds__(kThreads) void k_topk_rows(const float* __restrict_
 
     if (keff > 0) {
         {
-            uint4* h0 = reinterpret_cast<uint4*>(hist0);
-            uint4* h1 = reinterpret_cast<uint4*>(hist1);
+            uint4* h01 = reinterpret_cast<uint4*>(hist01);
             uint4* h2 = reinterpret_cast<uint4*>(hist2);
 #pragma unroll
-            for (int i = 0; i < kBins0 * kCopies0 / 4 / kThreads; ++i)
-                h0[tid + i * kThreads] = uint4{0u, 0u, 0u, 0u};
-#pragma unroll
-            for (int i = 0; i < kBins1 * kCopies1 / 4 / kThreads; ++i)
-                h1[tid + i * kThreads] = uint4{0u, 0u, 0u, 0u};
-            if (tid < kBins2 * kCopies2 / 4)
+            for (int i = 0; i < (kH0 + kH1) / 4 / NT; ++i)
+                h01[tid + i * NT] = uint4{0u, 0u, 0u, 0u};
+            if (tid < kH2 / 4)
                 h2[tid] = uint4{0u, 0u, 0u, 0u};
         }
-        uint32_t key[kPerThread];
+        uint32_t key[PT];
 #pragma unroll
-        for (int j = 0; j < kPerThread; ++j)
+        for (int j = 0; j < PT; ++j)
             key[j] = rank_bits(v[j]);
         __syncthreads();
 
         // ---- radix select of the keff-th largest key
         uint32_t prefix = 0, rem = (uint32_t)keff, active = valid;
-        radix_pass<kShift0, kBins0, kCopies0>(hist0, wsum[0], sel, key, active, prefix, rem, tid, lane, wave);
-        radix_pass<kShift1, kBins1, kCopies1>(hist1, wsum[1], sel, key, active, prefix, rem, tid, lane, wave);
-        radix_pass<kShift2, kBins2, kCopies2>(hist2, wsum[2], sel, key, active, prefix, rem, tid, lane, wave);
+        radix_pass<NT, PT, kShift0, kBins0, C0>(hist0, wsum[0], sel, key, active, prefix, rem, tid, lane, wave);
+        radix_pass<NT, PT, kShift1, kBins1, C1>(hist1, wsum[1], sel, key, active, prefix, rem, tid, lane, wave);
+        radix_pass<NT, PT, kShift2, kBins2, C2>(hist2, wsum[2], sel, key, active, prefix, rem, tid, lane, wave);
         const uint32_t T = prefix, budget = rem;
 
         // ---- emission in ascending column order
         uint32_t ngt = 0, neq = 0;
 #pragma unroll
-        for (int j = 0; j < kPerThread; ++j)
+        for (int j = 0; j < PT; ++j)
             if ((valid >> j) & 1u) {
                 ngt += key[j] > T ? 1u : 0u;
                 neq += key[j] == T ? 1u : 0u;
             }
         const uint32_t packed = ngt | (neq << 16);
-        const uint32_t excl = block_incl_scan(packed, wsum[3], lane, wave) - packed;
+        const uint32_t excl = block_incl_scan<NT>(packed, wsum[3], lane, wave) - packed;
         uint32_t gt_before = excl & 0xFFFFu, eq_before = excl >> 16;
-        // the selection is gathered in LDS (the first histogram is no longer
-        // needed) and then written to the row with contiguous stores
-        uint32_t* stage = hist0;
-        static_assert(kBins0 * kCopies0 >= kTopkMaxCols, "staging fits the first histogram");
+        // the selection is gathered in LDS (the first two histograms are no
+        // longer needed) and then written to the row with contiguous stores
+        uint32_t* stage = hist01;
 #pragma unroll
-        for (int j = 0; j < kPerThread; ++j) {
+        for (int j = 0; j < PT; ++j) {
             if (!((valid >> j) & 1u))
                 continue;
             // slots are < keff by construction; the bound only keeps a
@@ -242,10 +260,10 @@ __global__ __launch_bounds__(kThreads) void k_topk_rows(const float* __restrict_
             }
         }
         __syncthreads();
-        for (int i = tid; i < keff; i += kThreads)
+        for (int i = tid; i < keff; i += NT)
             orow[i] = (int32_t)stage[i];
     }
-    for (int i = keff + tid; i < topk; i += kThreads)
+    for (int i = keff + tid; i < topk; i += NT)
         orow[i] = -1;
 }
 
@@ -256,8 +274,12 @@ hipError_t launch_topk_rows(const float* scores, int64_t ld, int64_t rows, int64
                             int64_t ld_out, hipStream_t stream)
 {
     const int vec_ok = ((reinterpret_cast<uintptr_t>(scores) & 15u) == 0 && ld % 4 == 0) ? 1 : 0;
-    k_topk_rows<<<dim3((unsigned)rows), kThreads, 0, stream>>>(scores, ld, (int)cols, vec_ok, row_start, row_end,
-                                                               (int)topk, out, ld_out);
+    if (rows >= kTopkWideRows)
+        k_topk_rows<512><<<dim3((unsigned)rows), 512, 0, stream>>>(scores, ld, (int)cols, vec_ok, row_start,
+                                                                   row_end, (int)topk, out, ld_out);
+    else
+        k_topk_rows<1024><<<dim3((unsigned)rows), 1024, 0, stream>>>(scores, ld, (int)cols, vec_ok, row_start,
+                                                                     row_end, (int)topk, out, ld_out);
     return hipGetLastError();
 }
 
