@@ -51,9 +51,13 @@ def _load():
         lib.oracle_topk_rows.argtypes = [P, L, L, L, P, P, L, P, L]
         C = ctypes.c_int
         lib.oracle_moe_ex.argtypes = [P, P, P, P, P, L, L, L, L, L, C, C, C, C, P, P, P, P, P]
+        lib.oracle_moe_stages.argtypes = [P, P, P, P, P, L, L, L, L, L, C, C, C, C, P, P, P, P, P, P, P, P]
+        lib.oracle_moe_activation.argtypes = [P, P, L, L, C, C, P]
+        lib.oracle_moe_combine.argtypes = [P, P, L, L, L, C, C, P]
         for f in (lib.oracle_linear_f32, lib.oracle_linear_bf16, lib.oracle_topk,
                   lib.oracle_moe, lib.oracle_f64_to_bf16, lib.oracle_num_threads,
-                  lib.oracle_topk_rows, lib.oracle_moe_ex):
+                  lib.oracle_topk_rows, lib.oracle_moe_ex, lib.oracle_moe_stages, lib.oracle_moe_activation,
+                  lib.oracle_moe_combine):
             f.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -207,6 +211,71 @@ def moe_ex(x, w_router, b_router, w1, w2, topk, act=ACT_SWIGLU, probs_at_act=Tru
     if rc:
         raise ValueError("oracle_moe_ex rejected its arguments")
     return y, ids_out, probs, logits
+
+
+def moe_stages(x, w_router, b_router, w1, w2, topk, act=ACT_SWIGLU, probs_at_act=True, apply_weights=False,
+               acc_fp64=True, ids=None):
+    """moe_ex() plus the layer's storage points per (token, slot) pair:
+    returns (y, ids, probs, logits, h, a, part) with h uint16 [M, topk,
+    rows of w1[e]] (first projection, bf16), a uint16 [M, topk, I]
+    (activation, bf16) and part float64 [M, topk, H] (down projection of
+    the slot, before any weight)."""
+    x = _c(x, np.uint16)
+    w_router = _c(w_router, np.float32)
+    b_router = _c(b_router, np.float32)
+    w1 = _c(w1, np.uint16)
+    w2 = _c(w2, np.uint16)
+    M, H = x.shape
+    E, H2 = w_router.shape
+    E2, R1, H3 = w1.shape
+    E3, H4, I = w2.shape
+    assert H == H2 == H3 == H4 and E == E2 == E3 and R1 == (2 * I if act == ACT_SWIGLU else I)
+    ids_in = _c(ids, np.int32)
+    if ids_in is not None:
+        assert ids_in.shape == (M, topk)
+    y = np.empty((M, H), np.float32)
+    ids_out = np.empty((M, topk), np.int32)
+    probs = np.empty((M, topk), np.float64)
+    logits = np.empty((M, E), np.float32)
+    h = np.empty((M, topk, R1), np.uint16)
+    a = np.empty((M, topk, I), np.uint16)
+    part = np.empty((M, topk, H), np.float64)
+    rc = _load().oracle_moe_stages(_ptr(x), _ptr(w_router), _ptr(b_router), _ptr(w1), _ptr(w2),
+                                   M, H, E, I, topk, int(act), int(bool(probs_at_act)), int(bool(apply_weights)),
+                                   int(bool(acc_fp64)), _ptr(ids_in), _ptr(logits), _ptr(ids_out),
+                                   _ptr(probs), _ptr(y), _ptr(h), _ptr(a), _ptr(part))
+    if rc:
+        raise ValueError("oracle_moe_stages rejected its arguments")
+    return y, ids_out, probs, logits, h, a, part
+
+
+def moe_activation(h, p, act=ACT_SWIGLU, probs_at_act=True):
+    """The MoE layer's activation step alone: h uint16 [P, 2I] (SwiGLU, gate
+    half first) or [P, I] (squared-ReLU) bf16 first-projection outputs, p
+    float64 [P]; returns a uint16 [P, I] = RN_bf16(act(h) * (p or 1))."""
+    h = _c(h, np.uint16)
+    p = _c(np.asarray(p, np.float64), np.float64)
+    P, R = h.shape
+    I = R // 2 if act == ACT_SWIGLU else R
+    assert p.shape == (P,)
+    a = np.empty((P, I), np.uint16)
+    if _load().oracle_moe_activation(_ptr(h), _ptr(p), P, I, int(act), int(bool(probs_at_act)), _ptr(a)):
+        raise ValueError("oracle_moe_activation rejected its arguments")
+    return a
+
+
+def moe_combine(part, p, apply_weights=False, acc_fp64=True):
+    """The MoE layer's top-k sum alone: part float64 [M, topk, H] slot values,
+    p float64 [M, topk]; returns float32 [M, H]."""
+    part = _c(np.asarray(part, np.float64), np.float64)
+    p = _c(np.asarray(p, np.float64), np.float64)
+    M, k, H = part.shape
+    assert p.shape == (M, k)
+    y = np.empty((M, H), np.float32)
+    if _load().oracle_moe_combine(_ptr(part), _ptr(p), M, k, H, int(bool(apply_weights)), int(bool(acc_fp64)),
+                                  _ptr(y)):
+        raise ValueError("oracle_moe_combine rejected its arguments")
+    return y
 
 
 def f64_to_bf16(v):

@@ -337,12 +337,97 @@ int oracle_topk_rows(const float* scores, long ld, long rows, long cols,
  * and the (apply_weights, acc_fp64) matrix of the top-k sum, whose (false,
  * false) point must apply no weights) are independent switches here.
  */
-int oracle_moe_ex(const uint16_t* x, const float* wr, const float* br,
-                  const uint16_t* w1, const uint16_t* w2,
-                  long M, long H, long E, long I, long topk,
-                  int act, int probs_at_act, int apply_weights, int acc_fp64,
-                  const int32_t* ids_in, float* logits_out, int32_t* ids_out,
-                  double* probs_out, float* y)
+/* Step 5 for one (token, slot) pair: a[i] = RN_bf16(act_i(h) * q) in
+ * binary64, q = p when the probability is applied at the activation, else 1.
+ * h holds the bf16 storage point of step 4 widened to binary64; act 1 is
+ * SwiGLU on the gate|up halves, act 2 squared-ReLU. */
+static void moe_activation_row(const double* h, long I, int act, double q, uint16_t* a)
+{
+    for (long i = 0; i < I; ++i) {
+        double v;
+        if (act == 1) {
+            double g = h[i], u = h[I + i];
+            double sg = 1.0 / (1.0 + exp(-g));
+            v = (g * sg) * u;
+        } else {
+            double r = h[i] > 0.0 ? h[i] : 0.0;
+            v = r * r;
+        }
+        a[i] = f64_to_bf16(v * q);
+    }
+}
+
+/* Step 7 for one output element of one token: the slot-order sum of the
+ * slot values s[j] (binary64 y_j), weighted by p[j] when apply_weights. */
+static float moe_combine_elem(const double* s, const double* p, long topk, long stride, int apply_weights,
+                              int acc_fp64)
+{
+    double acc = 0.0;
+    float acc32 = 0.0f;
+    for (long j = 0; j < topk; ++j) {
+        const double v = s[j * stride];
+        if (acc_fp64) {
+            acc += apply_weights ? p[j] * v : v;
+        } else {
+            const double part = (double)f64_to_f32(v);
+            const double t = apply_weights ? (double)f64_to_f32((double)f64_to_f32(p[j]) * part) : part;
+            acc32 = f64_to_f32((double)acc32 + t);
+        }
+    }
+    return acc_fp64 ? f64_to_f32(acc) : acc32;
+}
+
+/* Step 5 alone, for P pairs: h [P, rows1] bf16 (rows1 = 2I for SwiGLU, I for
+ * squared-ReLU), p [P] binary64, a [P, I] bf16 out. */
+int oracle_moe_activation(const uint16_t* h, const double* p, long P, long I, int act, int probs_at_act,
+                          uint16_t* a)
+{
+    if (P < 0 || I <= 0 || (act != 1 && act != 2) || (P > 0 && (!h || !p || !a)))
+        return -1;
+    const long rows1 = act == 1 ? 2 * I : I;
+    int bad = 0;
+#pragma omp parallel for schedule(static) reduction(| : bad)
+    for (long r = 0; r < P; ++r) {
+        double* hv = (double*)malloc(sizeof(double) * (size_t)rows1);
+        if (!hv) {
+            bad = 1;
+            continue;
+        }
+        for (long c = 0; c < rows1; ++c)
+            hv[c] = bf16_to_f64(h[r * rows1 + c]);
+        moe_activation_row(hv, I, act, probs_at_act ? p[r] : 1.0, a + r * I);
+        free(hv);
+    }
+    return bad ? -1 : 0;
+}
+
+/* Step 7 alone: part [M, topk, H] binary64 slot values, p [M, topk]
+ * binary64, y [M, H] fp32 out. */
+int oracle_moe_combine(const double* part, const double* p, long M, long topk, long H, int apply_weights,
+                       int acc_fp64, float* y)
+{
+    if (M < 0 || topk <= 0 || H <= 0 || (M > 0 && (!part || !p || !y)))
+        return -1;
+#pragma omp parallel for schedule(static)
+    for (long m = 0; m < M; ++m)
+        for (long c = 0; c < H; ++c)
+            y[m * H + c] = moe_combine_elem(part + m * topk * H + c, p + m * topk, topk, H, apply_weights,
+                                            acc_fp64);
+    return 0;
+}
+
+/* The same layer, also returning its storage points per (token, slot) pair
+ * m * topk + j (each output may be NULL):
+ *   h_out     [M, topk, rows1] bf16 bit patterns of step 4
+ *   a_out     [M, topk, I]     bf16 bit patterns of step 5
+ *   part_out  [M, topk, H]     binary64 y_j of step 6 (before any weight)   */
+int oracle_moe_stages(const uint16_t* x, const float* wr, const float* br,
+                      const uint16_t* w1, const uint16_t* w2,
+                      long M, long H, long E, long I, long topk,
+                      int act, int probs_at_act, int apply_weights, int acc_fp64,
+                      const int32_t* ids_in, float* logits_out, int32_t* ids_out,
+                      double* probs_out, float* y,
+                      uint16_t* h_out, uint16_t* a_out, double* part_out)
 {
     if (M < 0 || H <= 0 || E <= 0 || I <= 0 || topk <= 0 || topk > E)
         return -1;
@@ -360,10 +445,10 @@ int oracle_moe_ex(const uint16_t* x, const float* wr, const float* br,
         float* l = (float*)malloc(sizeof(float) * (size_t)E);
         double* h = (double*)malloc(sizeof(double) * (size_t)rows1);
         double* a = (double*)malloc(sizeof(double) * (size_t)I);
-        double* acc = (double*)calloc((size_t)H, sizeof(double));
-        float* acc32 = (float*)calloc((size_t)H, sizeof(float));
+        uint16_t* ab = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)I);
+        double* ys = (double*)malloc(sizeof(double) * (size_t)(topk * H));
         int32_t* ids = ids_out + m * topk;
-        if (!l || !h || !a || !acc || !acc32) {
+        if (!l || !h || !a || !ab || !ys) {
             bad = 1;
             goto done;
         }
@@ -409,47 +494,50 @@ int oracle_moe_ex(const uint16_t* x, const float* wr, const float* br,
                 double s = 0.0;
                 for (long k = 0; k < H; ++k)
                     s += bf16_to_f64(xm[k]) * bf16_to_f64(w1e[c * H + k]);
-                h[c] = bf16_to_f64(f64_to_bf16(s));
+                const uint16_t hb = f64_to_bf16(s);
+                h[c] = bf16_to_f64(hb);
+                if (h_out)
+                    h_out[(m * topk + j) * rows1 + c] = hb;
             }
             /* 5. activation (probability applied here or not), bf16 storage point */
-            const double q = probs_at_act ? p : 1.0;
-            for (long i = 0; i < I; ++i) {
-                double v;
-                if (act == 1) {
-                    double g = h[i], u = h[I + i];
-                    double sg = 1.0 / (1.0 + exp(-g));
-                    v = (g * sg) * u;
-                } else {
-                    double r = h[i] > 0.0 ? h[i] : 0.0;
-                    v = r * r;
-                }
-                a[i] = bf16_to_f64(f64_to_bf16(v * q));
-            }
-            /* 6.+7. down projection, combined over slots in slot order */
+            moe_activation_row(h, I, act, probs_at_act ? p : 1.0, ab);
+            for (long i = 0; i < I; ++i)
+                a[i] = bf16_to_f64(ab[i]);
+            if (a_out)
+                memcpy(a_out + (m * topk + j) * I, ab, sizeof(uint16_t) * (size_t)I);
+            /* 6. down projection of the slot */
             const uint16_t* w2e = w2 + e * H * I;
             for (long c = 0; c < H; ++c) {
                 double s = 0.0;
                 for (long i = 0; i < I; ++i)
                     s += a[i] * bf16_to_f64(w2e[c * I + i]);
-                if (acc_fp64) {
-                    acc[c] += apply_weights ? p * s : s;
-                } else {
-                    const double part = (double)f64_to_f32(s);
-                    const double t = apply_weights ? (double)f64_to_f32((double)f64_to_f32(p) * part) : part;
-                    acc32[c] = f64_to_f32((double)acc32[c] + t);
-                }
+                ys[j * H + c] = s;
             }
         }
+        if (part_out)
+            memcpy(part_out + m * topk * H, ys, sizeof(double) * (size_t)(topk * H));
+        /* 7. combine over slots in slot order */
         for (long c = 0; c < H; ++c)
-            y[m * H + c] = acc_fp64 ? f64_to_f32(acc[c]) : acc32[c];
+            y[m * H + c] = moe_combine_elem(ys + c, probs_out + m * topk, topk, H, apply_weights, acc_fp64);
     done:
         free(l);
         free(h);
         free(a);
-        free(acc);
-        free(acc32);
+        free(ab);
+        free(ys);
     }
     return bad ? -1 : 0;
+}
+
+int oracle_moe_ex(const uint16_t* x, const float* wr, const float* br,
+                  const uint16_t* w1, const uint16_t* w2,
+                  long M, long H, long E, long I, long topk,
+                  int act, int probs_at_act, int apply_weights, int acc_fp64,
+                  const int32_t* ids_in, float* logits_out, int32_t* ids_out,
+                  double* probs_out, float* y)
+{
+    return oracle_moe_stages(x, wr, br, w1, w2, M, H, E, I, topk, act, probs_at_act, apply_weights, acc_fp64,
+                             ids_in, logits_out, ids_out, probs_out, y, NULL, NULL, NULL);
 }
 
 /* The gated layer with the probability at the activation and an unweighted
