@@ -94,12 +94,15 @@ def main():
     ap.add_argument("--no-bf16", action="store_true")
     ap.add_argument("--no-moe", action="store_true")
     ap.add_argument("--no-topk", action="store_true")
-    ap.add_argument("--mode", choices=("step", "copy"), default="step",
+    ap.add_argument("--mode", choices=("step", "copy", "cpu-leg"), default="step",
                     help="copy: one 512 MiB device-to-device copy, the known-size kernel that "
-                         "scales the PMC byte counters")
+                         "scales the PMC byte counters; cpu-leg: time the oracle (child process)")
+    ap.add_argument("--seconds", type=float, default=10.0)
     args = ap.parse_args()
     if args.mode == "copy":
         return copy_calibration()
+    if args.mode == "cpu-leg":
+        return cpu_leg(args.seconds)
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
                           "n_gpus": args.gpus}))
@@ -159,17 +162,36 @@ def main():
         calls = [lambda M=M, wd=wd: bi.bi_linear_f32(xs[M], wd.t(), bias, out=outs[M]) for wd in copies]
         us = time_graph_calls(torch, calls, stream)
         t = us * 1e-6
+        t_hbm = router_bytes(M) / (HBM_PEAK_GBS * 1e9)
+        t_mfma = router_flops(M) / (FP32_MFMA_PEAK_TFLOPS * 1e12)
         per_m[str(M)] = {
             "us": round(us, 3),
             "GBps": round(router_bytes(M) / t / 1e9, 1),
             "TFLOPs": round(router_flops(M) / t / 1e12, 2),
             "hbm_frac": round(router_bytes(M) / t / 1e9 / HBM_PEAK_GBS, 4),
+            "mfma_frac": round(router_flops(M) / t / 1e12 / FP32_MFMA_PEAK_TFLOPS, 4),
+            # which peak binds an ideal kernel at this M (fp32 MFMA from M = 64)
+            "bound": "hbm" if t_hbm >= t_mfma else "mfma",
+            "path": decode_path_name(bi, M),
         }
     achieved = bytes_step / (ms_per_step * 1e-3) / 1e9
+    floors = floors_leg(torch, bi, dev)
+    # the dominant kernel: the one-launch XCD hand-over decode, which serves
+    # the sweep's small batches; algorithmic bytes per call over its average
+    # per-call duration, both averaged over the calls it serves
+    xcd_m = [M for M in sweep if per_m[str(M)]["path"] == "decode_xcd"]
+    dom = None
+    if xcd_m:
+        dom_us = sum(per_m[str(M)]["us"] for M in xcd_m) / len(xcd_m)
+        dom_bytes = sum(router_bytes(M) for M in xcd_m) / len(xcd_m)
+        dom = {"kernel": "k_decode<F32,F32,4,1,HANDOFF> (XCD hand-over decode, one launch per call)",
+               "M": xcd_m, "us": round(dom_us, 3), "bytes": int(dom_bytes),
+               "GBps": round(dom_bytes / dom_us / 1e3, 1)}
 
     extra = {"decode_per_M": per_m, "weight": f"cold: {N_COPIES} rotating copies of W (384 MiB)",
              "timing": "HIP graph replay; events bracket only the timed replays",
-             "event_pair_floor_us": round(event_pair_floor(torch, stream), 2)}
+             "event_pair_floor_us": round(event_pair_floor(torch, stream), 2),
+             "floors": floors, "step_GBps": round(achieved, 1)}
 
     if not args.no_prefill:
         extra["prefill"] = prefill_leg(torch, np, bi, wl, w, copies, bias, dev)
@@ -183,7 +205,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(np, wl, w, sweep)
+        cpu = cpu_baseline(sweep)
 
     line = {
         "metric": "router GateLinear fp32 GEMM, decode sweep M=1..128: HBM GB/s (bit-invariant)",
@@ -201,12 +223,7 @@ def main():
         "config": {"workload": "DSv4 router GateLinear fp32, X[M,4096] W[256,4096] (weight.t()) + bias, "
                                "decode sweep M in {1,2,4,8,15,16,17,32,33,64,128}",
                    "sweep": sweep, "N": 256, "K": 4096},
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": (MEASURED_TRAFFIC["bytes_per_call"]
-                                 if kernel_sources_digest() == MEASURED_TRAFFIC["sources_sha256"] else None),
-                     "kernel": "decode call = k_decode (k-tile partials) + k_decode_fold, "
-                               "average over the sweep's calls (step time / calls per step)"},
+        "roofline": roofline_line(dom, achieved, floors),
         "cpu_baseline": cpu,
         "extra": extra,
     }
@@ -374,9 +391,13 @@ def copy_calibration():
     print(json.dumps({"copy_bytes": 4 * n, "ok": bool(b[-1].item() == 1.0)}))
 
 
-def cpu_baseline(np, wl, w, sweep):
-    """The fp64 oracle as it stands, on the decode sweep, on the host cores."""
+def cpu_leg(seconds):
+    """Child process: the fp64 oracle as it stands on the decode sweep for about
+    `seconds` seconds, with whatever OMP_NUM_THREADS the parent set."""
     import oracle
+    import workloads as wl
+    w = wl.router_weights(0)
+    sweep = list(wl.ROUTER_DECODE_M)
     batches = {M: wl.router_batch(M, w).x for M in sweep}
     reps = 0
     t0 = time.perf_counter()
@@ -384,14 +405,116 @@ def cpu_baseline(np, wl, w, sweep):
         for M in sweep:
             oracle.linear_f32(batches[M], w.w, w.b)
         reps += 1
-        if time.perf_counter() - t0 > 10.0:
+        if time.perf_counter() - t0 > seconds:
             break
     dt = time.perf_counter() - t0
-    bytes_step = sum(router_bytes(M) for M in sweep)
-    return {"value": round(bytes_step * reps / dt / 1e9, 3), "unit": "GB/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
-            "sample": f"{reps} passes of the decode sweep (M=1..128, N=256, K=4096), fp64 C oracle, "
-                      f"{dt:.1f} s"}
+    print(json.dumps({"reps": reps, "seconds": dt, "threads": oracle.num_threads(),
+                      "GBps": sum(router_bytes(M) for M in sweep) * reps / dt / 1e9}))
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_baseline(sweep, seconds=10.0):
+    """The fp64 oracle on the decode sweep, timed on the host cores in child
+    processes: at OMP_NUM_THREADS=1 and at the thread count the environment
+    sets (all host CPUs when it sets none)."""
+    import subprocess
+    runs = {}
+    for label, threads in (("multi", os.environ.get("OMP_NUM_THREADS") or str(os.cpu_count())), ("one", "1")):
+        env = dict(os.environ, OMP_NUM_THREADS=threads)
+        out = subprocess.run([sys.executable, os.path.abspath(__file__), "--mode", "cpu-leg",
+                              "--seconds", str(seconds)], env=env, capture_output=True, text=True, check=True)
+        runs[label] = json.loads(out.stdout.strip().splitlines()[-1])
+    m, o = runs["multi"], runs["one"]
+    return {"value": round(m["GBps"], 3), "unit": "GB/s", "cores": m["threads"], "kind": "oracle",
+            "sample": f"{m['reps']} passes of the decode sweep (M in {sweep}, N=256, K=4096), fp64 C oracle, "
+                      f"{m['seconds']:.1f} s on {m['threads']} threads",
+            "value_1_thread": round(o["GBps"], 3),
+            "sample_1_thread": f"{o['reps']} passes, {o['seconds']:.1f} s on 1 thread",
+            "host_cpus": os.cpu_count(), "cpu_model": cpu_model()}
+
+
+def decode_path_name(bi, M, N=256, K=4096):
+    """Which decode kernel the automatic plan picks for M rows of the router."""
+    return {bi.BI_PATH_DECODE: "decode_two_launch", bi.BI_PATH_DECODE_XCD: "decode_xcd",
+            bi.BI_PATH_PERSISTENT: "persistent", bi.BI_PATH_DECODE_WG: "decode_wg",
+            bi.BI_PATH_DECODE_DMA: "decode_dma"}.get(bi.plan_path(bi.BI_F32, M, N, K), "?")
+
+
+def floors_leg(torch, bi, dev):
+    """What a launch and a cold read cost on this part, and the shader clock.
+    Empty kernel: 512 workgroups, per launch in a replayed graph of 100
+    launches (one or two per group).  Cold reads: 4 MiB (96 copies) and
+    32 MiB (12 copies) read once each by a plain streaming kernel (256 and 512
+    workgroups of 256 threads, the fastest measured).  Clock: shader cycles
+    (s_memtime) per 100 MHz wall tick over a dependent fp32 chain, with one
+    wave per compute unit and with eight."""
+    stream = torch.cuda.Stream(dev)
+    res = {}
+    one = time_graph_calls(torch, [lambda: bi.bi_lab_empty(512)] * 100, stream)
+    two = time_graph_calls(torch, [lambda: (bi.bi_lab_empty(512), bi.bi_lab_empty(512))] * 50, stream)
+    res["empty_kernel_us"] = round(one, 3)
+    res["two_empty_kernels_us"] = round(two, 3)
+    for mib, ncopy, grid in ((4, 96, 256), (32, 12, 512)):
+        nb = mib << 20
+        bufs = [torch.ones(nb // 4, dtype=torch.float32, device=dev) for _ in range(ncopy)]
+        sink = torch.empty(grid, dtype=torch.int32, device=dev)
+        us = time_graph_calls(torch, [lambda b=b: bi.bi_lab_stream_read(b, sink, grid) for b in bufs], stream)
+        res[f"cold_read_{mib}MiB"] = {"us": round(us, 3), "GBps": round(nb / us / 1e3, 1), "workgroups": grid}
+        del bufs
+    out = torch.zeros((2048, 3), dtype=torch.int64, device=dev)
+    for grid, name in ((256, "sclk_MHz_one_wave_per_CU"), (2048, "sclk_MHz_eight_waves_per_CU")):
+        with torch.cuda.stream(stream):
+            bi.bi_lab_clock(out, grid, 2000)
+        torch.cuda.synchronize()
+        o = out[:grid].cpu().numpy().astype("float64")
+        res[name] = round(float(sorted(o[:, 0] / o[:, 1])[grid // 2] * 100.0), 1)
+    res["smi_sclk"] = smi_sclk()
+    return res
+
+
+def smi_sclk():
+    """The current shader clock as rocm-smi reports it (None if unavailable)."""
+    import subprocess
+    try:
+        out = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=20)
+        data = json.loads(out.stdout)
+        for card in data.values():
+            for k, v in card.items():
+                if "sclk" in k.lower():
+                    return v
+    except Exception:
+        return None
+    return None
+
+
+def roofline_line(dom, step_gbps, floors):
+    """The roofline object for the dominant kernel: algorithmic bytes per call
+    of the one-launch decode over its average duration, against the 8 TB/s
+    HBM peak and, for context, against what a plain kernel reading the same
+    4 MiB cold achieves here."""
+    cold = floors["cold_read_4MiB"]["GBps"]
+    traffic = (MEASURED_TRAFFIC["bytes_per_call"]
+               if kernel_sources_digest() == MEASURED_TRAFFIC["sources_sha256"] else None)
+    if dom is None:
+        return {"bound": "hbm", "achieved": round(step_gbps, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(step_gbps / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "kernel": "decode calls, average over the sweep"}
+    return {"bound": "hbm", "achieved": dom["GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(dom["GBps"] / HBM_PEAK_GBS, 4), "traffic": traffic,
+            "kernel": dom["kernel"], "calls": dom["M"], "us_per_call": dom["us"],
+            "algorithmic_bytes_per_call": dom["bytes"],
+            "frac_vs_cold_read_4MiB": round(dom["GBps"] / cold, 4),
+            "launch_floor_us": floors["empty_kernel_us"]}
 
 
 if __name__ == "__main__":

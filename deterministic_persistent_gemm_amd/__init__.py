@@ -23,7 +23,11 @@ LIB_PATH = os.path.join(_PKG, "libbi.so")
 
 BI_OK, BI_EINVAL, BI_EUNSUPPORTED, BI_EWORKSPACE, BI_EHIP = range(5)
 BI_F32, BI_BF16 = 0, 1
-BI_PATH_AUTO, BI_PATH_DECODE, BI_PATH_PERSISTENT, BI_PATH_DECODE_WG, BI_PATH_DECODE_DMA = 0, 1, 2, 3, 4
+BI_PATH_AUTO, BI_PATH_DECODE, BI_PATH_PERSISTENT, BI_PATH_DECODE_WG, BI_PATH_DECODE_DMA, BI_PATH_DECODE_XCD = (
+    0, 1, 2, 3, 4, 5)
+# bytes at the start of every workspace that hold the one-launch decode's
+# arrival counters (zero at first use; every call leaves them zero)
+WS_COUNTER_BYTES = 16384
 BI_R2_TILE_PARTIAL = 2
 BI_MFMA_F32_16X16X4_F32, BI_MFMA_F32_16X16X32_BF16 = 1, 2
 
@@ -57,9 +61,16 @@ _lib.bi_status_str.argtypes = [_I32]
 _lib.bi_indexer_topk.argtypes = [_P, _I64, _I64, _I64, _P, _P, _I64, _P, _I64, _P]
 _lib.bi_moe_grouped_gemm_ex.argtypes = [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _P, _P, _P, _P,
                                         _P, _SZ, _P]
+_lib.bi_lab_xcc_ids.argtypes = [_P, _I32, _I32, _P]
+_lib.bi_lab_empty.argtypes = [_I32, _I32, _P]
+_lib.bi_lab_stream_read.argtypes = [_P, _I64, _P, _I32, _P]
+_lib.bi_lab_clock.argtypes = [_P, _I32, _I32, _P]
+_lib.bi_lab_plan.argtypes = [_I32, _I64, _I64, _I64, ctypes.POINTER(_I32)]
+_lib.bi_lab_moe_layout.argtypes = [_I64, _I64, _I64, _I64, _I64, ctypes.POINTER(_I64)]
 for _f in (_lib.bi_linear_f32, _lib.bi_linear_bf16, _lib.bi_negctl_linear_f32, _lib.bi_lab_linear,
            _lib.bi_moe_grouped_gemm, _lib.bi_describe_recipe, _lib.bi_indexer_topk,
-           _lib.bi_moe_grouped_gemm_ex):
+           _lib.bi_moe_grouped_gemm_ex, _lib.bi_lab_xcc_ids, _lib.bi_lab_empty, _lib.bi_lab_stream_read,
+           _lib.bi_lab_clock, _lib.bi_lab_plan, _lib.bi_lab_moe_layout):
     _f.restype = _I32
 for _f in (_lib.bi_linear_workspace_size, _lib.bi_lab_workspace_size, _lib.bi_moe_workspace_size):
     _f.restype = _SZ
@@ -81,18 +92,43 @@ def _check(status: int, where: str):
 
 _ws_lock = threading.Lock()
 _ws_cache: dict = {}
+# Workspaces replaced by larger ones.  They are never freed: a HIP graph
+# captured while one of them was current keeps its address and writes there on
+# every replay, so releasing it to the caching allocator could hand that memory
+# to another tensor.
+_ws_retired: list = []
 
 
-def _workspace(nbytes: int, device: torch.device, stream: torch.cuda.Stream) -> torch.Tensor | None:
-    """Grow-only workspace per (device, stream); the library needs it only
-    for intermediate partials, so it is reused as is between calls."""
+def alloc_workspace(nbytes: int, device) -> torch.Tensor:
+    """A zero-filled workspace of at least `nbytes` bytes (the first
+    WS_COUNTER_BYTES hold counters that must be zero at first use)."""
+    return torch.zeros(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+def _workspace(nbytes: int, device: torch.device, stream: torch.cuda.Stream,
+               given: torch.Tensor | None = None) -> torch.Tensor | None:
+    """The caller's workspace if one is given (checked), else a grow-only
+    workspace cached per (device, stream).  Growing it inside a graph capture
+    is refused: run the call once eagerly at the largest shape first, or pass
+    `ws=` explicitly."""
+    if given is not None:
+        if given.dtype != torch.uint8 or given.dim() != 1 or not given.is_contiguous() or given.device != device:
+            raise ValueError(f"ws must be a contiguous 1-D uint8 tensor on {device}")
+        if given.numel() < nbytes:
+            raise ValueError(f"ws holds {given.numel()} bytes; this call needs {nbytes}")
+        return given
     if nbytes == 0:
         return None
     key = (device.index, stream.cuda_stream)
     with _ws_lock:
         ws = _ws_cache.get(key)
         if ws is None or ws.numel() < nbytes:
-            ws = torch.empty(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
+            if torch.cuda.is_current_stream_capturing():
+                raise RuntimeError("the cached workspace must grow during a graph capture; call once eagerly "
+                                   "at the largest shape before capturing, or pass ws=")
+            if ws is not None:
+                _ws_retired.append(ws)
+            ws = alloc_workspace(max(nbytes, 1 << 20, 0 if ws is None else 2 * ws.numel()), device)
             _ws_cache[key] = ws
         return ws
 
@@ -120,6 +156,19 @@ def _check_xw(x: torch.Tensor, wt: torch.Tensor, dtype: torch.dtype, name: str):
         raise ValueError(f"{name}: wt must be the weight.t() view of an [N, K] weight (wt.stride(0) == 1)")
 
 
+def _check_out(out, shape, dtypes, device, name):
+    """A caller-supplied output: on the inputs' GPU, of the call's shape and
+    dtype, unit column stride and a row pitch of at least its width."""
+    if not isinstance(out, torch.Tensor) or not out.is_cuda or out.device != device:
+        raise ValueError(f"{name}: out must be a tensor on {device}")
+    if out.dtype not in dtypes:
+        raise TypeError(f"{name}: out must be one of {dtypes}, got {out.dtype}")
+    if tuple(out.shape) != tuple(shape):
+        raise ValueError(f"{name}: out must have shape {tuple(shape)}, got {tuple(out.shape)}")
+    if out.dim() != 2 or out.stride(1) != 1 or (shape[0] > 1 and out.stride(0) < shape[1]):
+        raise ValueError(f"{name}: out must have unit column stride and a row pitch >= {shape[1]}")
+
+
 def _check_bias(bias, N, device, name):
     if bias is None:
         return
@@ -131,17 +180,19 @@ def _check_bias(bias, N, device, name):
 
 
 def bi_linear_f32(x: torch.Tensor, wt: torch.Tensor, bias: torch.Tensor | None = None,
-                  out: torch.Tensor | None = None) -> torch.Tensor:
-    """y = x @ wt + bias in fp32, batch-invariant.  x [M, K], wt = weight.t() [K, N]."""
+                  out: torch.Tensor | None = None, ws: torch.Tensor | None = None) -> torch.Tensor:
+    """y = x @ wt + bias in fp32, batch-invariant.  x [M, K], wt = weight.t() [K, N].
+    ws: optional caller-owned workspace (alloc_workspace), else a cached one."""
     _check_xw(x, wt, torch.float32, "bi_linear_f32")
     M, K = x.shape
     N = wt.shape[1]
     _check_bias(bias, N, x.device, "bi_linear_f32")
     if out is None:
         out = torch.empty((M, N), dtype=torch.float32, device=x.device)
+    _check_out(out, (M, N), (torch.float32,), x.device, "bi_linear_f32")
     s = _stream(x.device)
     nbytes = _lib.bi_linear_workspace_size(BI_F32, M, N, K)
-    ws = _workspace(nbytes, x.device, s)
+    ws = _workspace(nbytes, x.device, s, ws)
     _check(_lib.bi_linear_f32(_ptr(x), x.stride(0), _ptr(wt), wt.stride(1), _ptr(bias), _ptr(out),
                               out.stride(0), M, N, K, _ptr(ws), 0 if ws is None else ws.numel(),
                               ctypes.c_void_p(s.cuda_stream)), "bi_linear_f32")
@@ -149,7 +200,8 @@ def bi_linear_f32(x: torch.Tensor, wt: torch.Tensor, bias: torch.Tensor | None =
 
 
 def bi_linear_bf16(x: torch.Tensor, wt: torch.Tensor, bias: torch.Tensor | None = None,
-                   out_dtype: torch.dtype = torch.bfloat16, out: torch.Tensor | None = None) -> torch.Tensor:
+                   out_dtype: torch.dtype = torch.bfloat16, out: torch.Tensor | None = None,
+                   ws: torch.Tensor | None = None) -> torch.Tensor:
     """y = x @ wt + bias with bf16 operands, fp32 accumulation, bf16 or fp32 out."""
     _check_xw(x, wt, torch.bfloat16, "bi_linear_bf16")
     M, K = x.shape
@@ -159,9 +211,10 @@ def bi_linear_bf16(x: torch.Tensor, wt: torch.Tensor, bias: torch.Tensor | None 
         raise ValueError("out_dtype must be bfloat16 or float32")
     if out is None:
         out = torch.empty((M, N), dtype=out_dtype, device=x.device)
+    _check_out(out, (M, N), (torch.bfloat16, torch.float32), x.device, "bi_linear_bf16")
     s = _stream(x.device)
     nbytes = _lib.bi_linear_workspace_size(BI_BF16, M, N, K)
-    ws = _workspace(nbytes, x.device, s)
+    ws = _workspace(nbytes, x.device, s, ws)
     _check(_lib.bi_linear_bf16(_ptr(x), x.stride(0), _ptr(wt), wt.stride(1), _ptr(bias), _ptr(out),
                                BI_BF16 if out.dtype == torch.bfloat16 else BI_F32, out.stride(0), M, N, K,
                                _ptr(ws), 0 if ws is None else ws.numel(), ctypes.c_void_p(s.cuda_stream)),
@@ -177,6 +230,7 @@ def bi_negctl_linear_f32(x, wt, bias=None, out=None):
     _check_bias(bias, N, x.device, "bi_negctl_linear_f32")
     if out is None:
         out = torch.empty((M, N), dtype=torch.float32, device=x.device)
+    _check_out(out, (M, N), (torch.float32,), x.device, "bi_negctl_linear_f32")
     s = _stream(x.device)
     ws = _workspace(_lib.bi_linear_workspace_size(BI_F32, M, N, K), x.device, s)
     _check(_lib.bi_negctl_linear_f32(_ptr(x), x.stride(0), _ptr(wt), wt.stride(1), _ptr(bias), _ptr(out),
@@ -204,6 +258,7 @@ def bi_lab_linear(x, wt, bias=None, recipe: Recipe | None = None, path: int = BI
     out_dtype = out_dtype or (torch.float32 if dt == torch.float32 else torch.bfloat16)
     if out is None:
         out = torch.empty((M, N), dtype=out_dtype, device=x.device)
+    _check_out(out, (M, N), (torch.float32, torch.bfloat16), x.device, "bi_lab_linear")
     s = _stream(x.device)
     ws = _workspace(_lib.bi_lab_workspace_size(ctypes.byref(recipe), path, M, N, K), x.device, s)
     _check(_lib.bi_lab_linear(_ptr(x), x.stride(0), _ptr(wt), wt.stride(1), _ptr(bias), _ptr(out),
@@ -222,24 +277,24 @@ class MoEOptions(ctypes.Structure):
 BI_ACT_SWIGLU, BI_ACT_SQRELU = 0, 1
 
 
-def bi_moe_grouped_gemm(x, w_router, b_router, w13, w2, topk: int):
+def bi_moe_grouped_gemm(x, w_router, b_router, w13, w2, topk: int, ws=None):
     """Batch-invariant MoE layer.  Returns (y fp32 [M,H], topk_ids int32 [M,topk],
     topk_probs fp32 [M,topk]).  w13 [E, 2I, H] and w2 [E, H, I] are the experts'
     nn.Linear weights (their .t() views are what the GEMMs consume)."""
-    return _moe(x, w_router, b_router, w13, w2, topk, None, "bi_moe_grouped_gemm")
+    return _moe(x, w_router, b_router, w13, w2, topk, None, "bi_moe_grouped_gemm", ws)
 
 
 def bi_moe_grouped_gemm_ex(x, w_router, b_router, w1, w2, topk: int, activation: int = BI_ACT_SWIGLU,
                            probs_at_activation: bool = True, apply_weights: bool = False,
-                           acc_fp64: bool = True):
+                           acc_fp64: bool = True, ws=None):
     """The MoE layer with explicit activation and top-k-sum options.  SwiGLU:
     w1 [E, 2I, H]; squared-ReLU: w1 [E, I, H].  Same returns."""
     opt = MoEOptions(int(activation), int(bool(probs_at_activation)), int(bool(apply_weights)),
                      int(bool(acc_fp64)))
-    return _moe(x, w_router, b_router, w1, w2, topk, opt, "bi_moe_grouped_gemm_ex")
+    return _moe(x, w_router, b_router, w1, w2, topk, opt, "bi_moe_grouped_gemm_ex", ws)
 
 
-def _moe(x, w_router, b_router, w1, w2, topk, opt, name):
+def _moe(x, w_router, b_router, w1, w2, topk, opt, name, ws_given=None):
     if x.dtype != torch.bfloat16 or w1.dtype != torch.bfloat16 or w2.dtype != torch.bfloat16:
         raise TypeError(f"{name}: x, w1, w2 must be bfloat16")
     if w_router.dtype != torch.float32:
@@ -258,7 +313,7 @@ def _moe(x, w_router, b_router, w1, w2, topk, opt, name):
     ids = torch.empty((M, topk), dtype=torch.int32, device=x.device)
     probs = torch.empty((M, topk), dtype=torch.float32, device=x.device)
     s = _stream(x.device)
-    ws = _workspace(_lib.bi_moe_workspace_size(M, H, E, I, topk), x.device, s)
+    ws = _workspace(_lib.bi_moe_workspace_size(M, H, E, I, topk), x.device, s, ws_given)
     common = (_ptr(x), _ptr(w_router), _ptr(b_router), _ptr(w1), _ptr(w2), M, H, E, I, topk)
     tail = (_ptr(ids), _ptr(probs), _ptr(y), _ptr(ws), 0 if ws is None else ws.numel(),
             ctypes.c_void_p(s.cuda_stream))
@@ -282,11 +337,60 @@ def bi_indexer_topk(scores, topk: int, row_start=None, row_end=None, out=None):
             raise ValueError(f"bi_indexer_topk: {name} must be a contiguous int64 [rows] tensor on the same GPU")
     if out is None:
         out = torch.empty((rows, topk), dtype=torch.int32, device=scores.device)
+    _check_out(out, (rows, topk), (torch.int32,), scores.device, "bi_indexer_topk")
     s = _stream(scores.device)
     _check(_lib.bi_indexer_topk(_ptr(scores), max(scores.stride(0), cols), rows, cols, _ptr(row_start),
                                 _ptr(row_end), topk, _ptr(out), out.stride(0),
                                 ctypes.c_void_p(s.cuda_stream)), "bi_indexer_topk")
     return out
+
+
+def bi_lab_xcc_ids(grid_x: int, grid_y: int = 1, device=None) -> torch.Tensor:
+    """XCD id each workgroup of a grid_x x grid_y grid ran on (int64 [grid_y, grid_x])."""
+    device = torch.device(device or "cuda")
+    out = torch.empty((grid_y, grid_x), dtype=torch.int32, device=device)
+    s = _stream(device)
+    _check(_lib.bi_lab_xcc_ids(_ptr(out), grid_x, grid_y, ctypes.c_void_p(s.cuda_stream)), "bi_lab_xcc_ids")
+    return out.long() & 0xffffffff
+
+
+def plan_path(dtype: int, M: int, N: int, K: int) -> int:
+    """The kernel path (BI_PATH_*) the production entry points pick for M rows."""
+    p = ctypes.c_int32(-1)
+    _check(_lib.bi_lab_plan(dtype, M, N, K, ctypes.byref(p)), "bi_lab_plan")
+    return p.value
+
+
+def moe_layout(M: int, H: int, E: int, I: int, topk: int) -> dict:
+    """Byte offsets of the MoE workspace's sorted pair list, activations and
+    slot partials, and its size (bi_lab_moe_layout)."""
+    out = (_I64 * 4)()
+    _check(_lib.bi_lab_moe_layout(M, H, E, I, topk, out), "bi_lab_moe_layout")
+    return {"sorted": out[0], "act": out[1], "part": out[2], "total": out[3]}
+
+
+def bi_lab_empty(grid: int, threads: int = 64):
+    """Enqueue an empty kernel of `grid` workgroups (the per-launch floor)."""
+    s = _stream(torch.device("cuda", torch.cuda.current_device()))
+    _check(_lib.bi_lab_empty(grid, threads, ctypes.c_void_p(s.cuda_stream)), "bi_lab_empty")
+
+
+def bi_lab_stream_read(src: torch.Tensor, sink: torch.Tensor, grid: int):
+    """Read every byte of `src` once on the GPU (cold-read rate); sink: int32 [>= grid]."""
+    if not (src.is_cuda and src.is_contiguous() and sink.is_cuda and sink.dtype == torch.int32
+            and sink.numel() >= grid and src.device == sink.device):
+        raise ValueError("bi_lab_stream_read: contiguous CUDA src and an int32 sink of >= grid entries")
+    s = _stream(src.device)
+    _check(_lib.bi_lab_stream_read(_ptr(src), src.numel() * src.element_size(), _ptr(sink), grid,
+                                   ctypes.c_void_p(s.cuda_stream)), "bi_lab_stream_read")
+
+
+def bi_lab_clock(out: torch.Tensor, grid: int, iters: int):
+    """Shader-clock probe: out int64 [grid, 3] gets (cycles, wall ticks, keep-alive) per workgroup."""
+    if not (out.is_cuda and out.dtype == torch.int64 and out.is_contiguous() and out.numel() >= 3 * grid):
+        raise ValueError("bi_lab_clock: out must be a contiguous int64 CUDA tensor of >= 3 * grid entries")
+    s = _stream(out.device)
+    _check(_lib.bi_lab_clock(_ptr(out), grid, iters, ctypes.c_void_p(s.cuda_stream)), "bi_lab_clock")
 
 
 def lib():

@@ -163,6 +163,57 @@ bi_status_t bi_negctl_linear_f32(const float* x, int64_t ldx, const float* w, in
                       stream);
 }
 
+bi_status_t bi_lab_xcc_ids(uint32_t* out, int32_t grid_x, int32_t grid_y, hipStream_t stream)
+{
+    if (!out || grid_x <= 0 || grid_y <= 0 || (reinterpret_cast<uintptr_t>(out) & 3u) != 0)
+        return BI_EINVAL;
+    if ((int64_t)grid_x * grid_y > (int64_t(1) << 24) || grid_y > 65535)
+        return BI_EUNSUPPORTED;
+    return launch_xcc_ids(out, grid_x, grid_y, stream) == hipSuccess ? BI_OK : BI_EHIP;
+}
+
+bi_status_t bi_lab_plan(int32_t dtype, int64_t M, int64_t N, int64_t K, int32_t* path)
+{
+    if (!path || M <= 0)
+        return BI_EINVAL;
+    bi_recipe_t r;
+    bi_status_t st = recipe_for(dtype, N, K, &r);
+    if (st != BI_OK)
+        return st;
+    Plan p;
+    if ((st = make_plan(r, BI_PATH_AUTO, M, N, K, &p)) != BI_OK)
+        return st;
+    *path = p.path;
+    return BI_OK;
+}
+
+bi_status_t bi_lab_moe_layout(int64_t M, int64_t H, int64_t E, int64_t I, int64_t topk, int64_t* offsets)
+{
+    return moe_layout_offsets(M, H, E, I, topk, offsets);
+}
+
+bi_status_t bi_lab_empty(int32_t grid, int32_t threads, hipStream_t stream)
+{
+    if (grid <= 0 || threads <= 0 || threads > 1024 || threads % 64 != 0)
+        return BI_EINVAL;
+    return launch_empty(grid, threads, stream) == hipSuccess ? BI_OK : BI_EHIP;
+}
+
+bi_status_t bi_lab_stream_read(const void* src, int64_t bytes, uint32_t* sink, int32_t grid, hipStream_t stream)
+{
+    if (!src || !sink || bytes <= 0 || bytes % 16 != 0 || grid <= 0 || grid > 65535 ||
+        (reinterpret_cast<uintptr_t>(src) & 15u) != 0 || (reinterpret_cast<uintptr_t>(sink) & 3u) != 0)
+        return BI_EINVAL;
+    return launch_stream_read(src, bytes, sink, grid, stream) == hipSuccess ? BI_OK : BI_EHIP;
+}
+
+bi_status_t bi_lab_clock(uint64_t* out, int32_t grid, int32_t iters, hipStream_t stream)
+{
+    if (!out || grid <= 0 || grid > 65535 || iters <= 0 || (reinterpret_cast<uintptr_t>(out) & 7u) != 0)
+        return BI_EINVAL;
+    return launch_clock(out, grid, iters, stream) == hipSuccess ? BI_OK : BI_EHIP;
+}
+
 size_t bi_moe_workspace_size(int64_t M, int64_t H, int64_t E, int64_t I, int64_t topk)
 {
     return moe_workspace_size(M, H, E, I, topk);

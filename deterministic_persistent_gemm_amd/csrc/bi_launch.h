@@ -25,9 +25,15 @@ struct LinearArgs {
 };
 
 // fold == false leaves a decode-path call with several k tiles at its tile
-// partials (layout: [M tile][N tile][k tile][64 lanes] of f32x4 in ws) for a
-// consumer that folds them itself in the same order.
+// partials (layout: [M tile][N tile][k tile][64 lanes] of f32x4 at ws +
+// kDecodeCounterBytes) for a consumer that folds them itself in the same order.
 hipError_t launch_linear(int xkind, const LinearArgs& a, const Plan& p, void* ws, hipStream_t s,
                          bool fold = true);
+
+// Diagnostic kernels (bi_lab.hip).
+hipError_t launch_xcc_ids(uint32_t* out, int gx, int gy, hipStream_t s);
+hipError_t launch_empty(int grid, int threads, hipStream_t s);
+hipError_t launch_stream_read(const void* src, int64_t bytes, uint32_t* sink, int grid, hipStream_t s);
+hipError_t launch_clock(uint64_t* out, int grid, int iters, hipStream_t s);
 
 }  // namespace bi

@@ -43,36 +43,59 @@ namespace bi {
 
 __device__ __forceinline__ void store_elem(const LinearArgs& a, int row, int col, float v)
 {
-    if (a.bias)
-        v = v + a.bias[col];
     if (a.y_bf16)
         reinterpret_cast<uint16_t*>(a.y)[(int64_t)row * a.ldy + col] = f32_to_bf16_rne(v);
     else
         reinterpret_cast<float*>(a.y)[(int64_t)row * a.ldy + col] = v;
 }
 
-// acc holds rows row0 + q (q = 0..3) of column col.
+// acc holds rows row0 + q (q = 0..3) of column col.  The bias is one fp32 add
+// after the full reduction; without a bias nothing is added (adding +0.0
+// would turn a -0.0 result into +0.0).  Its element is loaded once, before
+// the rows, so the rows' stores do not each wait on a load.
 __device__ __forceinline__ void store_acc(const LinearArgs& a, int row0, int col, f32x4 acc)
 {
     if (col >= a.N)
         return;
+    const bool has_bias = a.bias != nullptr;
+    const float b = has_bias ? a.bias[col] : 0.f;
 #pragma unroll
     for (int q = 0; q < 4; ++q)
         if (row0 + q < a.M)
-            store_elem(a, row0 + q, col, acc[q]);
+            store_elem(a, row0 + q, col, has_bias ? acc[q] + b : acc[q]);
 }
 
 // -------------------------------------------------------------------- decode
 
+// Arrival counters of the XCD hand-over decode: one 32-bit counter per
+// 128-byte L2 line, at the start of the workspace.
+constexpr int kCounterStride = kDecodeCounterBytes / 4 / kDecodeMaxCounters;
+
 // One wave per (16-column N tile, k tile partial, group of MT 16-row M tiles).
 // The wave loads its slab of W once and runs MT independent chains over it,
 // one per M tile.  With a single k tile (block_k == K) the wave finishes the
-// output itself; otherwise it stores its tile partials, and k_decode_fold
-// adds them up in ascending tile order in a second launch (the kernel
-// boundary makes the partials visible; no device-wide fences or counters).
-template <typename OX, typename OW, int CH, int MT>
+// output itself.  Otherwise it stores its tile partials and then either
+//  * HANDOFF == false: k_decode_fold adds them up in ascending tile order in a
+//    second launch (the kernel boundary makes the partials visible), or
+//  * HANDOFF == true: the wave counts itself in at its output tile's arrival
+//    counter, and the wave that arrives last adds every partial of the tile
+//    in ascending tile order, adds the bias and stores -- one launch.
+//
+// The hand-over stays inside one XCD's L2.  Workgroups are dispatched
+// to the XCDs round-robin (workgroup w runs on XCD w mod 8, as AMD documents
+// for the MI300-family dispatcher), and the grid runs the N tile fastest with
+// N/16 a multiple of 8, so every wave of an output tile runs on XCD nt mod 8
+// and the L2 it shares is the coherence point of the hand-over: each wave's
+// partial stores are acknowledged by that L2 before its counter increment
+// (an atomic, also performed in that L2) is issued, and the last wave drops
+// its L1 before reading the other partials.  No device-scope fence, no L2
+// write-back, and no wave ever waits on another.  The counter wraps to zero
+// at its last arrival (atomic increment modulo tiles_k), so every call
+// leaves the counters as it found them: zero.
+template <typename OX, typename OW, int CH, int MT, bool HANDOFF = false>
 __global__ __launch_bounds__(64) void k_decode(LinearArgs a, int kbpt, int tiles_k, int mtiles,
-                                               f32x4* __restrict__ partials)
+                                               f32x4* __restrict__ partials,
+                                               uint32_t* __restrict__ counters = nullptr)
 {
     using EX = typename OX::elem;
     using EW = typename OW::elem;
@@ -149,6 +172,45 @@ __global__ __launch_bounds__(64) void k_decode(LinearArgs a, int kbpt, int tiles
             store_acc(a, row0, col, P[m][0]);
         else
             partials[(((int64_t)mt * ntiles + nt) * tiles_k + t) * 64 + lane] = P[m][0];
+    }
+    if constexpr (HANDOFF) {
+        if (tiles_k == 1)
+            return;
+        // this wave's partial stores are complete in the XCD's L2
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        uint32_t prev = 0;
+        if (lane == 0)
+            prev = __builtin_amdgcn_atomic_inc32(counters + (blockIdx.y * ntiles + nt) * kCounterStride,
+                                                 (uint32_t)(tiles_k - 1), __ATOMIC_RELAXED, "workgroup");
+        prev = (uint32_t)__builtin_amdgcn_readfirstlane((int)prev);
+        if (prev != (uint32_t)(tiles_k - 1))
+            return;
+        // last arrival: every other partial of the tile is in L2; drop stale
+        // L1 lines, then fold exactly as k_decode_fold does
+        asm volatile("buffer_inv sc0" ::: "memory");
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+            const int mt = mt0 + m;
+            const int row0 = mt * 16 + acc_row(lane, 0);
+            if (mt >= mtiles || row0 >= a.M)
+                continue;
+            const f32x4* p = partials + ((int64_t)mt * ntiles + nt) * tiles_k * 64 + lane;
+            constexpr int kBatch = 32;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            for (int u0 = 0; u0 < tiles_k; u0 += kBatch) {
+                const int n = min(kBatch, tiles_k - u0);
+                f32x4 v[kBatch];
+#pragma unroll
+                for (int i = 0; i < kBatch; ++i)
+                    if (i < n)
+                        v[i] = p[(int64_t)(u0 + i) * 64];   // this wave's own partial included
+#pragma unroll
+                for (int i = 0; i < kBatch; ++i)
+                    if (i < n)
+                        acc = (u0 + i == 0) ? v[i] : acc + v[i];
+            }
+            store_acc(a, row0, col, acc);
+        }
     }
 }
 
@@ -900,8 +962,9 @@ static hipError_t launch_stream_bf16(const LinearArgs& a, const Plan& p, hipStre
 
 // ------------------------------------------------------------------ launcher
 
-template <typename OX, typename OW, int MT>
-static hipError_t launch_decode_mt(const LinearArgs& a, const Plan& p, f32x4* partials, hipStream_t s)
+template <typename OX, typename OW, int MT, bool HANDOFF>
+static hipError_t launch_decode_mt(const LinearArgs& a, const Plan& p, f32x4* partials, uint32_t* counters,
+                                   hipStream_t s)
 {
     dim3 grid((unsigned)(p.ntiles * p.tiles_k), (unsigned)((p.mtiles + MT - 1) / MT));
     const int kbpt = p.kbpt;
@@ -916,40 +979,60 @@ static hipError_t launch_decode_mt(const LinearArgs& a, const Plan& p, f32x4* pa
         }
     if constexpr (kMaxCH >= 16) {
         if (ch == 16) {
-            k_decode<OX, OW, 16, MT><<<grid, 64, 0, s>>>(a, kbpt, p.tiles_k, p.mtiles, partials);
+            k_decode<OX, OW, 16, MT, HANDOFF><<<grid, 64, 0, s>>>(a, kbpt, p.tiles_k, p.mtiles, partials, counters);
             return hipGetLastError();
         }
     }
     if constexpr (kMaxCH >= 8) {
         if (ch == 8) {
-            k_decode<OX, OW, 8, MT><<<grid, 64, 0, s>>>(a, kbpt, p.tiles_k, p.mtiles, partials);
+            k_decode<OX, OW, 8, MT, HANDOFF><<<grid, 64, 0, s>>>(a, kbpt, p.tiles_k, p.mtiles, partials, counters);
             return hipGetLastError();
         }
     }
     switch (ch) {
-    case 4:  k_decode<OX, OW, 4, MT><<<grid, 64, 0, s>>>(a, kbpt, p.tiles_k, p.mtiles, partials); break;
-    case 2:  k_decode<OX, OW, 2, MT><<<grid, 64, 0, s>>>(a, kbpt, p.tiles_k, p.mtiles, partials); break;
-    default: k_decode<OX, OW, 1, MT><<<grid, 64, 0, s>>>(a, kbpt, p.tiles_k, p.mtiles, partials); break;
+    case 4:  k_decode<OX, OW, 4, MT, HANDOFF><<<grid, 64, 0, s>>>(a, kbpt, p.tiles_k, p.mtiles, partials, counters); break;
+    case 2:  k_decode<OX, OW, 2, MT, HANDOFF><<<grid, 64, 0, s>>>(a, kbpt, p.tiles_k, p.mtiles, partials, counters); break;
+    default: k_decode<OX, OW, 1, MT, HANDOFF><<<grid, 64, 0, s>>>(a, kbpt, p.tiles_k, p.mtiles, partials, counters); break;
     }
     return hipGetLastError();
+}
+
+// M tiles per wave: a wave's W fragments serve 2 M tiles from 4 M tiles on
+// and 4 from 12 on, while at least ~1000 waves remain (measured for the fp32
+// router: M=64 11.0 -> 10.4 us, M=96 13.5 -> 12.2, M=192 18.5 -> 17.6; below
+// 4 M tiles one M tile per wave is as fast)
+int decode_m_per_wave(const Plan& p)
+{
+    if (p.m_per_wave > 0)
+        return p.m_per_wave;
+    const int waves1 = p.ntiles * p.tiles_k * p.mtiles;
+    if (p.mtiles >= 12 && waves1 >= 6144)
+        return 4;
+    if (p.mtiles >= 4 && waves1 >= 2048)
+        return 2;
+    return 1;
 }
 
 template <typename OX, typename OW>
 static hipError_t launch_decode(const LinearArgs& a, const Plan& p, void* ws, hipStream_t s, bool fold)
 {
-    f32x4* partials = reinterpret_cast<f32x4*>(ws);
+    const int mt = p.path == kPathDecodeXcd ? xcd_m_per_wave(p) : decode_m_per_wave(p);
+    uint32_t* counters = reinterpret_cast<uint32_t*>(ws);
+    f32x4* partials = ws ? reinterpret_cast<f32x4*>(reinterpret_cast<char*>(ws) + kDecodeCounterBytes) : nullptr;
+    if (p.path == kPathDecodeXcd) {
+        if (mt == 4)
+            return launch_decode_mt<OX, OW, 4, true>(a, p, partials, counters, s);
+        if (mt == 2)
+            return launch_decode_mt<OX, OW, 2, true>(a, p, partials, counters, s);
+        return launch_decode_mt<OX, OW, 1, true>(a, p, partials, counters, s);
+    }
     hipError_t e;
-    // M tiles per wave: a wave's W fragments serve 2 M tiles from 4 M tiles
-    // on and 4 from 12 on, while at least ~1000 waves remain (measured for
-    // the fp32 router: M=64 11.0 -> 10.4 us, M=96 13.5 -> 12.2, M=192 18.5
-    // -> 17.6; below 4 M tiles one M tile per wave is as fast)
-    const int waves1 = p.ntiles * p.tiles_k * p.mtiles;
-    if (p.mtiles >= 12 && waves1 >= 6144)
-        e = launch_decode_mt<OX, OW, 4>(a, p, partials, s);
-    else if (p.mtiles >= 4 && waves1 >= 2048)
-        e = launch_decode_mt<OX, OW, 2>(a, p, partials, s);
+    if (mt == 4)
+        e = launch_decode_mt<OX, OW, 4, false>(a, p, partials, nullptr, s);
+    else if (mt == 2)
+        e = launch_decode_mt<OX, OW, 2, false>(a, p, partials, nullptr, s);
     else
-        e = launch_decode_mt<OX, OW, 1>(a, p, partials, s);
+        e = launch_decode_mt<OX, OW, 1, false>(a, p, partials, nullptr, s);
     if (e != hipSuccess || p.tiles_k == 1 || !fold)
         return e;
     k_decode_fold<<<dim3((unsigned)p.ntiles, (unsigned)p.mtiles), 64, 0, s>>>(a, p.tiles_k, partials);
@@ -1146,7 +1229,7 @@ static hipError_t launch_typed(const LinearArgs& a, const Plan& p, void* ws, hip
         if (p.path == kPathDecodeDma)
             return launch_decode_dma(a, p, s);
     }
-    if (p.path == kPathDecode || p.path == kPathDecodeWg)
+    if (p.path == kPathDecode || p.path == kPathDecodeWg || p.path == kPathDecodeXcd)
         return launch_decode<OX, OW>(a, p, ws, s, fold);
     return launch_persistent<OX, OW>(a, p, s);
 }

@@ -56,7 +56,9 @@ MoELayout moe_layout(int64_t M, int64_t H, int64_t E, int64_t I, int64_t topk, s
     const int64_t U = unit_rows_for(M, E, topk);
     L.max_units = (P + U - 1) / U + (P < E ? P : E);
     size_t o = 0;
-    L.router_ws = o;   o = align256(o + router_ws_bytes);
+    // the router's workspace (counter region, then its tile partials) comes
+    // first, so the counter region is the MoE workspace's own
+    L.router_ws = o;   o = align256(o + (router_ws_bytes > kDecodeCounterBytes ? router_ws_bytes : kDecodeCounterBytes));
     L.logits = o;      o = align256(o + (size_t)M * E * sizeof(float));
     L.offsets = o;     o = align256(o + (size_t)(E + 1) * sizeof(int32_t));
     L.unit_expert = o; o = align256(o + (size_t)L.max_units * sizeof(int32_t));
@@ -691,8 +693,10 @@ static hipError_t launch_grouped(const GroupedArgs& g, int unit_rows, int64_t ma
 // router's tile partials itself (saving the fold launch).
 static bi_status_t router_plan(const bi_recipe_t& r, int64_t M, int64_t E, int64_t H, Plan* p)
 {
+    // on a decode path the routing kernel folds the router's tile partials
+    // itself, so the router runs the two-launch decode's first kernel alone
     bi_status_t st = make_plan(r, BI_PATH_AUTO, M, E, H, p);
-    if (st == BI_OK && p->path == kPathDecodeWg)
+    if (st == BI_OK && (p->path == kPathDecodeWg || p->path == kPathDecodeXcd))
         st = make_plan(r, BI_PATH_DECODE, M, E, H, p);
     return st;
 }
@@ -708,6 +712,25 @@ size_t moe_workspace_size(int64_t M, int64_t H, int64_t E, int64_t I, int64_t to
     if (router_plan(r, M, E, H, &p) != BI_OK)
         return 0;
     return moe_layout(M, H, E, I, topk, p.ws_bytes).total;
+}
+
+bi_status_t moe_layout_offsets(int64_t M, int64_t H, int64_t E, int64_t I, int64_t topk, int64_t* out)
+{
+    if (!out || M <= 0 || H <= 0 || E <= 0 || I <= 0 || topk <= 0)
+        return BI_EINVAL;
+    bi_recipe_t r;
+    bi_status_t st = recipe_for(BI_F32, E, H, &r);
+    if (st != BI_OK)
+        return st;
+    Plan p;
+    if ((st = router_plan(r, M, E, H, &p)) != BI_OK)
+        return st;
+    const MoELayout L = moe_layout(M, H, E, I, topk, p.ws_bytes);
+    out[0] = (int64_t)L.sorted;
+    out[1] = (int64_t)L.act;
+    out[2] = (int64_t)L.part;
+    out[3] = (int64_t)L.total;
+    return BI_OK;
 }
 
 bi_status_t moe_run(const uint16_t* x, const float* w_router, const float* b_router, const uint16_t* w13,
@@ -772,7 +795,7 @@ bi_status_t moe_run(const uint16_t* x, const float* w_router, const float* b_rou
         return BI_EHIP;
     const unsigned route_groups = (unsigned)((M + kRouteTokens - 1) / kRouteTokens);
     const float* lsrc = fused_fold ? nullptr : logits;
-    const f32x4* psrc = fused_fold ? reinterpret_cast<const f32x4*>(base + L.router_ws) : nullptr;
+    const f32x4* psrc = fused_fold ? reinterpret_cast<const f32x4*>(base + L.router_ws + kDecodeCounterBytes) : nullptr;
     const int unit_rows = unit_rows_for(M, E, topk);
     const DispatchOut dout{unit_rows, offsets, sorted, unit_expert, unit_row, nunits};
     // one routing workgroup (M <= 16): the dispatch runs inside it

@@ -25,7 +25,7 @@ constexpr int kF32BlockK = 128;
 // the production weight.t() layout, keyed on (dtype, N, K) only.
 const KeyEntry kTable[] = {
 #include "bi_table.inc"
-    {-1, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0}   // end marker
+    {-1, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0}   // end marker
 };
 constexpr int kTableSize = (int)(sizeof(kTable) / sizeof(kTable[0])) - 1;
 
@@ -122,6 +122,24 @@ int device_cu_count()
     return cus;
 }
 
+int xcd_m_per_wave(const Plan& p)
+{
+    if (p.m_per_wave > 0)
+        return p.m_per_wave;
+    if ((int64_t)p.mtiles * p.ntiles <= kDecodeMaxCounters)
+        return 1;
+    return decode_m_per_wave(p);
+}
+
+bool decode_xcd_ok(const Plan& p)
+{
+    if (p.tiles_k < 2 || p.ntiles % 8 != 0)
+        return false;
+    const int mw = xcd_m_per_wave(p);
+    const int groups = (p.mtiles + mw - 1) / mw;
+    return (int64_t)groups * p.ntiles <= kDecodeMaxCounters;
+}
+
 bool tile_code_valid(int dtype, int code)
 {
     if (dtype == BI_F32)
@@ -150,11 +168,22 @@ bi_status_t make_plan(const bi_recipe_t& r, int32_t path_req, int64_t M, int64_t
     p.mtiles = (int)((M + 15) / 16);
     p.ntiles = (int)(N / 16);
     p.tiling = persistent_tiling(r);
+    // bits 8..15: a persistent tile shape, or the M tiles per wave of the
+    // k-tile-parallel decode paths (experiments only; never the numerics)
     const int tile_code = (path_req >> 8) & 0xff;
     path_req &= 0xff;
-    if (tile_code != 0 && (path_req != BI_PATH_PERSISTENT || !tile_code_valid(r.dtype, tile_code)))
-        return BI_EINVAL;
-    p.tile_code = tile_code;
+    if (tile_code != 0) {
+        if (path_req == BI_PATH_PERSISTENT) {
+            if (!tile_code_valid(r.dtype, tile_code))
+                return BI_EINVAL;
+            p.tile_code = tile_code;
+        } else if (path_req == BI_PATH_DECODE || path_req == BI_PATH_DECODE_XCD) {
+            if (tile_code != 1 && tile_code != 2 && tile_code != 4)
+                return BI_EINVAL;
+            p.m_per_wave = tile_code;
+        } else
+            return BI_EINVAL;
+    }
     const bool wg_ok = p.tiles_k >= 2 && p.tiles_k <= kDecodeWgMaxTiles;
     if (path_req == BI_PATH_DECODE)
         p.path = kPathDecode;
@@ -166,6 +195,10 @@ bi_status_t make_plan(const bi_recipe_t& r, int32_t path_req, int64_t M, int64_t
         if (!decode_dma_ok(p, K))
             return BI_EUNSUPPORTED;
         p.path = kPathDecodeDma;
+    } else if (path_req == BI_PATH_DECODE_XCD) {
+        if (!decode_xcd_ok(p))
+            return BI_EUNSUPPORTED;
+        p.path = kPathDecodeXcd;
     } else if (path_req == BI_PATH_PERSISTENT)
         p.path = kPathPersistent;
     else if (path_req == BI_PATH_AUTO) {
@@ -183,6 +216,8 @@ bi_status_t make_plan(const bi_recipe_t& r, int32_t path_req, int64_t M, int64_t
         const bool dma_ok = decode_dma_ok(p, K);
         if (M > r.m_decode_max)
             p.path = kPathPersistent;
+        else if (e && M <= e->m_xcd_max && decode_xcd_ok(p))
+            p.path = kPathDecodeXcd;
         else if (e && e->decode_path == BI_PATH_DECODE)
             p.path = kPathDecode;
         else if (e && e->decode_path == BI_PATH_DECODE_WG && wg_ok)
@@ -199,9 +234,10 @@ bi_status_t make_plan(const bi_recipe_t& r, int32_t path_req, int64_t M, int64_t
     }
     else
         return BI_EINVAL;
+    // tile partials follow the counter region every workspace starts with
     p.ws_bytes = 0;
-    if (p.path == kPathDecode && p.tiles_k > 1)
-        p.ws_bytes = (size_t)p.mtiles * (size_t)p.ntiles * (size_t)p.tiles_k * 64 * 16;
+    if ((p.path == kPathDecode || p.path == kPathDecodeXcd) && p.tiles_k > 1)
+        p.ws_bytes = kDecodeCounterBytes + (size_t)p.mtiles * (size_t)p.ntiles * (size_t)p.tiles_k * 64 * 16;
     *plan = p;
     return BI_OK;
 }

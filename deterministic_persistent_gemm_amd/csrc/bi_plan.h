@@ -8,7 +8,15 @@
 
 namespace bi {
 
-enum Path { kPathDecode = 1, kPathPersistent = 2, kPathDecodeWg = 3, kPathDecodeDma = 4 };
+enum Path { kPathDecode = 1, kPathPersistent = 2, kPathDecodeWg = 3, kPathDecodeDma = 4, kPathDecodeXcd = 5 };
+
+// Every workspace starts with a region of kDecodeCounterBytes that holds the
+// arrival counters of the one-launch decode (one 32-bit counter per
+// output-tile group, each on its own 128-byte line).  It must be zero when a
+// workspace is first used; no call writes anything else there, and every call
+// leaves the counters at zero.  Tile partials and MoE intermediates follow it.
+constexpr int kDecodeMaxCounters = 128;
+constexpr size_t kDecodeCounterBytes = 16384;
 
 // Most tile partials the one-launch decode kernel keeps in LDS (64 KiB).
 constexpr int kDecodeWgMaxTiles = 64;
@@ -34,6 +42,8 @@ struct KeyEntry {
     int32_t tile_a;
     int64_t m_b;
     int32_t tile_b, tile_c;
+    int32_t m_xcd_max;      // largest M on the XCD hand-over decode (0: never); below
+                            // m_decode_max it takes precedence over decode_path
 };
 
 // The table entry of a key, or nullptr.
@@ -52,6 +62,7 @@ struct Plan {
     int ntiles;      // 16-column tiles of N (decode path)
     Tiling tiling;   // persistent path
     int tile_code;   // persistent tile shape, 0 = automatic (table entry or heuristic)
+    int m_per_wave;  // decode paths: 16-row M tiles one wave carries (1, 2, 4), 0 = automatic
     size_t ws_bytes; // workspace the plan needs (decode tile partials)
 };
 
@@ -70,6 +81,18 @@ bool tile_code_valid(int dtype, int code);
 
 // Whether the direct-to-LDS decode kernel serves this plan (bi_linear.hip).
 bool decode_dma_ok(const Plan& p, int64_t K);
+
+// M tiles one decode wave carries (bi_linear.hip): the two-launch decode
+// shares W fragments over 2 or 4 M tiles at large M; the XCD hand-over keeps
+// one M tile per wave while the counters allow it, since its last wave folds
+// the M tiles of its group one after the other.
+int decode_m_per_wave(const Plan& p);
+int xcd_m_per_wave(const Plan& p);
+
+// Whether the one-launch decode serves this plan: several k tiles, N/16 a
+// multiple of 8 (so every wave of an output tile runs on one XCD), and no
+// more output-tile groups than there are counters.
+bool decode_xcd_ok(const Plan& p);
 
 // Number of compute units of the current device (cached per device).
 int device_cu_count();

@@ -17,8 +17,9 @@ with cold weights (rotating copies, beyond the Infinity Cache):
 
   * every decode form that serves the candidate (two launches with a
     workspace fold, one launch with an LDS fold, direct-to-LDS streaming for
-    a chained bf16 recipe) at M in DECODE_M and at the prefill sizes up to
-    DECODE_PROBE_MAX (the decode limit may lie beyond the decode sizes);
+    a chained bf16 recipe, one launch with the XCD hand-over fold) at M in
+    DECODE_M and at the prefill sizes up to DECODE_PROBE_MAX (the decode
+    limit may lie beyond the decode sizes);
   * every persistent tile shape at M in PREFILL_M and at the decode sizes
     where the persistent kernel might take over;
   * both at CROSS_M, which only places the decode limit between the
@@ -35,7 +36,8 @@ row inside the batch, then picks the entry for the profile:
             best candidate
 
 (candidates within --tie of the best keep the key's served recipe, so noise
-does not change a key's bits),
+does not change a key's bits; --keep-recipe considers the served block_k
+only, so a re-sweep changes kernel shapes and never a key's bits),
 
 and emits it as a JSON report and a line of bi_table.inc.  --write-table
 merges the entries into csrc/bi_table.inc (replacing the keys swept); the
@@ -58,10 +60,11 @@ CROSS_M = (512,)            # timed on both sides to place the decode limit, not
 DECODE_PROBE_MAX = 1024     # decode forms are also timed at the prefill sizes up to this M
 DECODE_MARGIN = 0.05        # the persistent kernel takes over once it is this much faster
 TABLE_HEADER = ("// Measured key table, written by deterministic_persistent_gemm_amd/sweep.py.\n"
-                "// {dtype, N, K, block_k, m_decode_max, decode_path, m_a, tile_a, m_b, tile_b, tile_c}\n")
+                "// {dtype, N, K, block_k, m_decode_max, decode_path, m_a, tile_a, m_b, tile_b, tile_c, "
+                "m_xcd_max}\n")
 F32_CODES = tuple(range(1, 11))
 BF16_CODES = tuple(range(11, 21))
-PATH_DECODE, PATH_PERSISTENT, PATH_DECODE_WG, PATH_DECODE_DMA = 1, 2, 3, 4
+PATH_DECODE, PATH_PERSISTENT, PATH_DECODE_WG, PATH_DECODE_DMA, PATH_DECODE_XCD = 1, 2, 3, 4, 5
 
 
 def parse_key(s: str, profile: str = "decode"):
@@ -103,6 +106,10 @@ def summarize(cand: dict) -> dict:
     cand = {"block_k": b, "decode": {M: {path: us}}, "persistent": {M: {code: us}}}"""
     best_dec = {M: min(v.values()) for M, v in cand["decode"].items() if v}
     best_dec_path = {M: min(v, key=v.get) for M, v in cand["decode"].items() if v}
+    # decode_path names the form that serves M above the XCD hand-over's
+    # range, so it is picked among the other forms
+    other = {M: {p: t for p, t in v.items() if p != PATH_DECODE_XCD} for M, v in cand["decode"].items()}
+    best_other_path = {M: min(v, key=v.get) for M, v in other.items() if v}
     best_per = {M: min(v.values()) for M, v in cand["persistent"].items() if v}
     best_code = {M: min(v, key=v.get) for M, v in cand["persistent"].items() if v}
     # decode serves M up to the last grid point before the persistent kernel
@@ -114,13 +121,22 @@ def summarize(cand: dict) -> dict:
             break
         m_dec = M
     dec_ms = [M for M in sorted(best_dec) if M <= m_dec]
-    paths = [best_dec_path[M] for M in dec_ms]
+    # the XCD hand-over serves M from 1 up to the last grid point of an
+    # unbroken run where it is the best decode form
+    m_xcd = 0
+    for M in dec_ms:
+        if best_dec_path[M] != PATH_DECODE_XCD:
+            break
+        m_xcd = M
+    paths = [best_other_path[M] for M in dec_ms if M > m_xcd and M in best_other_path] or \
+        [best_other_path[M] for M in dec_ms if M in best_other_path]
     decode_path = max(set(paths), key=paths.count) if paths else 0
     tiles = tile_segments(cand["persistent"], [M for M in best_code if M > m_dec])
     decode_total = sum(min(best_dec.get(M, math.inf), best_per.get(M, math.inf)) for M in DECODE_M
                        if M in best_dec or M in best_per)
     prefill_total = sum(best_per[M] for M in PREFILL_M if M in best_per)
-    return {"block_k": cand["block_k"], "m_decode_max": m_dec, "decode_path": decode_path, **tiles,
+    return {"block_k": cand["block_k"], "m_decode_max": m_dec, "decode_path": decode_path, "m_xcd_max": m_xcd,
+            **tiles,
             "decode_total_us": round(decode_total, 3), "prefill_total_us": round(prefill_total, 3)}
 
 
@@ -186,7 +202,7 @@ def choose(summaries: list, profile: str, keep_block_k: int | None = None, tie: 
 def table_line(dt: str, N: int, K: int, e: dict) -> str:
     d = "BI_F32" if dt == "f32" else "BI_BF16"
     return (f"{{{d}, {N}, {K}, {e['block_k']}, {e['m_decode_max']}, {e['decode_path']}, "
-            f"{e['m_a']}, {e['tile_a']}, {e['m_b']}, {e['tile_b']}, {e['tile_c']}}},")
+            f"{e['m_a']}, {e['tile_a']}, {e['m_b']}, {e['tile_b']}, {e['tile_c']}, {e.get('m_xcd_max', 0)}}},")
 
 
 def merge_table(text: str, lines: dict) -> str:
@@ -217,7 +233,8 @@ def parse_table(text: str):
         f = [x.strip() for x in s.strip("{},").split(",")]
         rows.append({"dtype": f[0], "N": int(f[1]), "K": int(f[2]), "block_k": int(f[3]),
                      "m_decode_max": int(f[4]), "decode_path": int(f[5]), "m_a": int(f[6]),
-                     "tile_a": int(f[7]), "m_b": int(f[8]), "tile_b": int(f[9]), "tile_c": int(f[10])})
+                     "tile_a": int(f[7]), "m_b": int(f[8]), "tile_b": int(f[9]), "tile_c": int(f[10]),
+                     "m_xcd_max": int(f[11]) if len(f) > 11 else 0})
     return rows
 
 
@@ -253,7 +270,7 @@ def _timeit(torch, fns, reps=3):
     return e0.elapsed_time(e1) * 1e3 / (reps * len(fns))
 
 
-def sweep_key(dt: str, N: int, K: int, profile: str, tie: float = 0.03, log=print):
+def sweep_key(dt: str, N: int, K: int, profile: str, tie: float = 0.03, log=print, keep_recipe: bool = False):
     import numpy as np
     import torch
 
@@ -271,7 +288,7 @@ def sweep_key(dt: str, N: int, K: int, profile: str, tie: float = 0.03, log=prin
     odt = torch.float32
     served = bi.bi_describe_recipe(bi.BI_F32 if dt == "f32" else bi.BI_BF16, N, K).block_k
     cands, summaries = [], []
-    for bk in block_k_candidates(dt, K):
+    for bk in ([served] if keep_recipe else block_k_candidates(dt, K)):
         r = bi.bi_describe_recipe(bi.BI_F32 if dt == "f32" else bi.BI_BF16, N, K)
         r.block_k = bk
         cand = {"block_k": bk, "decode": {}, "persistent": {}, "bits_ok": True}
@@ -294,7 +311,7 @@ def sweep_key(dt: str, N: int, K: int, profile: str, tie: float = 0.03, log=prin
 
             if M in DECODE_M or M <= DECODE_PROBE_MAX:
                 cand["decode"][M] = {}
-                for path in (PATH_DECODE, PATH_DECODE_WG, PATH_DECODE_DMA):
+                for path in (PATH_DECODE, PATH_DECODE_WG, PATH_DECODE_DMA, PATH_DECODE_XCD):
                     try:
                         run(path)
                     except bi.BIError:
@@ -357,6 +374,8 @@ def main(argv=None):
     ap.add_argument("--tie", type=float, default=None,
                     help="relative objective difference treated as a tie (the served recipe is kept); "
                          "default 0.03 when sweeping, the report's own with --from-json")
+    ap.add_argument("--keep-recipe", action="store_true",
+                    help="sweep only the block_k each key already serves (kernel shapes change, bits do not)")
     ap.add_argument("--out", default=None, help="directory for the JSON reports")
     ap.add_argument("--write-table", action="store_true", help="merge the entries into csrc/bi_table.inc")
     args = ap.parse_args(argv)
@@ -371,7 +390,7 @@ def main(argv=None):
     for dt, N, K, prof in keys:
         print(f"sweeping {dt}:{N}:{K} ({prof})", flush=True)
         rep = sweep_key(dt, N, K, prof, tie=0.03 if args.tie is None else args.tie,
-                        log=lambda s: print(s, flush=True))
+                        log=lambda s: print(s, flush=True), keep_recipe=args.keep_recipe)
         print(f"  entry: {rep['table_line']}", flush=True)
         if args.out:
             os.makedirs(args.out, exist_ok=True)

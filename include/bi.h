@@ -27,10 +27,14 @@
  *    must keep every row 16-byte aligned.
  *  - `ws` is a caller-owned device workspace of at least the size reported by
  *    the matching *_workspace_size() call (16-byte aligned; NULL when that
- *    size is 0).  It holds intermediate tile partials only: it needs no
- *    initialisation, every byte a call reads it has written earlier in the
- *    same call, and one workspace serves calls of any shape in sequence.  Two
- *    calls that are in flight at the same time must not share one workspace.
+ *    size is 0).  Its first 16 KiB hold the arrival counters of the
+ *    one-launch decode kernel: they must be ZERO when the workspace is first
+ *    used (zero-fill it once at allocation), no call writes anything else
+ *    there, and every call leaves them zero.  The rest holds intermediate
+ *    tile partials and needs no initialisation (every byte of it a call reads
+ *    it has written earlier in the same call).  One workspace serves calls of
+ *    any shape in sequence; two calls in flight at the same time must not
+ *    share one workspace.
  *  - Arguments are validated on the host before anything is enqueued; a
  *    rejected call enqueues nothing.  There is no fallback to a
  *    non-invariant path: a shape the recipe table cannot serve returns
@@ -209,6 +213,10 @@ const char* bi_status_str(bi_status_t status);
 
 /* Path selectors for bi_lab_linear().  BI_PATH_DECODE: k tile partials on
  * separate waves across the chip, folded by a second launch (workspace).
+ * BI_PATH_DECODE_XCD: the same waves and the same fold in one launch -- the
+ * wave that arrives last at its output tile's counter folds the tile's
+ * partials (workspace; recipes with several k tiles, N a multiple of 128 and
+ * at most 128 output-tile groups; BI_EUNSUPPORTED otherwise).
  * BI_PATH_DECODE_WG: one workgroup per 16x16 output tile whose waves share
  * the k tile partials through LDS, one launch, no workspace (recipes with 2
  * to 64 k tiles; BI_EUNSUPPORTED otherwise).  BI_PATH_DECODE_DMA: fully
@@ -226,9 +234,11 @@ const char* bi_status_str(bi_status_t status);
  * 20 = 64x64 on 4x2 waves fed by a ring of eight 64-k LDS stages through
  * direct-to-LDS loads; 18 and 19 serve fully chained recipes only, 20 needs
  * K a multiple of 64; a shape that cannot serve falls back to another).
+ * With BI_PATH_DECODE or BI_PATH_DECODE_XCD, bits 8..15 may force the
+ * number of 16-row M tiles one decode wave carries (1, 2 or 4; 0: automatic).
  * Tile shapes never change the numerics. */
 enum { BI_PATH_AUTO = 0, BI_PATH_DECODE = 1, BI_PATH_PERSISTENT = 2, BI_PATH_DECODE_WG = 3,
-       BI_PATH_DECODE_DMA = 4 };
+       BI_PATH_DECODE_DMA = 4, BI_PATH_DECODE_XCD = 5 };
 
 /* The same linear layer with an explicit recipe and an explicit kernel path,
  * for A/B experiments (e.g. fully chained vs tile-partial, or one BLOCK_K
@@ -257,6 +267,54 @@ bi_status_t bi_negctl_linear_f32(const float* x, int64_t ldx,
                                  float* y, int64_t ldy,
                                  int64_t M, int64_t N, int64_t K,
                                  void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Diagnostic for the one-launch decode, which needs every workgroup of an
+ * output tile on one XCD (one L2): launches a grid_x x grid_y grid of
+ * 64-thread workgroups, and workgroup (x, y) writes the id of the XCD it ran
+ * on to out[y * grid_x + x].  out: device, 4-byte aligned, grid_x * grid_y
+ * uint32 entries.  Workgroups are dispatched to the XCDs round-robin in
+ * linear workgroup order, so ids that agree modulo 8 should report one XCD. */
+bi_status_t bi_lab_xcc_ids(uint32_t* out, int32_t grid_x, int32_t grid_y, hipStream_t stream);
+
+/* The kernel path (BI_PATH_*) the production entry points pick for M rows of
+ * a (dtype, N, K) key -- M picks the kernel shape, never the recipe (GateLinear
+ * page, "A correction to why the key excludes M").  path: host pointer to
+ * one int32.  BI_EINVAL for M <= 0 or a NULL path, BI_EUNSUPPORTED for keys
+ * the recipe table cannot serve. */
+bi_status_t bi_lab_plan(int32_t dtype, int64_t M, int64_t N, int64_t K, int32_t* path);
+
+/* Where a MoE call of this shape keeps its storage points in the workspace,
+ * for stage-wise checks of the layer (fused-MoE page, "What's included": the
+ * bf16 activation with the probability applied and the per-slot down
+ * projection are the layer's storage points).  offsets: host int64[4] =
+ * byte offsets of the pair list sorted by expert (int32 [M*topk], entry p is
+ * the pair m*topk + j of sorted position p), of the activations (bf16
+ * [M*topk, I] in sorted-position order) and of the fp32 slot partials
+ * ([M*topk, H] in pair order), and the workspace size.  They hold a call's
+ * values once it has completed, until the next call on the workspace. */
+bi_status_t bi_lab_moe_layout(int64_t M, int64_t H, int64_t E, int64_t I, int64_t topk, int64_t* offsets);
+
+/* Measurement floors (GateLinear page, "Update: is the M=4096 cost
+ * avoidable?": a decode-sized kernel is judged by its device time, which sits
+ * on a per-launch floor).  None of these is on the batch-invariant path.
+ *  bi_lab_empty        launches an empty kernel of `grid` workgroups of
+ *                      `threads` threads (a multiple of 64, <= 1024): its
+ *                      device time is the floor every launch pays.
+ *  bi_lab_stream_read  reads `bytes` (a multiple of 16) at `src` (device,
+ *                      16-byte aligned) once with `grid` workgroups of 256
+ *                      threads and writes one word per workgroup to sink
+ *                      (device, `grid` uint32): the cold-read rate the
+ *                      chip achieves, the practical HBM reference.
+ *  bi_lab_clock        each of `grid` 64-thread workgroups runs iters x 64
+ *                      dependent fp32 multiply-adds and writes three uint64
+ *                      to out[3 wg ..]: shader-clock cycles (s_memtime),
+ *                      constant-rate wall-clock ticks (s_memrealtime) and a
+ *                      value that keeps the chain alive.
+ * Invalid arguments return BI_EINVAL before anything is enqueued. */
+bi_status_t bi_lab_empty(int32_t grid, int32_t threads, hipStream_t stream);
+bi_status_t bi_lab_stream_read(const void* src, int64_t bytes, uint32_t* sink, int32_t grid,
+                               hipStream_t stream);
+bi_status_t bi_lab_clock(uint64_t* out, int32_t grid, int32_t iters, hipStream_t stream);
 
 #ifdef __cplusplus
 }

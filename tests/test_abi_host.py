@@ -103,7 +103,14 @@ def lab_ws(path, M):
 def test_workspace_required_and_sized():
     # the two-launch decode path keeps its tile partials in the workspace
     need = lab_ws(bi.BI_PATH_DECODE, 1)
-    assert need == 16 * 32 * 64 * 16          # N tiles x k tiles x 64 lanes x f32x4
+    # the counter region every workspace starts with, then N tiles x k tiles
+    # x 64 lanes x f32x4
+    assert need == bi.WS_COUNTER_BYTES + 16 * 32 * 64 * 16
+    # the XCD hand-over decode keeps the same partials and its counters in
+    # that region
+    assert lab_ws(bi.BI_PATH_DECODE_XCD, 1) == need
+    assert lab_call(bi.BI_PATH_DECODE_XCD) == bi.BI_EWORKSPACE
+    assert lab_call(bi.BI_PATH_DECODE_XCD, ws=FAKE, ws_bytes=need - 1) == bi.BI_EWORKSPACE
     assert lab_call(bi.BI_PATH_DECODE) == bi.BI_EWORKSPACE
     assert lab_call(bi.BI_PATH_DECODE, ws=FAKE, ws_bytes=need - 1) == bi.BI_EWORKSPACE
     # ... growing with M

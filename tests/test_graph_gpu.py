@@ -106,3 +106,64 @@ def test_graph_indexer_topk(bi, rows):
     out = torch.empty((rows, 2048), dtype=torch.int32, device="cuda")
     replay_and_check(torch, lambda: bi.bi_indexer_topk(s, 2048, rs, re, out=out), [out], f"top-k rows={rows}")
 
+
+
+def test_cached_workspace_outlives_a_graph_that_captured_it(bi):
+    # capture a call at M=1 (it uses the stream's cached workspace), then grow
+    # that cache with an eager call at M=128 on the same stream; the captured
+    # graph still writes into the first workspace on replay, so that memory
+    # must not be handed to another tensor.  A sentinel allocated after the
+    # growth must survive the replays, and the replays keep their bits.
+    import torch
+    banner("graph replay after the cached workspace grew")
+    w = wl.router_weights(0)
+    wd, bd = dev(w.w), dev(w.b)
+    stream = torch.cuda.Stream()
+    x1 = dev(wl.router_batch(1, w).x)
+    x128 = dev(wl.router_batch(128, w).x)
+    y1 = torch.empty((1, 256), dtype=torch.float32, device="cuda")
+    with torch.cuda.stream(stream):
+        bi.bi_linear_f32(x1, weight_t(wd), bd, out=y1)
+    torch.cuda.synchronize()
+    ref = host(y1).copy()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        bi.bi_linear_f32(x1, weight_t(wd), bd, out=y1)
+    torch.cuda.synchronize()
+    key = (torch.cuda.current_device(), stream.cuda_stream)
+    before = bi._ws_cache[key].data_ptr()
+    with torch.cuda.stream(stream):
+        big = bi.bi_linear_f32(x128, weight_t(wd), bd)
+    torch.cuda.synchronize()
+    assert bi._ws_cache[key].data_ptr() != before or \
+        bi._ws_cache[key].numel() >= bi.lib().bi_linear_workspace_size(bi.BI_F32, 128, 256, 4096)
+    big_ref = host(big).copy()
+    sentinels = [torch.full((1 << 18,), 3.25, dtype=torch.float32, device="cuda") for _ in range(8)]
+    for r in range(REPLAYS):
+        y1.fill_(float("nan"))
+        with torch.cuda.stream(stream):
+            g.replay()
+        torch.cuda.synchronize()
+        assert_bitwise(host(y1), ref, f"replay {r} after the workspace grew")
+        for s in sentinels:
+            assert bool((s == 3.25).all()), "a tensor allocated after the growth was overwritten"
+    with torch.cuda.stream(stream):
+        again = bi.bi_linear_f32(x128, weight_t(wd), bd)
+    torch.cuda.synchronize()
+    assert_bitwise(host(again), big_ref, "M=128 after the replays")
+    del g
+
+
+def test_workspace_growth_inside_a_capture_is_refused(bi):
+    # a call whose workspace would have to grow during a capture raises
+    # instead of allocating memory the graph would then depend on
+    import torch
+    w = wl.router_weights(0)
+    wd, bd = dev(w.w), dev(w.b)
+    stream = torch.cuda.Stream()
+    x = dev(wl.router_batch(16, w).x)
+    g = torch.cuda.CUDAGraph()
+    with pytest.raises(RuntimeError, match="graph capture"):
+        with torch.cuda.graph(g, stream=stream):
+            bi.bi_linear_f32(x, weight_t(wd), bd)
+    torch.cuda.synchronize()

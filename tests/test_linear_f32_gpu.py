@@ -98,8 +98,10 @@ def test_both_kernel_paths_agree_bitwise(bi, router):
         a = host(bi.bi_lab_linear(x, weight_t(wd), bd, path=bi.BI_PATH_DECODE))
         b = host(bi.bi_lab_linear(x, weight_t(wd), bd, path=bi.BI_PATH_PERSISTENT))
         c = host(bi.bi_lab_linear(x, weight_t(wd), bd, path=bi.BI_PATH_DECODE_WG))
+        h = host(bi.bi_lab_linear(x, weight_t(wd), bd, path=bi.BI_PATH_DECODE_XCD))
         assert_bitwise(a, b, f"decode vs persistent at M={M}")
         assert_bitwise(c, b, f"one-launch decode vs persistent at M={M}")
+        assert_bitwise(h, b, f"XCD hand-over decode vs persistent at M={M}")
 
 
 @pytest.mark.parametrize("K,block_k", [(320, 32), (4096, 64), (2048, 128), (512, 256)])
@@ -180,9 +182,10 @@ def test_poisoned_tail_rows_and_guard_bands(bi, router):
 
 
 def test_poisoned_workspace(bi, router):
-    # the workspace needs no initialisation: every partial is written before
-    # it is read in the same call, so NaN left there must not leak into the
-    # result.  Uses its own workspace through the C ABI.
+    # beyond its zeroed counter region the workspace needs no initialisation:
+    # every partial is written before it is read in the same call, so NaN
+    # left there must not leak into the result.  Uses its own workspace
+    # through the C ABI.
     import ctypes
     import torch
     w, wd, bd = router
@@ -192,6 +195,7 @@ def test_poisoned_workspace(bi, router):
     L = bi.lib()
     need = L.bi_linear_workspace_size(bi.BI_F32, M, N, K)
     ws = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda")   # 0xFFFFFFFF is a NaN
+    ws[:bi.WS_COUNTER_BYTES] = 0           # the counter region starts at zero, by contract
     x = dev(batch.x)
     y = torch.empty((M, N), dtype=torch.float32, device="cuda")
     s = torch.cuda.current_stream()

@@ -65,9 +65,10 @@ def test_tile_ranges_merge_to_three():
 
 def test_table_lines_merge_and_parse():
     e = {"block_k": 128, "m_decode_max": 128, "decode_path": 1, "m_a": 1024, "tile_a": 3, "m_b": 1024,
-         "tile_b": 4, "tile_c": 4}
+         "tile_b": 4, "tile_c": 4, "m_xcd_max": 64}
     line = sweep.table_line("f32", 256, 4096, e)
-    assert line == "{BI_F32, 256, 4096, 128, 128, 1, 1024, 3, 1024, 4, 4},"
+    assert line == "{BI_F32, 256, 4096, 128, 128, 1, 1024, 3, 1024, 4, 4, 64},"
+    assert sweep.parse_table(line)[0]["m_xcd_max"] == 64
     text = sweep.merge_table(sweep.TABLE_HEADER, {"BI_F32,256,4096": line})
     e2 = dict(e, block_k=256)
     text = sweep.merge_table(text, {"BI_F32,256,4096": sweep.table_line("f32", 256, 4096, e2),
@@ -99,3 +100,23 @@ def test_compiled_table_is_what_the_library_serves():
         for t in (r["tile_a"], r["tile_b"], r["tile_c"]):
             assert t == 0 or t in codes, r
         assert r["decode_path"] in (0, 1, 3, 4)
+        # the XCD hand-over serves a prefix of the decode range, and only keys
+        # whose N tiles split evenly over the eight XCDs
+        assert 0 <= r["m_xcd_max"] <= r["m_decode_max"], r
+        assert r["m_xcd_max"] == 0 or (r["N"] // 16) % 8 == 0, r
+        if r["m_xcd_max"]:
+            assert bi.plan_path(dt, 1, r["N"], r["K"]) == bi.BI_PATH_DECODE_XCD, r
+
+
+def test_summary_xcd_prefix_and_other_decode_form():
+    # the XCD hand-over (5) is best up to M=32, the two-launch decode (1)
+    # from 64; decode_path is picked among the non-XCD forms
+    c = cand(128,
+             {1: {1: 6.7, 5: 5.6, 3: 13.0}, 8: {1: 7.0, 5: 5.8}, 32: {1: 8.0, 5: 6.7}, 64: {1: 9.4, 5: 9.8},
+              128: {1: 12.8, 5: 13.3}},
+             {1: {3: 40.0}, 8: {3: 40.0}, 32: {3: 40.0}, 64: {3: 30.0}, 128: {3: 31.0}, 4096: {10: 90.0}})
+    s = sweep.summarize(c)
+    assert s["m_xcd_max"] == 32 and s["decode_path"] == 1 and s["m_decode_max"] == 128
+    # a hand-over that loses at the first point serves nothing
+    c["decode"][1][5] = 7.0
+    assert sweep.summarize(c)["m_xcd_max"] == 0

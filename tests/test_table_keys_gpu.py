@@ -2,8 +2,8 @@
 table sets for it.
 
 The recipe is a function of (dtype, N, K) alone; M only chooses the kernel
-path (decode up to m_decode_max, then up to three persistent tile shapes
-split at m_a and m_b).  For each key, two probe rows are planted at the first
+path (the XCD hand-over decode up to m_xcd_max, another decode form up to
+m_decode_max, then up to three persistent tile shapes split at m_a and m_b).  For each key, two probe rows are planted at the first
 and last position of batches whose sizes sit on both sides of every one of
 those boundaries; the probe rows must keep their bits at every M, and agree
 with the oracle (fp32 keys within atol 2e-3 / rtol 1e-4, GateLinear page,
@@ -25,8 +25,9 @@ TABLE_ROWS = sweep.parse_table(open(sweep.TABLE).read())
 
 def boundary_ms(row):
     ms = {1, 2, 17}
-    for m in (row["m_decode_max"], row["m_a"], row["m_b"]):
-        ms.update({m, m + 1})
+    for m in (row["m_decode_max"], row["m_a"], row["m_b"], row["m_xcd_max"]):
+        if m > 0:
+            ms.update({m, m + 1})
     return sorted(ms)
 
 @pytest.fixture(scope="module")
