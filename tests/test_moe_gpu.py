@@ -11,13 +11,10 @@ Bars:
   gap exceeds TAU (near ties may legitimately resolve either way; they are
   listed and checked stage-wise);
 * probabilities: rtol 1e-5 against the oracle's softmax of the same ids;
-* outputs: rtol 1e-2 and atol = 32 * 2^-8 / sqrt(topk * I) * rms(out)
-  against the oracle re-run with the GPU's ids.  The GPU rounds its fp32
-  values and the oracle its binary64 values to the bf16 storage points, so a
-  value near a rounding boundary can land one bf16 ulp apart; one such flip
-  moves an output by about 2^-8 |a| |w2|, while rms(out) grows like
-  sqrt(topk * I) |a| |w2|.  The bound allows ~8 flips of a 4-sigma activation
-  in one output (1.6e-3 rms at the Qwen shape);
+* outputs: rtol 1e-2 and atol = c * rms(out) against the oracle re-run with
+  the GPU's ids, c about twice the worst output shift that storage-point
+  flips caused in the stage-wise measurement (tests/moe_bars.py: 3.5e-3 at
+  the Qwen shape, 4.5e-3 for the small layers);
 * probe tokens: ids, probs and outputs bitwise equal across every M.
 """
 import numpy as np
@@ -26,14 +23,11 @@ import pytest
 import oracle
 import workloads as wl
 from tests.gpu_util import assert_bitwise, assert_close, banner, bf16_to_f32, dev, host, weight_t
+from tests.moe_bars import RTOL, moe_atol
 
 pytestmark = pytest.mark.gpu
 
 TAU = 1e-4
-
-
-def moe_atol(rms, topk, I):
-    return 32.0 * 2.0 ** -8 / np.sqrt(topk * I) * rms
 
 
 @pytest.fixture(scope="module")
@@ -92,7 +86,7 @@ def test_moe_sweep_against_oracle_and_invariant(bi, moe):
         yf, _, pf, _ = oracle.moe(xs, w.w_router, None, w.w13, w.w2, wl.MOE_TOPK, ids=ids[rows])
         assert_close(probs[rows], pf, 0.0, 1e-5, f"probs M={M}")
         rms = float(np.sqrt(np.mean(yf.astype(np.float64) ** 2)))
-        err = assert_close(y[rows], yf, moe_atol(rms, wl.MOE_TOPK, wl.MOE_I), 1e-2, f"moe out M={M}")
+        err = assert_close(y[rows], yf, moe_atol(rms, wl.MOE_H), RTOL, f"moe out M={M}")
         print(f"M={M}: rms(out)={rms:.3e} max|err|={err:.2e} near-tie tokens={int((~clear).sum())}")
         for pid, pos in batch.probes.items():
             for p in pos:
@@ -113,7 +107,7 @@ def test_moe_repeat_and_poisoned_workspace(bi, moe):
     y0, i0, p0 = run_moe(bi, batch.x, d)
     s = torch.cuda.current_stream()
     ws = bi._ws_cache[(torch.cuda.current_device(), s.cuda_stream)]
-    ws.fill_(0xFF)
+    ws[bi.WS_COUNTER_BYTES:].fill_(0xFF)       # the counter region stays zero, by contract
     y1, i1, p1 = run_moe(bi, batch.x, d)
     assert_bitwise(y1, y0, "after poisoning the workspace")
     np.testing.assert_array_equal(i1, i0)
@@ -132,7 +126,7 @@ def test_moe_zero_router_and_zero_down_projection(bi, moe):
     assert np.all(probs == np.float32(1.0 / 128.0))
     yo, _, _, _ = oracle.moe(batch.x[:4], np.zeros_like(w.w_router), None, w.w13, w.w2, 8)
     rms = float(np.sqrt(np.mean(yo.astype(np.float64) ** 2)))
-    assert_close(y[:4], yo, moe_atol(rms, 8, wl.MOE_I), 1e-2, "zero-router outputs")
+    assert_close(y[:4], yo, moe_atol(rms, wl.MOE_H), RTOL, "zero-router outputs")
     banner("moe zero down projection")
     y2, _, _ = run_moe(bi, batch.x, dict(d, w2=torch.zeros_like(d["w2"])))
     assert np.all(y2 == 0.0)
@@ -154,4 +148,4 @@ def test_moe_small_shape_full_oracle(bi, E, topk):
         yf, _, pf, _ = oracle.moe(x, w.w_router, b, w.w13, w.w2, topk, ids=ids)
         assert_close(probs, pf, 0.0, 1e-5, f"small probs M={M}")
         rms = float(np.sqrt(np.mean(yf.astype(np.float64) ** 2)))
-        assert_close(y, yf, moe_atol(rms, topk, 64), 1e-2, f"small moe M={M}")
+        assert_close(y, yf, moe_atol(rms, 256), RTOL, f"small moe M={M}")
