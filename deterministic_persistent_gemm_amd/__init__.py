@@ -67,10 +67,11 @@ _lib.bi_lab_stream_read.argtypes = [_P, _I64, _P, _I32, _P]
 _lib.bi_lab_clock.argtypes = [_P, _I32, _I32, _P]
 _lib.bi_lab_plan.argtypes = [_I32, _I64, _I64, _I64, ctypes.POINTER(_I32)]
 _lib.bi_lab_moe_layout.argtypes = [_I64, _I64, _I64, _I64, _I64, ctypes.POINTER(_I64)]
+_lib.bi_linear_f32_noalloc.argtypes = [_P, _I64, _P, _I64, _P, _P, _I64, _I64, _I64, _I64, _P]
 for _f in (_lib.bi_linear_f32, _lib.bi_linear_bf16, _lib.bi_negctl_linear_f32, _lib.bi_lab_linear,
            _lib.bi_moe_grouped_gemm, _lib.bi_describe_recipe, _lib.bi_indexer_topk,
            _lib.bi_moe_grouped_gemm_ex, _lib.bi_lab_xcc_ids, _lib.bi_lab_empty, _lib.bi_lab_stream_read,
-           _lib.bi_lab_clock, _lib.bi_lab_plan, _lib.bi_lab_moe_layout):
+           _lib.bi_lab_clock, _lib.bi_lab_plan, _lib.bi_lab_moe_layout, _lib.bi_linear_f32_noalloc):
     _f.restype = _I32
 for _f in (_lib.bi_linear_workspace_size, _lib.bi_lab_workspace_size, _lib.bi_moe_workspace_size):
     _f.restype = _SZ
@@ -196,6 +197,23 @@ def bi_linear_f32(x: torch.Tensor, wt: torch.Tensor, bias: torch.Tensor | None =
     _check(_lib.bi_linear_f32(_ptr(x), x.stride(0), _ptr(wt), wt.stride(1), _ptr(bias), _ptr(out),
                               out.stride(0), M, N, K, _ptr(ws), 0 if ws is None else ws.numel(),
                               ctypes.c_void_p(s.cuda_stream)), "bi_linear_f32")
+    return out
+
+
+def bi_linear_f32_noalloc(x: torch.Tensor, wt: torch.Tensor, bias: torch.Tensor | None, out: torch.Tensor
+                          ) -> torch.Tensor:
+    """bi_linear_f32 into a caller-given `out`, with the library's static
+    scratch instead of a workspace: nothing is allocated (calls that overlap
+    on one GPU race on that scratch)."""
+    _check_xw(x, wt, torch.float32, "bi_linear_f32_noalloc")
+    M, K = x.shape
+    N = wt.shape[1]
+    _check_bias(bias, N, x.device, "bi_linear_f32_noalloc")
+    _check_out(out, (M, N), (torch.float32,), x.device, "bi_linear_f32_noalloc")
+    s = _stream(x.device)
+    _check(_lib.bi_linear_f32_noalloc(_ptr(x), x.stride(0), _ptr(wt), wt.stride(1), _ptr(bias), _ptr(out),
+                                      out.stride(0), M, N, K, ctypes.c_void_p(s.cuda_stream)),
+           "bi_linear_f32_noalloc")
     return out
 
 

@@ -22,7 +22,8 @@ LIB = os.path.join(PKG, "libbi.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["bi_abi.cpp", "bi_plan.cpp", "bi_linear.hip", "bi_moe.hip", "bi_topk.hip", "bi_lab.hip"]
+SOURCES = ["bi_abi.cpp", "bi_plan.cpp", "bi_linear.hip", "bi_moe.hip", "bi_topk.hip", "bi_lab.hip",
+           "bi_noalloc.hip"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-ffp-contract=off", "-Wall", "-Wno-unused-function",
           "-I", INCLUDE, "-I", CSRC]

@@ -59,6 +59,41 @@ bi_status_t run_linear(int xkind, const void* x, int64_t ldx, const void* w, int
 
 }  // namespace
 
+namespace bi {
+
+bi_status_t linear_f32_checked(const float* x, int64_t ldx, const float* w, int64_t ldw, const float* bias,
+                               float* y, int64_t ldy, int64_t M, int64_t N, int64_t K, size_t* ws_needed)
+{
+    bi_status_t st = check_linear(x, ldx, w, ldw, bias, y, ldy, M, N, K, 4, 4, 4);
+    if (st != BI_OK || M == 0) {
+        *ws_needed = 0;
+        return st;
+    }
+    bi_recipe_t r;
+    if ((st = recipe_for(BI_F32, N, K, &r)) != BI_OK)
+        return st;
+    Plan p;
+    if ((st = make_plan(r, BI_PATH_AUTO, M, N, K, &p)) != BI_OK)
+        return st;
+    *ws_needed = p.ws_bytes;
+    return BI_OK;
+}
+
+bi_status_t linear_f32_run(const float* x, int64_t ldx, const float* w, int64_t ldw, const float* bias, float* y,
+                           int64_t ldy, int64_t M, int64_t N, int64_t K, void* ws, size_t ws_bytes,
+                           hipStream_t stream)
+{
+    bi_status_t st = check_linear(x, ldx, w, ldw, bias, y, ldy, M, N, K, 4, 4, 4);
+    if (st != BI_OK || M == 0)
+        return st;
+    bi_recipe_t r;
+    if ((st = recipe_for(BI_F32, N, K, &r)) != BI_OK)
+        return st;
+    return run_linear(kXF32, x, ldx, w, ldw, bias, y, 0, ldy, M, N, K, r, BI_PATH_AUTO, ws, ws_bytes, stream);
+}
+
+}  // namespace bi
+
 extern "C" {
 
 const char* bi_status_str(bi_status_t s)
@@ -103,14 +138,7 @@ bi_status_t bi_linear_f32(const float* x, int64_t ldx, const float* w, int64_t l
                           float* y, int64_t ldy, int64_t M, int64_t N, int64_t K, void* ws,
                           size_t ws_bytes, hipStream_t stream)
 {
-    bi_status_t st = check_linear(x, ldx, w, ldw, bias, y, ldy, M, N, K, 4, 4, 4);
-    if (st != BI_OK || M == 0)
-        return st;
-    bi_recipe_t r;
-    if ((st = recipe_for(BI_F32, N, K, &r)) != BI_OK)
-        return st;
-    return run_linear(kXF32, x, ldx, w, ldw, bias, y, 0, ldy, M, N, K, r, BI_PATH_AUTO, ws, ws_bytes,
-                      stream);
+    return linear_f32_run(x, ldx, w, ldw, bias, y, ldy, M, N, K, ws, ws_bytes, stream);
 }
 
 bi_status_t bi_linear_bf16(const uint16_t* x, int64_t ldx, const uint16_t* w, int64_t ldw,

@@ -4,6 +4,7 @@
 #include <hip/hip_runtime_api.h>
 #include <stdint.h>
 
+#include "bi.h"
 #include "bi_plan.h"
 
 namespace bi {
@@ -29,6 +30,14 @@ struct LinearArgs {
 // kDecodeCounterBytes) for a consumer that folds them itself in the same order.
 hipError_t launch_linear(int xkind, const LinearArgs& a, const Plan& p, void* ws, hipStream_t s,
                          bool fold = true);
+
+// bi_linear_f32 in two steps (bi_abi.cpp): the validation and the workspace
+// bytes the automatic plan needs (nothing enqueued), and the call itself.
+bi_status_t linear_f32_checked(const float* x, int64_t ldx, const float* w, int64_t ldw, const float* bias,
+                               float* y, int64_t ldy, int64_t M, int64_t N, int64_t K, size_t* ws_needed);
+bi_status_t linear_f32_run(const float* x, int64_t ldx, const float* w, int64_t ldw, const float* bias, float* y,
+                           int64_t ldy, int64_t M, int64_t N, int64_t K, void* ws, size_t ws_bytes,
+                           hipStream_t stream);
 
 // Diagnostic kernels (bi_lab.hip).
 hipError_t launch_xcc_ids(uint32_t* out, int gx, int gy, hipStream_t s);

@@ -117,6 +117,23 @@ bi_status_t bi_linear_bf16(const uint16_t* x, int64_t ldx,
                            int64_t M, int64_t N, int64_t K,
                            void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* bi_linear_f32 for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation):
+ * the same arguments, plan and kernels, hence the same bits, with no caller
+ * workspace.  The workspace is a static device array of the library, 16 MiB
+ * + 16 KiB per GPU, held until the process ends; shapes whose plan needs more
+ * (none of the compiled fp32 keys up to its decode limit) return
+ * BI_EWORKSPACE before anything is enqueued.  Its first call on a device
+ * finds the array's address and clears its counters with a small kernel on
+ * `stream`.  The library allocates nothing here.  All calls on one GPU share
+ * the array: calls that overlap on one GPU (other streams, other host threads)
+ * race and must be serialised by the caller. */
+bi_status_t bi_linear_f32_noalloc(const float* x, int64_t ldx,
+                                  const float* w, int64_t ldw,
+                                  const float* bias,
+                                  float* y, int64_t ldy,
+                                  int64_t M, int64_t N, int64_t K, hipStream_t stream);
+
 /* Batch-invariant MoE layer with gated SwiGLU experts (fused-MoE page, "What's
  * included"; strict-review summary):
  *   logits = fp32(x) . w_router^T (+ b_router)      fp32 router, recipe of

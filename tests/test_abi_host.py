@@ -199,3 +199,15 @@ def test_direct_to_lds_decode_scope():
     assert call(bi.BI_BF16, 1536, 2048, 1) == bi.BI_EUNSUPPORTED                  # 512-k tile partials
     assert call(bi.BI_BF16, 4096, 4096, 65) == bi.BI_EUNSUPPORTED                 # more than 4 M tiles
     assert call(bi.BI_BF16, 64, 480, 1, block_k=480) == bi.BI_EUNSUPPORTED        # K not a phase multiple
+
+
+def test_noalloc_entry_rejects_on_the_host():
+    # validation and the scratch-size check come before any HIP call: an
+    # unlisted fp32 key whose decode partials (8 M tiles x 256 N tiles x 32 k
+    # tiles x 1 KiB at M = 128) exceed the 16 MiB static scratch, bad
+    # pointers and pitches; M = 0 is a no-op
+    f = L.bi_linear_f32_noalloc
+    assert f(FAKE, 4096, FAKE, 4096, None, FAKE, 4096, 128, 4096, 4096, None) == bi.BI_EWORKSPACE
+    assert f(None, 4096, FAKE, 4096, None, FAKE, 256, 1, 256, 4096, None) == bi.BI_EINVAL
+    assert f(FAKE, 4095, FAKE, 4096, None, FAKE, 256, 1, 256, 4096, None) == bi.BI_EINVAL
+    assert f(FAKE, 4096, FAKE, 4096, None, FAKE, 256, 0, 256, 4096, None) == bi.BI_OK
