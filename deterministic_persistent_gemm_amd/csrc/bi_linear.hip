@@ -51,18 +51,28 @@ __device__ __forceinline__ void store_elem(const LinearArgs& a, int row, int col
 
 // acc holds rows row0 + q (q = 0..3) of column col.  The bias is one fp32 add
 // after the full reduction; without a bias nothing is added (adding +0.0
-// would turn a -0.0 result into +0.0).  Its element is loaded once, before
-// the rows, so the rows' stores do not each wait on a load.
-__device__ __forceinline__ void store_acc(const LinearArgs& a, int row0, int col, f32x4 acc)
+// would turn a -0.0 result into +0.0).  b is the bias element of col, loaded
+// by the caller (load_bias), possibly long before.
+__device__ __forceinline__ void store_acc(const LinearArgs& a, int row0, int col, f32x4 acc, float b)
 {
     if (col >= a.N)
         return;
     const bool has_bias = a.bias != nullptr;
-    const float b = has_bias ? a.bias[col] : 0.f;
 #pragma unroll
     for (int q = 0; q < 4; ++q)
         if (row0 + q < a.M)
             store_elem(a, row0 + q, col, has_bias ? acc[q] + b : acc[q]);
+}
+
+__device__ __forceinline__ float load_bias(const LinearArgs& a, int col)
+{
+    return (a.bias && col < a.N) ? a.bias[col] : 0.f;
+}
+
+// The same with the bias element loaded here, once, before the rows.
+__device__ __forceinline__ void store_acc(const LinearArgs& a, int row0, int col, f32x4 acc)
+{
+    store_acc(a, row0, col, acc, load_bias(a, col));
 }
 
 // -------------------------------------------------------------------- decode
@@ -112,6 +122,9 @@ __global__ __launch_bounds__(64) void k_decode(LinearArgs a, int kbpt, int tiles
     const int t = blockIdx.x / ntiles;
     const int nt = blockIdx.x % ntiles;
     const int mt0 = blockIdx.y * MT;
+    // the wave that finishes an output tile adds the bias last; its element
+    // is requested now so that the epilogue never waits on memory
+    const float bcol = (tiles_k == 1 || HANDOFF) ? load_bias(a, nt * 16 + acc_col(lane)) : 0.f;
 
     const int64_t kbase = (int64_t)t * kbpt * kKBlock + kSlotLen * g;
     const EW* wp = reinterpret_cast<const EW*>(a.w) + (int64_t)(nt * 16 + r) * a.ldw + kbase;
@@ -133,8 +146,14 @@ __global__ __launch_bounds__(64) void k_decode(LinearArgs a, int kbpt, int tiles
     FragOf<OX> xf0[CH][MT], xf1[CH][MT];
     auto load_chunk = [&](FragOf<OW> (&wf)[CH][1], FragOf<OX> (&xf)[CH][MT], int c) {
 #pragma unroll
-        for (int i = 0; i < CH; ++i)
-            load_frag<OW>(wf[i][0], wp + (int64_t)(c + i) * kKBlock);
+        for (int i = 0; i < CH; ++i) {
+            // the hand-over serves small M: every weight element is read by
+            // exactly one wave, so it streams past the caches
+            if constexpr (HANDOFF)
+                load_frag_nt<OW>(wf[i][0], wp + (int64_t)(c + i) * kKBlock);
+            else
+                load_frag<OW>(wf[i][0], wp + (int64_t)(c + i) * kKBlock);
+        }
 #pragma unroll
         for (int m = 0; m < MT; ++m)
 #pragma unroll
@@ -169,7 +188,7 @@ __global__ __launch_bounds__(64) void k_decode(LinearArgs a, int kbpt, int tiles
         if (mt >= mtiles || row0 >= a.M)
             continue;
         if (tiles_k == 1)
-            store_acc(a, row0, col, P[m][0]);
+            store_acc(a, row0, col, P[m][0], bcol);
         else
             partials[(((int64_t)mt * ntiles + nt) * tiles_k + t) * 64 + lane] = P[m][0];
     }
@@ -209,7 +228,7 @@ __global__ __launch_bounds__(64) void k_decode(LinearArgs a, int kbpt, int tiles
                     if (i < n)
                         acc = (u0 + i == 0) ? v[i] : acc + v[i];
             }
-            store_acc(a, row0, col, acc);
+            store_acc(a, row0, col, acc, bcol);
         }
     }
 }
@@ -226,6 +245,7 @@ __global__ __launch_bounds__(64) void k_decode_fold(LinearArgs a, int tiles_k,
     const int row0 = mt * 16 + acc_row(lane, 0);
     if (row0 >= a.M)
         return;
+    const float b = load_bias(a, nt * 16 + acc_col(lane));
     const f32x4* p = partials + ((int64_t)mt * ntiles + nt) * tiles_k * 64 + lane;
     constexpr int kBatch = 32;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -241,7 +261,7 @@ __global__ __launch_bounds__(64) void k_decode_fold(LinearArgs a, int tiles_k,
             if (i < n)
                 acc = (u0 + i == 0) ? v[i] : acc + v[i];
     }
-    store_acc(a, row0, nt * 16 + acc_col(lane), acc);
+    store_acc(a, row0, nt * 16 + acc_col(lane), acc, b);
 }
 
 // One workgroup per (16-row M tile, 16-column N tile), NW waves.  Wave w
