@@ -478,23 +478,7 @@ def floors_leg(torch, bi, dev):
         torch.cuda.synchronize()
         o = out[:grid].cpu().numpy().astype("float64")
         res[name] = round(float(sorted(o[:, 0] / o[:, 1])[grid // 2] * 100.0), 1)
-    res["smi_sclk"] = smi_sclk()
     return res
-
-
-def smi_sclk():
-    """The current shader clock as rocm-smi reports it (None if unavailable)."""
-    import subprocess
-    try:
-        out = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=20)
-        data = json.loads(out.stdout)
-        for card in data.values():
-            for k, v in card.items():
-                if "sclk" in k.lower():
-                    return v
-    except Exception:
-        return None
-    return None
 
 
 def roofline_line(dom, step_gbps, floors):

@@ -39,7 +39,13 @@
  *    rejected call enqueues nothing.  There is no fallback to a
  *    non-invariant path: a shape the recipe table cannot serve returns
  *    BI_EUNSUPPORTED.  M == 0 returns BI_OK and enqueues nothing.
- *  - Thread safety: the library has no mutable global state.
+ *  - Global state and thread safety: the library's mutable global state is
+ *    per-device values written once and then only read (the compute-unit
+ *    count; the device address of bi_linear_f32_noalloc's static scratch,
+ *    behind a once-flag) and that scratch array itself, which the calls of
+ *    bi_linear_f32_noalloc on one GPU share.  Every other entry point reads
+ *    and writes only caller memory, so calls from several host threads are
+ *    safe as long as they do not share a workspace or an output.
  */
 #ifndef BI_H
 #define BI_H
@@ -213,15 +219,27 @@ bi_status_t bi_moe_grouped_gemm_ex(const uint16_t* x,
                                    int32_t* topk_ids, float* topk_probs, float* y,
                                    void* ws, size_t ws_bytes, hipStream_t stream);
 
-/* Workspace bytes the calls above need for a given problem (0 if none). */
+/* Workspace bytes the calls above need for a given problem (0 if none, or if
+ * the arguments are invalid).  For the linear layer the workspace holds the
+ * counter region and the k tile partials of the decode kernel M selects
+ * (GateLinear page, "A correction to why the key excludes M": M picks the
+ * kernel shape, never the recipe), so its size depends on M while the
+ * results do not.  For the MoE layer it also holds the router logits, the
+ * expert-sorted routing, the bf16 activations and the fp32 slot partials
+ * (fused-MoE page, "What's included": expert counts and routing stay on the
+ * device).  Pure host computations; nothing is enqueued. */
 size_t bi_linear_workspace_size(int32_t dtype, int64_t M, int64_t N, int64_t K);
 size_t bi_moe_workspace_size(int64_t M, int64_t H, int64_t E, int64_t I, int64_t topk);
 
-/* The recipe of a key; takes no M.  Returns BI_EUNSUPPORTED for keys the
- * table cannot serve. */
+/* The recipe of a key; takes no M (GateLinear page, "What" and "A correction
+ * to why the key excludes M": the config is keyed on (dtype, N, K) and never
+ * on M).  out: host pointer.  Returns BI_EUNSUPPORTED for keys the table
+ * cannot serve, BI_EINVAL for a NULL out or an unknown dtype. */
 bi_status_t bi_describe_recipe(int32_t dtype, int64_t N, int64_t K, bi_recipe_t* out);
 
-/* Static string for a status code. */
+/* Static, never-freed string naming a status code (Sparse-MLA page, the
+ * fail-closed review notes: a call that cannot keep batch invariance reports
+ * an error instead of returning a batch-dependent result). */
 const char* bi_status_str(bi_status_t status);
 
 /* ---------------------------------------------------------------------------

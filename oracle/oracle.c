@@ -25,12 +25,12 @@
  *    expert GEMMs, and a top-k reduction with unit weights summed in fp64;
  *    review summary: gate|up half-split and a fixed slot-order reduction.
  *  - "[BI][DSv4] Pin sparse-MLA decode and prefill scheduling", commit notes
- *    of the deterministic per-row top-k: score descending, exact ties by
- *    ascending index, -0.0 treated as +0.0; for the indexer's top-k, every
- *    fp32 bit pattern is ranked by a monotone int32 key, lanes outside the
- *    row's window rank below every lane inside it (validity first), and the
- *    selection is emitted in ascending column order, row-local, with a -1
- *    tail.
+ *    of the deterministic per-row top-k: the larger score comes first, equal
+ *    scores are taken in column order, and a negative zero counts as a
+ *    positive one; for the indexer's top-k every fp32 bit pattern gets a
+ *    monotone int32 rank, a lane outside the row's window never outranks one
+ *    inside it, and the chosen columns are returned sorted, counted from the
+ *    window start, with -1 filling the unused slots.
  */
 #include <math.h>
 #include <stdint.h>

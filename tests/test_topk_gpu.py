@@ -81,27 +81,74 @@ SPECIALS = [0x00000000, 0x80000000, 0x7F800000, 0xFF800000, 0x7FC00000, 0xFFC000
             0xFFFFFFFF, 0xFFFFFFFE, 0x7FFFFFFF, 0x3F800000]
 
 
-@pytest.mark.parametrize("topk", [512, 1024, 2048])
-def test_special_bit_pattern_matrix(bi, topk):
-    g = np.random.default_rng(topk)
+def special_matrix(seed, copies=1):
+    """Rows dominated by each special pattern in three window shapes, the
+    whole set repeated `copies` times with fresh random fill."""
+    g = np.random.default_rng(seed)
     cols = 8192
-    rows = len(SPECIALS) * 3
+    rows = len(SPECIALS) * 3 * copies
     bits = g.integers(0, 2**32, (rows, cols), dtype=np.uint64).astype(np.uint32)
     rs = np.zeros(rows, np.int64)
     re = np.full(rows, cols, np.int64)
-    for i, b in enumerate(SPECIALS):
-        for w in range(3):
-            r = 3 * i + w
-            # a plateau of the special pattern, wide enough that the cut lands in it
-            mask = g.random(cols) < 0.6
-            bits[r, mask] = b
-            if w == 1:                      # window narrower than top-k inside a wider row
-                rs[r], re[r] = 1, 31
-            elif w == 2:                    # window wide enough to truncate at every top-k
-                rs[r], re[r] = 700, 3300
-    s = bits.view(np.float32)
+    for c in range(copies):
+        for i, b in enumerate(SPECIALS):
+            for w in range(3):
+                r = (c * len(SPECIALS) + i) * 3 + w
+                # a plateau of the special pattern, wide enough that the cut lands in it
+                mask = g.random(cols) < 0.6
+                bits[r, mask] = b
+                if w == 1:                      # window narrower than top-k inside a wider row
+                    rs[r], re[r] = 1, 31
+                elif w == 2:                    # window wide enough to truncate at every top-k
+                    rs[r], re[r] = 700, 3300
+    return bits.view(np.float32), rs, re
+
+
+@pytest.mark.parametrize("topk", [512, 1024, 2048])
+def test_special_bit_pattern_matrix(bi, topk):
+    s, rs, re = special_matrix(topk)
     banner(f"topk special bit patterns topk={topk}")
     check(bi, s, topk, rs, re, what="special patterns")
+
+
+# From 1024 rows the kernel runs its 512-thread form (16 columns per thread,
+# halved histogram copies); the inputs below reach it with every special
+# pattern, the scalar load path and each top-k size.
+@pytest.mark.parametrize("topk", [512, 1024, 2048])
+def test_special_bit_pattern_matrix_wide_form(bi, topk):
+    s, rs, re = special_matrix(topk + 1, copies=19)          # 1026 rows
+    assert s.shape[0] >= 1024
+    banner(f"topk special bit patterns, 512-thread form, topk={topk}")
+    check(bi, s, topk, rs, re, what="special patterns, wide form")
+
+
+@pytest.mark.parametrize("pitch_extra", [1, 37])
+def test_odd_row_pitch_wide_form(bi, pitch_extra):
+    g = np.random.default_rng(100 + pitch_extra)
+    rows, cols = 1030, 1000
+    s = np.maximum(g.standard_normal((rows, cols)), 0).astype(np.float32)
+    rs = g.integers(0, 500, rows)
+    re = rs + g.integers(0, 600, rows)
+    banner(f"topk strided pitch={cols + pitch_extra}, 512-thread form")
+    check(bi, s, 512, rs, re, pitch=cols + pitch_extra, what="strided, wide form")
+
+
+def test_both_forms_select_the_same_rows(bi):
+    # the same rows in a 1023-row batch (1024-thread form) and a 1024-row
+    # batch (512-thread form) give the same selection
+    g = np.random.default_rng(4)
+    cols = 8192
+    s = np.where(g.random((1024, cols)) < 0.5, 0.0, g.standard_normal((1024, cols))).astype(np.float32)
+    s = (s.view(np.uint32) & 0xFFFF0000).view(np.float32)           # bf16-rounded ties, as the indexer has
+    rs = g.integers(-5, 4000, 1024)
+    re = rs + g.integers(0, 8000, 1024)
+    for topk in wl.INDEXER_TOPK:
+        banner(f"topk 1023 vs 1024 rows topk={topk}")
+        a = gpu_topk(bi, s[:1023], topk, rs[:1023], re[:1023])
+        b = gpu_topk(bi, s, topk, rs, re)
+        assert np.array_equal(a, b[:1023]), f"the two forms differ at topk={topk}"
+    want = oracle.topk_rows(s, 2048, rs.astype(np.int64), re.astype(np.int64))
+    assert np.array_equal(b, want)
 
 
 def test_window_offset_invariance_and_degenerate_rows(bi):
