@@ -40,11 +40,12 @@ FP32_MFMA_PEAK_TFLOPS = 157.3
 BF16_MFMA_PEAK_TFLOPS = 2500.0
 N_COPIES = 96
 
-# HBM bytes per decode call (k_decode + k_decode_fold), averaged over the sweep, from two rocprofv3
-# PMC runs: FETCH_SIZE scaled x2.0 and WRITE_SIZE x1.0 by a 512 MiB copy of known size (see
-# profiles/router_decode_hbm_bytes.md).  Valid only for the kernel sources with this digest; any
-# later change to them reports traffic as null until the counters are taken again.
-MEASURED_TRAFFIC = {"sources_sha256": "773602231e0e90f74c12c752f74117d8bef3e26e1ce315da533698aa560d4425", "bytes_per_call": 10170846}
+# HBM bytes per launch of the dominant kernel (the XCD hand-over decode), averaged over the sweep's
+# calls it serves (M = 1 .. 64), from two rocprofv3 PMC runs: FETCH_SIZE scaled x2.0 and WRITE_SIZE
+# x1.0 by a 512 MiB copy of known size (see profiles/router_decode_hbm_bytes.md).  Valid only for the
+# kernel sources with this digest; any later change to them reports traffic as null until the counters
+# are taken again.
+MEASURED_TRAFFIC = {"sources_sha256": "f964c8fac37fbe5e8b83c3a21d6897478bf8904d2887f0c59b4e2c6a17dc0b51", "bytes_per_call": 7936328}
 KERNEL_SOURCES = ("bi_device.h", "bi_launch.h", "bi_linear.hip", "bi_plan.cpp", "bi_plan.h", "bi_table.inc")
 
 
