@@ -479,6 +479,43 @@ def floors_leg(torch, bi, dev):
         torch.cuda.synchronize()
         o = out[:grid].cpu().numpy().astype("float64")
         res[name] = round(float(sorted(o[:, 0] / o[:, 1])[grid // 2] * 100.0), 1)
+    res.update(ceilings_leg(torch, bi, dev))
+    return res
+
+
+def ceilings_leg(torch, bi, dev):
+    """What a compute unit sustains with nothing else in the way: LDS read
+    bytes per shader clock (one 16-wave workgroup per CU reading 64 KiB of LDS
+    with conflict-free 16-byte loads) and the issue interval of the recipe's
+    MFMA instructions on register operands (eight waves per CU, two per SIMD,
+    eight independent chains each).  Cycles and clock come from the probes'
+    own shader-cycle and wall-tick counters (median over the workgroups)."""
+    grid = 256
+    out = torch.zeros((grid, 3), dtype=torch.int64, device=dev)
+
+    def run(launch):
+        launch()                      # warm-up
+        torch.cuda.synchronize()
+        launch()
+        torch.cuda.synchronize()
+        o = out.cpu().numpy().astype("float64")
+        cyc = float(sorted(o[:, 0])[grid // 2])
+        mhz = float(sorted(o[:, 0] / o[:, 1])[grid // 2] * 100.0)
+        return cyc, mhz
+
+    res = {}
+    iters = 1000
+    cyc, mhz = run(lambda: bi.bi_lab_lds_read(out, grid, iters))
+    res["lds_read"] = {"B_per_clk_per_CU": round(iters * 65536 / cyc, 1), "MHz": round(mhz, 1),
+                       "probe": "16 waves per CU, ds_read_b128, conflict-free"}
+    for name, dtype, iters, flop, peak in (("mfma_bf16_16x16x32", bi.BI_BF16, 2000, 16384, 2500.0),
+                                           ("mfma_f32_16x16x4", bi.BI_F32, 1000, 2048, FP32_MFMA_PEAK_TFLOPS)):
+        cyc, mhz = run(lambda d=dtype, n=iters: bi.bi_lab_mfma_rate(out, d, grid, n))
+        per = cyc / (iters * 8 * 2)            # two waves per SIMD, eight MFMAs per round
+        tf = 256 * 4 * mhz * 1e6 / per * flop / 1e12
+        res[name] = {"cycles_per_instr_per_SIMD": round(per, 2), "MHz": round(mhz, 1),
+                     "TFLOPs": round(tf, 1), "frac_of_peak": round(tf / peak, 3),
+                     "probe": "register operands, 8 waves per CU, 8 independent chains per wave"}
     return res
 
 

@@ -65,13 +65,16 @@ _lib.bi_lab_xcc_ids.argtypes = [_P, _I32, _I32, _P]
 _lib.bi_lab_empty.argtypes = [_I32, _I32, _P]
 _lib.bi_lab_stream_read.argtypes = [_P, _I64, _P, _I32, _P]
 _lib.bi_lab_clock.argtypes = [_P, _I32, _I32, _P]
+_lib.bi_lab_lds_read.argtypes = [_P, _I32, _I32, _P]
+_lib.bi_lab_mfma_rate.argtypes = [_P, _I32, _I32, _I32, _P]
 _lib.bi_lab_plan.argtypes = [_I32, _I64, _I64, _I64, ctypes.POINTER(_I32)]
 _lib.bi_lab_moe_layout.argtypes = [_I64, _I64, _I64, _I64, _I64, ctypes.POINTER(_I64)]
 _lib.bi_linear_f32_noalloc.argtypes = [_P, _I64, _P, _I64, _P, _P, _I64, _I64, _I64, _I64, _P]
 for _f in (_lib.bi_linear_f32, _lib.bi_linear_bf16, _lib.bi_negctl_linear_f32, _lib.bi_lab_linear,
            _lib.bi_moe_grouped_gemm, _lib.bi_describe_recipe, _lib.bi_indexer_topk,
            _lib.bi_moe_grouped_gemm_ex, _lib.bi_lab_xcc_ids, _lib.bi_lab_empty, _lib.bi_lab_stream_read,
-           _lib.bi_lab_clock, _lib.bi_lab_plan, _lib.bi_lab_moe_layout, _lib.bi_linear_f32_noalloc):
+           _lib.bi_lab_clock, _lib.bi_lab_plan, _lib.bi_lab_moe_layout, _lib.bi_linear_f32_noalloc,
+           _lib.bi_lab_lds_read, _lib.bi_lab_mfma_rate):
     _f.restype = _I32
 for _f in (_lib.bi_linear_workspace_size, _lib.bi_lab_workspace_size, _lib.bi_moe_workspace_size):
     _f.restype = _SZ
@@ -409,6 +412,26 @@ def bi_lab_clock(out: torch.Tensor, grid: int, iters: int):
         raise ValueError("bi_lab_clock: out must be a contiguous int64 CUDA tensor of >= 3 * grid entries")
     s = _stream(out.device)
     _check(_lib.bi_lab_clock(_ptr(out), grid, iters, ctypes.c_void_p(s.cuda_stream)), "bi_lab_clock")
+
+
+def _check_probe_out(out: torch.Tensor, grid: int, where: str):
+    if not (out.is_cuda and out.dtype == torch.int64 and out.is_contiguous() and out.numel() >= 3 * grid):
+        raise ValueError(f"{where}: out must be a contiguous int64 CUDA tensor of >= 3 * grid entries")
+
+
+def bi_lab_lds_read(out: torch.Tensor, grid: int, iters: int):
+    """LDS read-rate probe: out int64 [grid, 3] gets (cycles, wall ticks, keep-alive) per workgroup."""
+    _check_probe_out(out, grid, "bi_lab_lds_read")
+    s = _stream(out.device)
+    _check(_lib.bi_lab_lds_read(_ptr(out), grid, iters, ctypes.c_void_p(s.cuda_stream)), "bi_lab_lds_read")
+
+
+def bi_lab_mfma_rate(out: torch.Tensor, dtype: int, grid: int, iters: int):
+    """MFMA issue-rate probe (BI_F32: 16x16x4 f32, BI_BF16: 16x16x32 bf16): out int64 [grid, 3]."""
+    _check_probe_out(out, grid, "bi_lab_mfma_rate")
+    s = _stream(out.device)
+    _check(_lib.bi_lab_mfma_rate(_ptr(out), dtype, grid, iters, ctypes.c_void_p(s.cuda_stream)),
+           "bi_lab_mfma_rate")
 
 
 def lib():

@@ -3,8 +3,10 @@
 // None of them is on the batch-invariant path.  They measure what that path
 // is up against on this part: where workgroups run (the XCD hand-over decode
 // needs every wave of an output tile on one XCD), what one kernel launch
-// costs with nothing in it, how fast the chip streams a cold buffer, and the
-// shader clock while every compute unit is busy.  GateLinear page, "Update:
+// costs with nothing in it, how fast the chip streams a cold buffer, the
+// shader clock while every compute unit is busy, and the rates at which a
+// compute unit reads its LDS and issues the recipe's MFMA instructions when
+// nothing else is in the way.  GateLinear page, "Update:
 // is the M=4096 cost avoidable?": a decode-sized kernel is judged by its
 // device time against a launch floor, not by wall time.
 #include <hip/hip_runtime.h>
@@ -94,6 +96,137 @@ __global__ __launch_bounds__(64) void k_clock(uint64_t* __restrict__ out, int it
 hipError_t launch_clock(uint64_t* out, int grid, int iters, hipStream_t s)
 {
     k_clock<<<(unsigned)grid, 64, 0, s>>>(out, iters, 1.0f);
+    return hipGetLastError();
+}
+
+// LDS read rate.  One workgroup of 16 waves fills 64 KiB of LDS, then every
+// lane reads 16-byte chunks `iters` x 4 times; the 64 lanes of a wave take 64
+// consecutive chunks (one contiguous KiB, no bank conflicts) and the slice
+// moves on by a KiB every round.  Every word read is folded with three-input
+// adds (two vector ALU instructions per 16-byte load, which keeps the ALU far
+// from limiting the rate); thread 0 records the shader cycles and wall ticks
+// of the read loop (between two barriers), and the folded words feed a
+// conditional store so that no read can be dropped.
+__global__ __launch_bounds__(1024) void k_lds_read(uint64_t* __restrict__ out, int iters)
+{
+    __shared__ u32x4 buf[4096];
+    const int tid = threadIdx.x;
+    for (int i = tid; i < 4096; i += 1024)
+        buf[i] = u32x4{(uint32_t)i, (uint32_t)i * 2654435761u, (uint32_t)blockIdx.x, 0x9E37u};
+    __syncthreads();
+    const uint64_t c0 = __builtin_readcyclecounter();
+    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+    uint32_t a0 = 0, a1 = 0;
+    int base = tid;
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const u32x4 v = buf[base + j * 1024];
+            a0 = a0 + v[0] + v[1];
+            a1 = a1 + v[2] + v[3];
+        }
+        base = (base + 64) & 1023;
+    }
+    __syncthreads();
+    const uint64_t c1 = __builtin_readcyclecounter();
+    const uint64_t t1 = __builtin_amdgcn_s_memrealtime();
+    if (tid == 0) {
+        out[3 * blockIdx.x] = c1 - c0;
+        out[3 * blockIdx.x + 1] = t1 - t0;
+    }
+    if ((a0 ^ a1) == 0xFFFFFFFFu)
+        out[3 * blockIdx.x + 2] = 1;
+}
+
+hipError_t launch_lds_read(uint64_t* out, int grid, int iters, hipStream_t s)
+{
+    k_lds_read<<<(unsigned)grid, 1024, 0, s>>>(out, iters);
+    return hipGetLastError();
+}
+
+// MFMA issue rate on register operands: eight waves per workgroup, each
+// running eight independent accumulator chains (two A and four B operands,
+// fixed pseudo-random values with random signs and mantissas, as switching
+// data costs clock) of the recipe's instruction for `iters` rounds.  Thread
+// 0 records shader cycles and wall ticks; the accumulators are folded into a
+// conditional store.
+__device__ __forceinline__ uint32_t lab_hash(uint32_t x)
+{
+    x ^= x >> 16;
+    x *= 0x7FEB352Du;
+    x ^= x >> 15;
+    x *= 0x846CA68Bu;
+    x ^= x >> 16;
+    return x;
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(512) void k_mfma_rate(uint64_t* __restrict__ out, int iters)
+{
+    const int tid = threadIdx.x;
+    const uint32_t seed = (uint32_t)tid * 0x9E3779B1u ^ (uint32_t)blockIdx.x * 0x85EBCA77u;
+    f32x4 acc[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+        acc[c] = f32x4{(float)c, (float)(c + 1), (float)(c + 2), (float)(c + 3)};
+    const uint64_t c0 = __builtin_readcyclecounter();
+    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+    if constexpr (BF16) {
+        bf16x8 a[2], b[4];
+#pragma unroll
+        for (int i = 0; i < 6; ++i) {
+            u32x4 v;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                v[e] = (lab_hash(seed + 4u * i + e) & 0x807F807Fu) | 0x3F003F00u;   // +-[0.5, 1)
+            if (i < 2)
+                a[i] = __builtin_bit_cast(bf16x8, v);
+            else
+                b[i - 2] = __builtin_bit_cast(bf16x8, v);
+        }
+        for (int it = 0; it < iters; ++it) {
+#pragma unroll
+            for (int c = 0; c < 8; ++c)
+                acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[c & 1], b[c >> 1], acc[c], 0, 0, 0);
+        }
+    } else {
+        float a[2], b[4];
+#pragma unroll
+        for (int i = 0; i < 6; ++i) {
+            const float v = __uint_as_float((lab_hash(seed + i) & 0x807FFFFFu) | 0x3F000000u);
+            if (i < 2)
+                a[i] = v;
+            else
+                b[i - 2] = v;
+        }
+        for (int it = 0; it < iters; ++it) {
+#pragma unroll
+            for (int c = 0; c < 8; ++c)
+                acc[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[c & 1], b[c >> 1], acc[c], 0, 0, 0);
+        }
+    }
+    __syncthreads();
+    const uint64_t c1 = __builtin_readcyclecounter();
+    const uint64_t t1 = __builtin_amdgcn_s_memrealtime();
+    if (tid == 0) {
+        out[3 * blockIdx.x] = c1 - c0;
+        out[3 * blockIdx.x + 1] = t1 - t0;
+    }
+    uint32_t h = 0;
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+        h ^= __float_as_uint(acc[c][0]) ^ __float_as_uint(acc[c][1]) ^ __float_as_uint(acc[c][2]) ^
+             __float_as_uint(acc[c][3]);
+    if (h == 0xFFFFFFFFu)
+        out[3 * blockIdx.x + 2] = 1;
+}
+
+hipError_t launch_mfma_rate(uint64_t* out, bool bf16, int grid, int iters, hipStream_t s)
+{
+    if (bf16)
+        k_mfma_rate<true><<<(unsigned)grid, 512, 0, s>>>(out, iters);
+    else
+        k_mfma_rate<false><<<(unsigned)grid, 512, 0, s>>>(out, iters);
     return hipGetLastError();
 }
 

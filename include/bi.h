@@ -345,11 +345,26 @@ bi_status_t bi_lab_moe_layout(int64_t M, int64_t H, int64_t E, int64_t I, int64_
  *                      to out[3 wg ..]: shader-clock cycles (s_memtime),
  *                      constant-rate wall-clock ticks (s_memrealtime) and a
  *                      value that keeps the chain alive.
+ *  bi_lab_lds_read     each of `grid` workgroups of 1024 threads fills 64 KiB
+ *                      of LDS and reads it iters x 4 times with
+ *                      conflict-free 16-byte loads (64 KiB per round):
+ *                      the LDS read rate a compute unit sustains.
+ *  bi_lab_mfma_rate    each of `grid` workgroups of 512 threads runs, per
+ *                      wave, iters x 8 independent MFMAs of the recipe's
+ *                      instruction for `dtype` (BI_F32: 16x16x4 f32,
+ *                      BI_BF16: 16x16x32 bf16) on register operands: the
+ *                      issue rate the matrix cores sustain with nothing else
+ *                      in the way.
+ *                      Both write three uint64 per workgroup to out[3 wg ..]
+ *                      (device, 8-byte aligned): shader cycles and wall ticks
+ *                      of the loop, and a word that keeps its results alive.
  * Invalid arguments return BI_EINVAL before anything is enqueued. */
 bi_status_t bi_lab_empty(int32_t grid, int32_t threads, hipStream_t stream);
 bi_status_t bi_lab_stream_read(const void* src, int64_t bytes, uint32_t* sink, int32_t grid,
                                hipStream_t stream);
 bi_status_t bi_lab_clock(uint64_t* out, int32_t grid, int32_t iters, hipStream_t stream);
+bi_status_t bi_lab_lds_read(uint64_t* out, int32_t grid, int32_t iters, hipStream_t stream);
+bi_status_t bi_lab_mfma_rate(uint64_t* out, int32_t dtype, int32_t grid, int32_t iters, hipStream_t stream);
 
 #ifdef __cplusplus
 }
