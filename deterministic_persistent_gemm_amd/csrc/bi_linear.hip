@@ -34,6 +34,8 @@
 // separate from the kernel shape lets each regime have its own shape.
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "bi_device.h"
 #include "bi_launch.h"
 
@@ -360,6 +362,14 @@ __device__ __forceinline__ void dma16(const void* g, uint32_t lds)
     asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(g), "s"(lds) : "memory", "m0");
 }
 
+// The same with a wave-uniform 64-bit base in scalar registers and a 32-bit
+// per-lane byte offset (one vector register per load stream instead of two).
+__device__ __forceinline__ void dma16s(uint32_t voff, const void* sbase, uint32_t lds)
+{
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(sbase), "s"(lds)
+                 : "memory", "m0");
+}
+
 __device__ __forceinline__ uint32_t lds_addr(const void* p)
 {
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
@@ -520,7 +530,10 @@ struct Stager {
     static constexpr int kPer16 = 16 / (int)sizeof(E);
     static constexpr int kChunks = KS / kPer16;          // 16-byte chunks per row
     static constexpr int kPitch = KS;                    // LDS row pitch, elements
-    static constexpr int kRowsPerWindow = kChunks >= 16 ? 1 : 16 / kChunks;
+    // rows of 64 bytes (four chunks) take their key from row / 2: measured
+    // conflict-free, where row / 4 costs about three conflict cycles per
+    // 16-row fragment read
+    static constexpr int kRowsPerWindow = kChunks >= 16 ? 1 : kChunks == 4 ? 2 : 16 / kChunks;
     static constexpr int kKeyMask = (kChunks >= 16 ? 16 : kChunks) - 1;
     static constexpr int kTotal = ROWS * kChunks;
     static constexpr int kPerThread = (kTotal + NT - 1) / NT;
@@ -980,6 +993,290 @@ static hipError_t launch_stream_bf16(const LinearArgs& a, const Plan& p, hipStre
     return hipGetLastError();
 }
 
+// ------------------------------- large bf16 tiles fed by a ring of 32-k stages
+
+// Fully chained bf16 recipes at large M: one BM x BN output tile per
+// workgroup of WM x WN waves (each an FM x FN block of 16x16 accumulators,
+// two waves per SIMD), X and W streamed by direct-to-LDS loads into a ring
+// of R stages of one 32-k block each, issued R - 1 blocks ahead.  A wave
+// holds the fragments of two k blocks: while the MFMAs of block s issue, the
+// fragments of block s + 1 are read -- the X fragments first, then one W
+// fragment after each group of FM MFMAs that used block s's W fragment at
+// that position, which is then free -- so the reads land behind the MFMAs
+// and the loop waits only at its one barrier per block.  The chains are the
+// recipe's fully chained ones (one v_mfma_f32_16x16x32_bf16 per k block, in
+// ascending order), so the bits equal every other path's.
+//
+// Stage layout: X rows 0..BM-1 then W rows 0..BN-1, 64 bytes (32 k) per row,
+// chunk c of row q at position c ^ ((q / 2) & 3), which measured free of
+// bank conflicts for the 16-row fragment reads on gfx950 (the key (q / 4) & 3
+// spreads the same reads over distinct 16-byte bank groups too, yet costs
+// about three conflict cycles per read: SQ_LDS_BANK_CONFLICT).  A
+// direct-to-LDS load covers 16 rows (1 KiB); lane i lands at row i / 4,
+// position i % 4, and so fetches chunk (i % 4) ^ key(row) of its row.
+// Epilogue of a wave's (16 FM) x (16 FN) block through LDS: the block is
+// written to the wave's own LDS area in groups of 128 / sizeof(E) columns
+// (one element per lane and row of each 16x16 accumulator, the same bias add
+// and rounding as store_acc), then read back as 16-byte row chunks and stored
+// with 16-byte global stores -- instead of one 2- or 4-byte store per element.
+// Rows are padded by 16 bytes so that the element writes of the four row
+// groups of a wave fall on distinct banks.  Caller: the whole block lies
+// inside Y, and Y and its row pitch are 16-byte aligned.
+constexpr int kEpiPitch = 128 + 16;                     // bytes per staged row
+constexpr int kEpiBytes = 64 * kEpiPitch;                // one wave's area (64 rows)
+
+template <typename E, int FM, int FN>
+__device__ __forceinline__ void ring_epilogue(const LinearArgs& a, const f32x4 (&acc)[FM][FN], unsigned char* area,
+                                              int row0, int col0, int lane)
+{
+    static_assert(FM * 16 == 64, "a wave's block is 64 rows");
+    constexpr int CG = 128 / (int)sizeof(E);            // columns per group
+    constexpr int TG = CG / 16;                         // accumulator columns per group
+    constexpr int kChunks = 128 / 16;                   // 16-byte chunks per staged row
+    const bool has_bias = a.bias != nullptr;
+#pragma unroll
+    for (int grp = 0; grp < FN / TG; ++grp) {
+#pragma unroll
+        for (int t = 0; t < TG; ++t) {
+            const int fn = grp * TG + t;
+            const float b = load_bias(a, col0 + fn * 16 + acc_col(lane));
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const float v = has_bias ? acc[fm][fn][q] + b : acc[fm][fn][q];
+                    E* dst = reinterpret_cast<E*>(area + (fm * 16 + acc_row(lane, q)) * kEpiPitch) + t * 16 + acc_col(lane);
+                    if constexpr (sizeof(E) == 2)
+                        *dst = f32_to_bf16_rne(v);
+                    else
+                        *dst = v;
+                }
+        }
+        // the element writes and the chunk reads go through different types:
+        // keep the compiler from moving one past the other (the LDS itself
+        // executes a wave's accesses in order)
+        asm volatile("" ::: "memory");
+#pragma unroll
+        for (int i = 0; i < 64 * kChunks / 64; ++i) {
+            const int c = lane + 64 * i;
+            const int row = c / kChunks, ch = c % kChunks;
+            const u32x4 v = *reinterpret_cast<const u32x4*>(area + row * kEpiPitch + ch * 16);
+            E* y = reinterpret_cast<E*>(a.y) + (int64_t)(row0 + row) * a.ldy + col0 + grp * CG + ch * (16 / (int)sizeof(E));
+            __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(y));
+        }
+        asm volatile("" ::: "memory");
+    }
+}
+
+template <int BM, int BN, int WM, int WN, int R, int NL>
+__global__ __launch_bounds__(WM * WN * 64) void k_ring_bf16(LinearArgs a, int tiles_m, int tiles_n, int xbm, int xbn)
+{
+    constexpr int NW = WM * WN;
+    constexpr int FM = BM / (WM * 16), FN = BN / (WN * 16);
+    constexpr int kRow = kKBlock * 2;                       // bytes of a row's 32-k slice
+    constexpr int kFrag = 16 * kRow;                        // 16 rows: one fragment, one load
+    constexpr int kXBytes = BM * kRow;
+    constexpr int kStage = (BM + BN) * kRow;
+    // the first NL waves issue the loads: LX + LW loads of 1 KiB per stage each
+    constexpr int LX = BM / (16 * NL), LW = BN / (16 * NL);
+    constexpr int LS = LX + LW;
+    static_assert(NL <= NW && LX * 16 * NL == BM && LW * 16 * NL == BN, "stage rows split evenly over the loaders");
+    static_assert(R >= 3 && (R - 2) * LS < 64, "a ring of at least three stages");
+    __shared__ __attribute__((aligned(16))) unsigned char ring[R * kStage];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int wm = w / WN, wn = w % WN;
+    const int r = lane & 15, g = lane >> 4;
+    const int ns = a.K / kKBlock;
+    const int tiles = tiles_m * tiles_n;
+    const uint16_t* xg = reinterpret_cast<const uint16_t*>(a.x);
+    const uint16_t* wg = reinterpret_cast<const uint16_t*>(a.w);
+    const uint32_t lds0 = lds_addr(ring);
+    // lane (r, g) reads chunk g of row r of a fragment's 16 rows; the key of
+    // row 16 j + r is (r / 2) & 3 for every j
+    const unsigned char* fbase = ring + r * kRow + ((g ^ ((r >> 1) & 3)) << 4);
+    const int xf0 = wm * FM * kFrag, wf0 = kXBytes + wn * FN * kFrag;
+
+    for (int it = blockIdx.x; it < tiles; it += gridDim.x) {
+        const int tile = xcd_tile(it, tiles_n, xbm, xbn);
+        const int m0 = (tile / tiles_n) * BM, n0 = (tile % tiles_n) * BN;
+        // loading wave w loads rows 16 (w LX + t) .. +15 of the X tile and
+        // 16 (w LW + t) .. +15 of the W tile; rows past M (N) read row M-1
+        // (N-1), whose results are never stored.  Each load is a per-lane
+        // byte offset from the tile's first row (a scalar base).
+        const unsigned char* xt = reinterpret_cast<const unsigned char*>(xg + (int64_t)m0 * a.ldx);
+        const unsigned char* wt = reinterpret_cast<const unsigned char*>(wg + (int64_t)n0 * a.ldw);
+        uint32_t voff[LS];
+        const int wl = w < NL ? w : 0;                     // waves past NL load nothing
+#pragma unroll
+        for (int t = 0; t < LS; ++t) {
+            const int row = 16 * (t < LX ? wl * LX + t : wl * LW + t - LX) + (lane >> 2);
+            const int chunk = (lane & 3) ^ ((row >> 1) & 3);
+            voff[t] = t < LX ? (uint32_t)((int64_t)(min(m0 + row, a.M - 1) - m0) * a.ldx * 2 + chunk * 16)
+                             : (uint32_t)((int64_t)(min(n0 + row, a.N - 1) - n0) * a.ldw * 2 + chunk * 16);
+        }
+        // block st into slot st % R; past the last block the loads re-read
+        // the last block into a slot no later block uses (the slot of block
+        // st - R, long consumed), so that every step of the loop is the same
+        auto issue_one = [&](int st, int t) {
+            const uint32_t base = lds0 + (uint32_t)(st % R) * kStage;
+            const int64_t k0 = (int64_t)min(st, ns - 1) * kKBlock * 2;
+            const uint32_t dst = t < LX ? base + (wl * LX + t) * kFrag : base + kXBytes + (wl * LW + t - LX) * kFrag;
+            dma16s(voff[t], (t < LX ? xt : wt) + k0, (uint32_t)__builtin_amdgcn_readfirstlane((int)dst));
+        };
+        auto issue = [&](int st) {
+            if (NL < NW && w >= NL)
+                return;
+#pragma unroll
+            for (int t = 0; t < LS; ++t)
+                issue_one(st, t);
+        };
+        auto fragx = [&](const unsigned char* sb, int fm) {
+            return *reinterpret_cast<const u32x4*>(sb + xf0 + fm * kFrag);
+        };
+        auto fragw = [&](const unsigned char* sb, int fn) {
+            return *reinterpret_cast<const u32x4*>(sb + wf0 + fn * kFrag);
+        };
+
+        f32x4 acc[FM][FN];
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn)
+                acc[fm][fn] = f32x4{0.f, 0.f, 0.f, 0.f};
+        auto mfma_col = [&](const u32x4 (&xc)[FM], const u32x4& wc, int fn) {
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm)
+                acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xc[fm]),
+                                                                      __builtin_bit_cast(bf16x8, wc), acc[fm][fn], 0, 0, 0);
+        };
+
+        // the previous tile's fragment reads are done everywhere before the
+        // ring is refilled
+        wait_lgkm0();
+        bar();
+#pragma unroll
+        for (int st = 0; st < R - 1; ++st)
+            issue(st);
+        wait_vm<(R - 2) * LS>();
+        bar();
+        // X fragments of two blocks alternate between xa and xb; each W
+        // fragment is replaced in place once its FM MFMAs have issued
+        // (in the order the loop's own reads have -- X, then W by column --
+        // so that the loop's first wait on a fragment is as loose as its
+        // others)
+        u32x4 xa[FM], xb[FM], wf[FN];
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm)
+            xa[fm] = fragx(fbase, fm);
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn)
+            wf[fn] = fragw(fbase, fn);
+        __builtin_amdgcn_sched_group_barrier(0x100, FM, 0);
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn)
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+
+        // block st: make block st+1 visible (this wave's loads of it waited
+        // for, then the barrier, which also tells that every wave is done
+        // with block st-1, whose slot the loads of this step refill), then
+        // the MFMAs of block st with block st+1's fragment reads between them
+        // and, in the loading waves, the loads of block st+R-1 spread over the
+        // same gaps (inline assembly, which the compiler keeps in place), so
+        // that they issue while the matrix unit is busy.  The last step reads
+        // a slot of re-read data that nothing uses.
+        auto step = [&](auto loader, int st, const u32x4 (&xc)[FM], u32x4 (&xn)[FM]) {
+            constexpr bool LD = decltype(loader)::value;
+            wait_vm<(R - 3) * LS>();
+            bar();
+            const unsigned char* sb = fbase + ((st + 1) % R) * kStage;
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm)
+                xn[fm] = fragx(sb, fm);
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn) {
+                mfma_col(xc, wf[fn], fn);
+                wf[fn] = fragw(sb, fn);
+                if constexpr (LD) {
+                    // the loads split the code into scheduling regions; keep
+                    // each region's order: (the X reads,) the MFMAs, the read
+                    if (fn == 0)
+                        __builtin_amdgcn_sched_group_barrier(0x100, FM, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x008, FM, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+#pragma unroll
+                    for (int t = fn * LS / FN; t < (fn + 1) * LS / FN; ++t)
+                        issue_one(st + R - 1, t);
+                }
+            }
+            if constexpr (!LD) {
+                // one W fragment read after each group of FM MFMAs
+                __builtin_amdgcn_sched_group_barrier(0x100, FM, 0);
+#pragma unroll
+                for (int fn = 0; fn < FN; ++fn) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, FM, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                }
+            }
+        };
+        if (NL == NW || w < NL) {
+            for (int st = 0; st < ns; st += 2) {
+                step(std::true_type{}, st, xa, xb);
+                step(std::true_type{}, st + 1, xb, xa);
+            }
+        } else {
+            for (int st = 0; st < ns; st += 2) {
+                step(std::false_type{}, st, xa, xb);
+                step(std::false_type{}, st + 1, xb, xa);
+            }
+        }
+        // every load into the ring has landed and every wave is done with
+        // it before the epilogue stages the output there
+        wait_vm<0>();
+        wait_lgkm0();
+        bar();
+
+        const bool inside = m0 + BM <= a.M && n0 + BN <= a.N;
+        const int esz = a.y_bf16 ? 2 : 4;
+        const bool aligned = ((uintptr_t)a.y & 15) == 0 && ((a.ldy * esz) & 15) == 0;
+        if (inside && aligned) {
+            if (a.y_bf16)
+                ring_epilogue<uint16_t, FM, FN>(a, acc, ring + w * kEpiBytes, m0 + wm * FM * 16, n0 + wn * FN * 16, lane);
+            else
+                ring_epilogue<float, FM, FN>(a, acc, ring + w * kEpiBytes, m0 + wm * FM * 16, n0 + wn * FN * 16, lane);
+        } else {
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+                for (int fn = 0; fn < FN; ++fn)
+                    store_acc(a, m0 + (wm * FM + fm) * 16 + acc_row(lane, 0), n0 + (wn * FN + fn) * 16 + acc_col(lane),
+                              acc[fm][fn]);
+        }
+    }
+}
+
+// What the ring kernel needs: a fully chained recipe (no tile partials), an
+// even number of 32-k blocks (the loop takes them in pairs), and byte offsets
+// inside a tile's rows that fit 32 bits.
+static bool ring_ok(const LinearArgs& a, const Plan& p, int BM, int BN)
+{
+    return p.tiles_k == 1 && a.K % (2 * kKBlock) == 0 &&
+           (int64_t)(BM - 1) * a.ldx * 2 + (int64_t)a.K * 2 < (int64_t(1) << 32) &&
+           (int64_t)(BN - 1) * a.ldw * 2 + (int64_t)a.K * 2 < (int64_t(1) << 32);
+}
+
+template <int BM, int BN, int WM, int WN, int R, int NL>
+static hipError_t launch_ring_bf16(const LinearArgs& a, const Plan& p, hipStream_t s)
+{
+    if (!ring_ok(a, p, BM, BN))
+        return hipErrorInvalidValue;
+    const int tiles_m = (a.M + BM - 1) / BM;
+    const int tiles_n = (a.N + BN - 1) / BN;
+    const int grid = min(tiles_m * tiles_n, device_cu_count());
+    const XcdBlock xb = xcd_block(tiles_m, tiles_n, BM, BN, grid);
+    k_ring_bf16<BM, BN, WM, WN, R, NL><<<grid, WM * WN * 64, 0, s>>>(a, tiles_m, tiles_n, xb.xbm, xb.xbn);
+    return hipGetLastError();
+}
+
 // ------------------------------------------------------------------ launcher
 
 template <typename OX, typename OW, int MT, bool HANDOFF>
@@ -1208,11 +1505,12 @@ static hipError_t launch_persistent(const LinearArgs& a, const Plan& p, hipStrea
         default: return launch_persistent_t<OX, OW, 32, 32, 2, 2, 1>(a, p, s);
         }
     } else {
-        // measured on MI355X for the (bf16, 4096, 4096) GEMM: 256x256 on 4x2
-        // waves at M=4096 (127 us; 128x256: 159 us); 64x64 at M=256 (32 us)
+        // measured on MI355X for the (bf16, 4096, 4096) GEMM: 256x256 fed by
+        // the 32-k ring at M=4096 (112-120 us; register-staged 256x256:
+        // 134-140 us; 128x256: 161 us); 64x64 at M=256 (25 us)
         if (code == 0) {
             if (p.tiles_k == 1 && tiles(256, 256) >= cus)
-                code = 19;
+                code = 21;
             else
                 code = tiles(128, 256) >= cus ? 15 : 12;
         }
@@ -1225,6 +1523,12 @@ static hipError_t launch_persistent(const LinearArgs& a, const Plan& p, hipStrea
             if (a.K % (2 * kKBlock) == 0 && (p.tiles_k == 1 || p.kbpt % 2 == 0))
                 return launch_stream_bf16(a, p, s);
             code = 12;
+        }
+        if (code == 21 || code == 22) {
+            if (ring_ok(a, p, 256, 256))
+                return code == 21 ? launch_ring_bf16<256, 256, 4, 2, 4, 4>(a, p, s)
+                                  : launch_ring_bf16<256, 256, 4, 2, 4, 8>(a, p, s);
+            code = p.tiles_k == 1 ? 19 : 15;
         }
         switch (code) {
         case 11: return launch_persistent_t<OX, OW, 128, 128, 2, 2, 2>(a, p, s);

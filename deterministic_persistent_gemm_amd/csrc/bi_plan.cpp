@@ -144,7 +144,7 @@ bool tile_code_valid(int dtype, int code)
 {
     if (dtype == BI_F32)
         return (code >= 1 && code <= 10);
-    return code >= 11 && code <= 20;
+    return code >= 11 && code <= 22;
 }
 
 static Tiling persistent_tiling(const bi_recipe_t& r)

@@ -267,8 +267,11 @@ const char* bi_status_str(bi_status_t status);
  * 14 = 256x128, 15 = 128x256, 16 = 64x128 with 128-k stages, 17 = 64x64
  * with 32-k stages, 18 = 256x256 on 2x4 waves, 19 = 256x256 on 4x2 waves,
  * 20 = 64x64 on 4x2 waves fed by a ring of eight 64-k LDS stages through
- * direct-to-LDS loads; 18 and 19 serve fully chained recipes only, 20 needs
- * K a multiple of 64; a shape that cannot serve falls back to another).
+ * direct-to-LDS loads, 21 = 256x256 on 4x2 waves fed by a ring of four 32-k
+ * LDS stages through direct-to-LDS loads issued by four of the waves, 22 =
+ * the same with all eight waves loading; 18, 19, 21 and 22 serve fully
+ * chained recipes only, 20-22 need K a multiple of 64; a shape that cannot
+ * serve falls back to another).
  * With BI_PATH_DECODE or BI_PATH_DECODE_XCD, bits 8..15 may force the
  * number of 16-row M tiles one decode wave carries (1, 2 or 4; 0: automatic).
  * Tile shapes never change the numerics. */

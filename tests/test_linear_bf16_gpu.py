@@ -110,13 +110,14 @@ def test_bf16_with_bias_and_ragged_m(bi):
 @pytest.mark.parametrize("K", [1024, 768])
 def test_every_bf16_tile_shape_gives_the_same_bits(bi, K):
     # K=1024 keys use two 512-k tile partials; K=768 is fully chained, the
-    # only form the 256x256 shapes (codes 18, 19) exist in
+    # only form the 256x256 shapes (codes 18, 19, 21, 22) exist in (for the
+    # partial recipe those codes fall back to another shape)
     g = np.random.default_rng(47)
     w = wl.normal_bf16(g, (320, K), 0.02)
     x = dev(wl.normal_bf16(g, (300, K), 1.0))
     wd = dev(w)
     ref = host(bi.bi_linear_bf16(x, weight_t(wd), None))
-    for code in range(11, 21):
+    for code in range(11, 23):
         banner(f"bf16 M=300 N=320 K={K} persistent tile code {code}")
         y = host(bi.bi_lab_linear(x, weight_t(wd), None, path=bi.BI_PATH_PERSISTENT | (code << 8)))
         assert_bitwise(y, ref, f"bf16 tile code {code}")
@@ -170,3 +171,50 @@ def test_stream_ring_tiles(bi, M, N, K, chained):
         y = host(bi.bi_lab_linear(x, weight_t(wd), b, recipe=r, path=bi.BI_PATH_PERSISTENT | (20 << 8),
                                   out_dtype=torch.float32))
         assert_close(y, oracle.linear_bf16(host(x), w, host(b), out="f32"), 1e-5, 1e-4, "code 20 vs oracle")
+
+
+@pytest.mark.parametrize("M,N,K", [(256, 256, 64), (300, 320, 768), (513, 2000, 192), (1024, 1536, 2048),
+                                   (4096, 4096, 4096), (4097, 272, 128)])
+def test_ring_fed_256_tiles(bi, M, N, K):
+    # the 256x256 tile fed by a ring of 32-k direct-to-LDS stages (codes 21
+    # and 22: four or eight loading waves) gives the bits of the
+    # register-staged 256x256 tile (code 19): full and ragged tiles (the
+    # 16-byte staged epilogue and the element-wise one), bias or none, bf16
+    # and fp32 output, one to many tiles per workgroup
+    import torch
+    g = np.random.default_rng(M + 3 * N + 7 * K)
+    w = wl.normal_bf16(g, (N, K), 0.02)
+    wd = dev(w)
+    x = dev(wl.normal_bf16(g, (M, K), 1.0))
+    b = dev((g.standard_normal(N) * 0.01).astype(np.float32))
+    r = bi.bi_describe_recipe(bi.BI_BF16, N, K)
+    r.block_k = K
+    for odt in (torch.bfloat16, torch.float32):
+        for bias in (None, b):
+            y19 = host(bi.bi_lab_linear(x, weight_t(wd), bias, recipe=r, path=bi.BI_PATH_PERSISTENT | (19 << 8),
+                                        out_dtype=odt))
+            for code in (21, 22):
+                banner(f"bf16 M={M} N={N} K={K} tile code {code} vs 19 out={odt} bias={bias is not None}")
+                y = host(bi.bi_lab_linear(x, weight_t(wd), bias, recipe=r,
+                                          path=bi.BI_PATH_PERSISTENT | (code << 8), out_dtype=odt))
+                assert_bitwise(y, y19, f"code {code} vs 19 M={M} N={N} K={K}")
+    if M * N * K <= 64 * 1024 * 1024:
+        y = host(bi.bi_lab_linear(x, weight_t(wd), b, recipe=r, path=bi.BI_PATH_PERSISTENT | (21 << 8),
+                                  out_dtype=torch.float32))
+        assert_close(y, oracle.linear_bf16(host(x), w, host(b), out="f32"), 1e-5, 1e-4, "code 21 vs oracle")
+
+
+def test_ring_fed_tiles_fall_back_where_they_cannot_serve(bi):
+    # a recipe with tile partials, and K not a multiple of 64, run another
+    # shape under codes 21 and 22 (same bits, no error)
+    g = np.random.default_rng(5)
+    for K, block_k in ((1024, 512), (96, 96)):
+        w = wl.normal_bf16(g, (320, K), 0.02)
+        x = dev(wl.normal_bf16(g, (300, K), 1.0))
+        r = bi.bi_describe_recipe(bi.BI_BF16, 320, K)
+        r.block_k = block_k
+        ref = host(bi.bi_lab_linear(x, weight_t(dev(w)), None, recipe=r, path=bi.BI_PATH_PERSISTENT | (12 << 8)))
+        for code in (21, 22):
+            banner(f"bf16 K={K} block_k={block_k} tile code {code} fallback")
+            y = host(bi.bi_lab_linear(x, weight_t(dev(w)), None, recipe=r, path=bi.BI_PATH_PERSISTENT | (code << 8)))
+            assert_bitwise(y, ref, f"code {code} fallback K={K}")

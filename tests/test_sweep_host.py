@@ -96,7 +96,7 @@ def test_compiled_table_is_what_the_library_serves():
         assert rec.block_k == r["block_k"], r
         assert rec.m_decode_max == r["m_decode_max"], r
         assert r["K"] % r["block_k"] == 0 and r["block_k"] % 32 == 0
-        codes = range(1, 11) if dt == bi.BI_F32 else range(11, 21)
+        codes = range(1, 11) if dt == bi.BI_F32 else range(11, 23)
         for t in (r["tile_a"], r["tile_b"], r["tile_c"]):
             assert t == 0 or t in codes, r
         assert r["decode_path"] in (0, 1, 3, 4)
