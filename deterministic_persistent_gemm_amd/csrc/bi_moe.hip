@@ -455,7 +455,52 @@ struct GroupedArgs {
     int topk;
     uint16_t* act;            // GEMM1 output [P, I] by position
     float* part;              // GEMM2 output [P, H] by pair
+    // GEMM2 with the top-k sum folded in (small M): arrival counters, one
+    // per column block, in the workspace's counter region (nullptr: the sum
+    // runs as its own kernel), the layer output and the sum's options
+    uint32_t* comb_counters;
+    float* y;
+    int tokens, comb_apply, comb_fp64;
 };
+
+// Counters of the folded top-k sum: 128 bytes apart, after the first 64 of
+// the counter region.
+constexpr int kCombCounterStride = (int)(kDecodeCounterBytes / 4 / kDecodeMaxCounters);
+constexpr int kCombCounterFirst = 64;
+constexpr int kCombMaxBlocks = kDecodeMaxCounters - kCombCounterFirst;
+// up to this many tokens the sum is folded into the down projection: its
+// last workgroup per column block (256 threads, 64 columns) then sums one
+// (token, column) per thread in one round of loads (measured on the
+// Qwen3-shaped layer: M=1 33.0 -> 31.8 us; at M=16, four sums per thread
+// one after another, 150.9 -> 158.4)
+constexpr int64_t kCombMaxTokens = 4;
+
+// The top-k sum of token t at column c, in slot order j = 0..topk-1
+// (fused-MoE page: fixed slot order; the (apply_weights, acc_fp64) options
+// honoured independently, so the unweighted fp32 point applies no weights):
+//   acc_fp64:  fp32( sum_j w_j * (double) part_j ),  w_j = p_j or 1, in binary64
+//   fp32:      acc = +0; acc = acc + t_j,  t_j = p_j * part_j (fp32) or part_j
+template <bool APPLY, bool FP64>
+__device__ __forceinline__ float topk_sum(const float* __restrict__ part, const float* __restrict__ probs,
+                                          int64_t t, int64_t c, int H, int topk)
+{
+    const float* p = part + (t * topk) * (int64_t)H + c;
+    if (FP64) {
+        double s = 0.0;
+        for (int j = 0; j < topk; ++j) {
+            const double v = (double)p[(int64_t)j * H];
+            s += APPLY ? (double)probs[t * topk + j] * v : v;
+        }
+        return (float)s;
+    } else {
+        float s = 0.0f;
+        for (int j = 0; j < topk; ++j) {
+            const float v = p[(int64_t)j * H];
+            s = s + (APPLY ? probs[t * topk + j] * v : v);
+        }
+        return s;
+    }
+}
 
 // Workgroup = TW x NW waves: TW waves split the k tile partials of one
 // output tile (folded in ascending order through LDS), NW waves take NW
@@ -566,7 +611,7 @@ __global__ __launch_bounds__(TW * NW * 64) void k_grouped(GroupedArgs g)
                     acc[m][b] = acc[m][b] + lds[(((t * NW + nw) * MT + m) * NB + b) * 64 + lane];
             }
     }
-    if (!nt_ok)
+    if (ACT != kActNone && !nt_ok)
         return;
 
     const int col = nt * 16 + acc_col(lane);
@@ -575,7 +620,7 @@ __global__ __launch_bounds__(TW * NW * 64) void k_grouped(GroupedArgs g)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const int p = row0 + m * kTileRows + acc_row(lane, q);
-            if (p >= row_end)
+            if (p >= row_end || !nt_ok)
                 continue;
             if (ACT == kActSwiGLU) {
                 // storage point of the gate/up projection, then the activation
@@ -601,15 +646,51 @@ __global__ __launch_bounds__(TW * NW * 64) void k_grouped(GroupedArgs g)
                 g.part[(int64_t)g.sorted[p] * g.n_out + col] = acc[m][0][q];
             }
         }
+    if constexpr (ACT == kActNone && TW == 1) {
+        // The top-k sum in the same launch (small M).  Every workgroup of
+        // column block bx runs on XCD bx mod 8 (workgroups go to the XCDs
+        // round-robin and the grid's row is a multiple of 8 blocks), so the
+        // partials of the block's columns, written by the workgroups of all
+        // work units, meet in that XCD's L2.  A workgroup's stores are
+        // complete there before it counts itself in; the workgroup that
+        // arrives last drops its L1 and sums the block's columns for every
+        // token.  The counter wraps to zero at the last arrival.
+        if (g.comb_counters) {
+            __shared__ uint32_t last;
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();
+            if (tid == 0) {
+                const uint32_t n = (uint32_t)g.nunits[0];
+                const uint32_t prev = __builtin_amdgcn_atomic_inc32(g.comb_counters + blockIdx.x * kCombCounterStride,
+                                                                    n - 1, __ATOMIC_RELAXED, "workgroup");
+                last = prev == n - 1;
+            }
+            __syncthreads();
+            if (!last)
+                return;
+            asm volatile("buffer_inv sc0" ::: "memory");
+            const int c0 = blockIdx.x * NW * 16;
+            const int ncol = min(NW * 16, g.n_out - c0);
+            for (int i = tid; i < g.tokens * ncol; i += NW * 64) {
+                const int64_t t = i / ncol, c = c0 + i % ncol;
+                float v;
+                if (g.comb_apply && g.comb_fp64)
+                    v = topk_sum<true, true>(g.part, g.probs, t, c, g.n_out, g.topk);
+                else if (g.comb_apply)
+                    v = topk_sum<true, false>(g.part, g.probs, t, c, g.n_out, g.topk);
+                else if (g.comb_fp64)
+                    v = topk_sum<false, true>(g.part, g.probs, t, c, g.n_out, g.topk);
+                else
+                    v = topk_sum<false, false>(g.part, g.probs, t, c, g.n_out, g.topk);
+                g.y[t * g.n_out + c] = v;
+            }
+        }
+    }
 }
 
 // ------------------------------------------------------------------- combine
 
-// Top-k sum in slot order j = 0..topk-1 (fused-MoE page: fixed slot order;
-// the (apply_weights, acc_fp64) options of the sum are honoured
-// independently, so the unweighted fp32 point applies no weights):
-//   acc_fp64:  y = fp32( sum_j w_j * (double) part_j ),  w_j = p_j or 1, in binary64
-//   fp32:      acc = +0; acc = acc + t_j,  t_j = p_j * part_j (fp32) or part_j
+// Top-k sum as its own kernel (larger M): topk_sum for every (token, column).
 template <bool APPLY, bool FP64>
 __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ part, const float* __restrict__ probs,
                                                  int M, int H, int topk, float* __restrict__ y)
@@ -617,23 +698,7 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ part,
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= (int64_t)M * H)
         return;
-    const int64_t m = i / H, c = i % H;
-    const float* p = part + (m * topk) * (int64_t)H + c;
-    if (FP64) {
-        double s = 0.0;
-        for (int j = 0; j < topk; ++j) {
-            const double v = (double)p[(int64_t)j * H];
-            s += APPLY ? (double)probs[m * topk + j] * v : v;
-        }
-        y[i] = (float)s;
-    } else {
-        float s = 0.0f;
-        for (int j = 0; j < topk; ++j) {
-            const float v = p[(int64_t)j * H];
-            s = s + (APPLY ? probs[m * topk + j] * v : v);
-        }
-        y[i] = s;
-    }
+    y[i] = topk_sum<APPLY, FP64>(part, probs, i / H, i % H, H, topk);
 }
 
 // ------------------------------------------------------------------ host side
@@ -866,8 +931,23 @@ bi_status_t moe_run(const uint16_t* x, const float* w_router, const float* b_rou
     g2.act = nullptr;
     g2.part = part;
     g2.act_probs = 0;
+    // small M: the top-k sum runs in the down projection's launch (one
+    // workgroup of four waves per 64 columns, TW == 1; the column blocks
+    // must split evenly over the eight XCDs)
+    const int64_t comb_blocks = (H / 16 + 3) / 4;
+    const bool fold_sum = M <= kCombMaxTokens && g2.tiles_k != 2 && g2.tiles_k != 4 &&
+                          comb_blocks % 8 == 0 && comb_blocks <= kCombMaxBlocks;
+    if (fold_sum) {
+        g2.comb_counters = reinterpret_cast<uint32_t*>(base + L.router_ws) + kCombCounterFirst * kCombCounterStride;
+        g2.y = y;
+        g2.tokens = (int)M;
+        g2.comb_apply = opt.apply_weights;
+        g2.comb_fp64 = opt.acc_fp64;
+    }
     if (launch_grouped<kActNone>(g2, unit_rows, L.max_units, stream) != hipSuccess)
         return BI_EHIP;
+    if (fold_sum)
+        return BI_OK;
 
     const int64_t n = M * H;
     const unsigned cgrid = (unsigned)((n + 255) / 256);

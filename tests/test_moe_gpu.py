@@ -149,3 +149,35 @@ def test_moe_small_shape_full_oracle(bi, E, topk):
         assert_close(probs, pf, 0.0, 1e-5, f"small probs M={M}")
         rms = float(np.sqrt(np.mean(yf.astype(np.float64) ** 2)))
         assert_close(y, yf, moe_atol(rms, 256), RTOL, f"small moe M={M}")
+
+
+@pytest.mark.parametrize("M", [1, 4, 5])
+def test_moe_small_m_folded_sum(bi, moe, M):
+    # up to four tokens the top-k sum runs in the down projection's launch
+    # (its last workgroup per column block sums every token; five tokens use
+    # the separate kernel): repeat calls give the same bits, the workspace's
+    # counter region is zero again afterwards, and graph replays reproduce
+    # the eager output
+    import torch
+    w, d = moe
+    batch = wl.moe_batch(M, w)
+    banner(f"moe M={M} folded top-k sum")
+    y0, i0, p0 = run_moe(bi, batch.x, d)
+    y1, i1, p1 = run_moe(bi, batch.x, d)
+    assert_bitwise(y1, y0, f"repeat M={M}")
+    s = torch.cuda.current_stream()
+    ws = bi._ws_cache[(torch.cuda.current_device(), s.cuda_stream)]
+    torch.cuda.synchronize()
+    assert int(ws[:bi.WS_COUNTER_BYTES].count_nonzero()) == 0
+    xd = dev(batch.x)
+    y = torch.empty((M, wl.MOE_H), dtype=torch.float32, device="cuda")
+    gws = bi.alloc_workspace(bi.lib().bi_moe_workspace_size(M, wl.MOE_H, wl.MOE_E, wl.MOE_I, wl.MOE_TOPK), xd.device)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        yy, _, _ = bi.bi_moe_grouped_gemm(xd, d["wr"], None, d["w13"], d["w2"], wl.MOE_TOPK, ws=gws)
+        y.copy_(yy)
+    for rep in range(3):
+        y.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert_bitwise(host(y), y0, f"graph replay {rep} M={M}")
