@@ -1466,6 +1466,230 @@ static hipError_t launch_persistent_t(const LinearArgs& a, const Plan& p, hipStr
     return hipGetLastError();
 }
 
+// ------------------------------- fp32 BMx32 tiles fed by a ring of 64-k stages
+
+// fp32 recipes with tile partials at mid M (the router at M = 1024 and 2048:
+// one tile per compute unit).  Every output element's tile partial is one
+// chain of dependent MFMAs (the recipe's chain from +0 over the k tile's
+// blocks, ascending), so a SIMD only keeps its matrix unit busy when it holds
+// several independent chains.  Here the chains are the BM/16 x 2 sub-tiles of
+// 16x16 times PAR k tiles worked on at once: eight waves, two per SIMD, wave
+// w takes sub-tile w % S (S = BM/8) and the C = PAR S / 8 consecutive k tiles
+// C (w / S) .. C (w / S) + C - 1 of every group of PAR k tiles.  At the end of
+// each group the waves past the first hand their partials to the first
+// through LDS, which adds the group's partials in ascending tile order
+// (acc = P0; acc = acc + P1; ...) -- the same fold as every other path, then
+// the bias once.
+//
+// X and W stream into a ring of R units by direct-to-LDS loads; a unit is one
+// 64-k stage of one k tile (BM X rows, then 32 W rows, of 256 bytes), and a
+// step consumes PAR units, one per k tile of the group.  At step j the loads
+// of units PAR j + R .. PAR j + R + PAR - 1 are issued: each lands in the slot
+// of a unit whose fragments were read during step j - 1 or earlier (the
+// barrier that opens step j follows every wave's wait for its fragment
+// reads), while the fragments of step j + 1 are read and step j's MFMAs
+// issue.  Past the last step the loads re-read the last stage into slots no
+// later step uses, so that every step is the same.
+//
+// Stage layout: chunk c of row q at position c ^ (q & 15), the layout of the
+// register-staged fp32 kernels' 64-k stages (measured free of bank conflicts
+// for the fragment reads; 128-byte rows of 32-k stages are not, with either
+// key tried).  A direct-to-LDS load covers 4 rows (1 KiB); lane i lands at
+// row i / 16, position i % 16, and so fetches chunk (i % 16) ^ (row & 15).
+template <int BM, int PAR, int R>
+__global__ __launch_bounds__(512) void k_ring_f32(LinearArgs a, int kbpt, int tiles_k, int tiles_m, int tiles_n,
+                                                  int xbm, int xbn)
+{
+    constexpr int kRow = 256;                               // 64 k of fp32
+    constexpr int kUnit = (BM + 32) * kRow;
+    constexpr int S = BM / 8;                               // 16x16 sub-tiles
+    constexpr int G = 8 / S;                                // wave groups
+    constexpr int C = PAR / G;                              // chains per wave
+    constexpr int LPU = (BM + 32) / 32;                     // 1 KiB loads per unit and wave
+    static_assert((BM == 32 || BM == 64) && C >= 1 && C * G == PAR && R >= 2 * PAR, "ring shape");
+    __shared__ __attribute__((aligned(16))) unsigned char ring[R * kUnit];
+    __shared__ f32x4 hand[G > 1 ? (G - 1) * S * C : 1][64];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int sub = w % S, grp = w / S;
+    const int sm = sub >> 1, sn = sub & 1;
+    const int r = lane & 15, g = lane >> 4;
+    const int spt = kbpt / 2;                               // stages per k tile
+    const int nsteps = (tiles_k / PAR) * spt;
+    const int nst = a.K / 64;                               // stages of the whole K
+    const int tiles = tiles_m * tiles_n;
+    const float* xg = reinterpret_cast<const float*>(a.x);
+    const float* wg = reinterpret_cast<const float*>(a.w);
+    const uint32_t lds0 = lds_addr(ring);
+    // lane (r, g) of a fragment reads chunks 2g, 2g+1 of k block b of row
+    // r of its sub-tile's X rows (W rows); the key of those rows is r
+    const unsigned char* fx = ring + (sm * 16 + r) * kRow;
+    const unsigned char* fw = ring + (BM + sn * 16 + r) * kRow;
+    // the wave index is uniform; reading it through the scalar unit lets
+    // the choice of X or W (whole 4-row groups) stay a scalar base
+    const int wu = __builtin_amdgcn_readfirstlane(w);
+
+    for (int it = blockIdx.x; it < tiles; it += gridDim.x) {
+        const int tile = xcd_tile(it, tiles_n, xbm, xbn);
+        const int m0 = (tile / tiles_n) * BM, n0 = (tile % tiles_n) * 32;
+        // wave w loads the 4-row groups w LPU .. w LPU + LPU - 1 of each unit
+        // (X rows 0..BM-1, then W rows); rows past M (N) read row M-1 (N-1),
+        // whose results are never stored
+        const unsigned char* xt = reinterpret_cast<const unsigned char*>(xg + (int64_t)m0 * a.ldx);
+        const unsigned char* wt = reinterpret_cast<const unsigned char*>(wg + (int64_t)n0 * a.ldw);
+        uint32_t voff[LPU];
+        bool isx[LPU];
+#pragma unroll
+        for (int t = 0; t < LPU; ++t) {
+            const int q = 4 * (wu * LPU + t) + (lane >> 4);
+            const int chunk = (lane & 15) ^ (q & 15);
+            isx[t] = wu * LPU + t < BM / 4;
+            voff[t] = isx[t] ? (uint32_t)((int64_t)(min(m0 + q, a.M - 1) - m0) * a.ldx * 4 + chunk * 16)
+                             : (uint32_t)((int64_t)(min(n0 + q - BM, a.N - 1) - n0) * a.ldw * 4 + chunk * 16);
+        }
+        // unit u = PAR j + h: stage j % spt of k tile PAR (j / spt) + h, in
+        // slot u % R
+        auto issue_unit = [&](int u) {
+            const int j = u / PAR, h = u % PAR;
+            const int st = min((PAR * (j / spt) + h) * spt + j % spt, nst - 1);
+            const uint32_t slot = lds0 + (uint32_t)(u % R) * kUnit + wu * LPU * 1024;
+#pragma unroll
+            for (int t = 0; t < LPU; ++t)
+                dma16s(voff[t], (isx[t] ? xt : wt) + (int64_t)st * 256,
+                       (uint32_t)__builtin_amdgcn_readfirstlane((int)(slot + t * 1024)));
+        };
+        // the fragments of this wave's chains at step j
+        auto frags = [&](Frag<true> (&A)[C][2], Frag<true> (&B)[C][2], int j) {
+#pragma unroll
+            for (int c = 0; c < C; ++c) {
+                const int slot = (PAR * j + grp * C + c) % R;
+#pragma unroll
+                for (int b = 0; b < 2; ++b) {
+                    const int c0 = b * 8 + 2 * g;
+                    A[c][b].lo = *reinterpret_cast<const f32x4*>(fx + slot * kUnit + (((c0) ^ r) << 4));
+                    A[c][b].hi = *reinterpret_cast<const f32x4*>(fx + slot * kUnit + (((c0 + 1) ^ r) << 4));
+                    B[c][b].lo = *reinterpret_cast<const f32x4*>(fw + slot * kUnit + (((c0) ^ r) << 4));
+                    B[c][b].hi = *reinterpret_cast<const f32x4*>(fw + slot * kUnit + (((c0 + 1) ^ r) << 4));
+                }
+            }
+        };
+        // the group's partials in ascending k tile order, after the barrier
+        // that follows the hand-over
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        f32x4 P[C];
+        auto fold = [&](bool first) {
+#pragma unroll
+            for (int c = 0; c < C; ++c)
+                acc = (first && c == 0) ? P[c] : acc + P[c];
+#pragma unroll
+            for (int q = 1; q < G; ++q)
+#pragma unroll
+                for (int c = 0; c < C; ++c)
+                    acc = acc + hand[((q - 1) * S + sub) * C + c][lane];
+        };
+
+        // the previous tile's fragment and hand-over reads are done
+        // everywhere before the ring is refilled
+        wait_lgkm0();
+        bar();
+#pragma unroll
+        for (int u = 0; u < R; ++u)
+            issue_unit(u);
+        // step 0 has landed
+        wait_vm<(R - PAR) * LPU>();
+        bar();
+        Frag<true> Aa[C][2], Ba[C][2], Ab[C][2], Bb[C][2];
+        frags(Aa, Ba, 0);
+
+        // step j: step j + 1 is visible (this wave's loads of it waited for,
+        // then the barrier); the next step's fragments are read while this
+        // step's MFMAs issue, the chains interleaved block by block
+        auto step = [&](int j, const Frag<true> (&A)[C][2], const Frag<true> (&B)[C][2], Frag<true> (&An)[C][2],
+                        Frag<true> (&Bn)[C][2]) {
+            wait_vm<(R - 2 * PAR) * LPU>();
+            wait_lgkm0();
+            bar();
+            if (j > 0 && j % spt == 0 && grp == 0)
+                fold(j == spt);
+#pragma unroll
+            for (int h = 0; h < PAR; ++h)
+                issue_unit(PAR * j + R + h);
+            frags(An, Bn, j + 1);
+            if (j % spt == 0) {
+#pragma unroll
+                for (int c = 0; c < C; ++c)
+                    P[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+#pragma unroll
+            for (int b = 0; b < 2; ++b) {
+#define BI_RING_STEP(SS)                                                      \
+                for (int c = 0; c < C; ++c)                                   \
+                    P[c] = mfma_f32_step<SS>(A[c][b], B[c][b], P[c]);
+#pragma unroll
+                BI_RING_STEP(0)
+#pragma unroll
+                BI_RING_STEP(1)
+#pragma unroll
+                BI_RING_STEP(2)
+#pragma unroll
+                BI_RING_STEP(3)
+#pragma unroll
+                BI_RING_STEP(4)
+#pragma unroll
+                BI_RING_STEP(5)
+#pragma unroll
+                BI_RING_STEP(6)
+#pragma unroll
+                BI_RING_STEP(7)
+#undef BI_RING_STEP
+            }
+            if (G > 1 && j % spt == spt - 1 && grp > 0) {
+#pragma unroll
+                for (int c = 0; c < C; ++c)
+                    hand[((grp - 1) * S + sub) * C + c][lane] = P[c];
+            }
+        };
+        for (int j = 0; j < nsteps; j += 2) {
+            step(j, Aa, Ba, Ab, Bb);
+            step(j + 1, Ab, Bb, Aa, Ba);
+        }
+        // the last group: its hand-over is in LDS after one more barrier
+        wait_vm<0>();
+        wait_lgkm0();
+        bar();
+        if (grp == 0) {
+            fold(nsteps == spt);
+            store_acc(a, m0 + sm * 16 + acc_row(lane, 0), n0 + sn * 16 + acc_col(lane), acc);
+        }
+    }
+}
+
+// What the fp32 ring kernel needs: a number of k tiles that PAR divides, each
+// an even number of 32-k blocks (at least four where partials are handed
+// over, so that a hand-over slot is read before it is written again), an even
+// number of steps, and byte offsets inside a tile's rows that fit 32 bits.
+static bool ring_f32_ok(const LinearArgs& a, const Plan& p, int bm, int par)
+{
+    const int spt = p.kbpt / 2;
+    const bool hands = bm == 32;
+    return p.tiles_k >= par && p.tiles_k % par == 0 && p.kbpt >= (hands ? 4 : 2) && p.kbpt % 2 == 0 &&
+           ((p.tiles_k / par) * spt) % 2 == 0 && a.K % 64 == 0 &&
+           (int64_t)(bm - 1) * a.ldx * 4 + (int64_t)a.K * 4 < (int64_t(1) << 32) &&
+           (int64_t)31 * a.ldw * 4 + (int64_t)a.K * 4 < (int64_t(1) << 32);
+}
+
+template <int BM, int PAR, int R>
+static hipError_t launch_ring_f32(const LinearArgs& a, const Plan& p, hipStream_t s)
+{
+    if (!ring_f32_ok(a, p, BM, PAR))
+        return hipErrorInvalidValue;
+    const int tiles_m = (a.M + BM - 1) / BM;
+    const int tiles_n = (a.N + 31) / 32;
+    const int grid = min(tiles_m * tiles_n, device_cu_count());
+    const XcdBlock xb = xcd_block(tiles_m, tiles_n, BM, 32, grid);
+    k_ring_f32<BM, PAR, R><<<grid, 512, 0, s>>>(a, p.kbpt, p.tiles_k, tiles_m, tiles_n, xb.xbm, xb.xbn);
+    return hipGetLastError();
+}
+
 // Persistent tile shapes (BM x BN, waves WM x WN, k blocks per LDS stage).
 // Code 0 picks automatically: the largest tile that still gives every compute
 // unit a tile.  Tiling never changes the numerics, only the speed.
@@ -1486,10 +1710,28 @@ static hipError_t launch_persistent(const LinearArgs& a, const Plan& p, hipStrea
         return a.K % stage_k(c) == 0 && (p.tiles_k == 1 || p.kbpt % kbs == 0);
     };
     if constexpr (OX::f32_frag) {
-        // measured on MI355X for the (fp32, 256, 4096) router: 64x64 on 8
-        // waves at M=4096 (99 us), 32x32 at M=1024 and 2048 (48 / 68 us)
+        // measured on MI355X for the (fp32, 256, 4096) router with cold
+        // weights: the ring-fed 32x32 tile up to M = 1024 (28.6 us there;
+        // register-staged 32x32: 36.8 us), the ring-fed 64x32 tile at
+        // M = 2048 (44.6 us; 52.2 us), 64x64 on 8 waves from M = 4096
+        // the ring-fed shapes stream fp32 rows as they are: operands widened
+        // from bf16 (the MoE router's activations) take the register-staged
+        // shapes
+        constexpr bool rings = std::is_same<OX, F32>::value && std::is_same<OW, F32>::value;
         if (code == 0)
-            code = tiles(64, 64) >= cus ? 4 : 3;
+            code = tiles(64, 64) >= cus ? 4 : !rings ? 3 : tiles(64, 32) >= cus ? 24 : 23;
+        if constexpr (rings) {
+            // the ring-fed 32x32 tile works on four k tiles at once where
+            // their number allows, else on two; the 64x32 tile on two
+            if (code == 23 && ring_f32_ok(a, p, 32, 4))
+                return launch_ring_f32<32, 4, 8>(a, p, s);
+            if (code == 23 && ring_f32_ok(a, p, 32, 2))
+                return launch_ring_f32<32, 2, 8>(a, p, s);
+            if (code == 24 && ring_f32_ok(a, p, 64, 2))
+                return launch_ring_f32<64, 2, 6>(a, p, s);
+        }
+        if (code == 23 || code == 24)
+            code = 3;
         if (!stage_fits(code))
             code = 7;
         switch (code) {

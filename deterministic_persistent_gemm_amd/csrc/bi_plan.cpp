@@ -143,7 +143,7 @@ bool decode_xcd_ok(const Plan& p)
 bool tile_code_valid(int dtype, int code)
 {
     if (dtype == BI_F32)
-        return (code >= 1 && code <= 10);
+        return (code >= 1 && code <= 10) || code == 23 || code == 24;
     return code >= 11 && code <= 22;
 }
 

@@ -24,6 +24,8 @@ with cold weights (rotating copies, beyond the Infinity Cache):
     where the persistent kernel might take over;
   * both at CROSS_M, which only places the decode limit between the
     prefill sizes (it counts in neither total);
+  * every persistent tile shape at SEGMENT_M, which only places the tile
+    ranges between the prefill sizes (it counts in no total);
 
 Times are per-call averages over a replayed HIP graph of the calls.  The
 sweeper then checks that every path and tile shape of the candidate gives the same bits
@@ -57,12 +59,13 @@ TABLE = os.path.join(PKG, "csrc", "bi_table.inc")
 DECODE_M = (1, 8, 16, 32, 64, 128)
 PREFILL_M = (256, 1024, 4096)
 CROSS_M = (512,)            # timed on both sides to place the decode limit, not in either total
+SEGMENT_M = (2048,)         # timed for the tile shapes only, to place their ranges, in no total
 DECODE_PROBE_MAX = 1024     # decode forms are also timed at the prefill sizes up to this M
 DECODE_MARGIN = 0.05        # the persistent kernel takes over once it is this much faster
 TABLE_HEADER = ("// Measured key table, written by deterministic_persistent_gemm_amd/sweep.py.\n"
                 "// {dtype, N, K, block_k, m_decode_max, decode_path, m_a, tile_a, m_b, tile_b, tile_c, "
                 "m_xcd_max}\n")
-F32_CODES = tuple(range(1, 11))
+F32_CODES = tuple(range(1, 11)) + (23, 24)
 BF16_CODES = tuple(range(11, 23))
 PATH_DECODE, PATH_PERSISTENT, PATH_DECODE_WG, PATH_DECODE_DMA, PATH_DECODE_XCD = 1, 2, 3, 4, 5
 
@@ -81,16 +84,19 @@ def parse_key(s: str, profile: str = "decode"):
 def stage_k(code: int) -> int:
     """k per LDS stage of a persistent tile shape (shapes whose stage does
     not divide K are served by the 32-k-stage shape of the dtype)."""
-    return 32 if code in (7, 8, 17) else 128 if code in (9, 10, 13, 16) else 64   # 20-22: 64
+    return 32 if code in (7, 8, 17) else 128 if code in (9, 10, 13, 16) else 64   # 20-24: 64
 
 
 def tile_codes(dt: str, K: int, block_k: int):
     """The distinct tile shapes a recipe can run: shapes whose stage does not
-    divide K, and the 256x256 shapes (single k tile only: 18, 19 and the
-    ring-fed 21, 22) of a recipe with several k tiles, would fall back to
-    another shape and are left out."""
+    divide K, the 256x256 shapes (single k tile only: 18, 19 and the
+    ring-fed 21, 22) of a recipe with several k tiles, and the ring-fed fp32
+    shapes (23, 24: an even number of k tiles of 64-k multiples) of a recipe
+    without, would fall back to another shape and are left out."""
     codes = F32_CODES if dt == "f32" else BF16_CODES
-    return tuple(c for c in codes if K % stage_k(c) == 0 and not (c in (18, 19, 21, 22) and block_k != K))
+    rings_f32 = (K // block_k) % 2 == 0 and block_k % 64 == 0
+    return tuple(c for c in codes if K % stage_k(c) == 0 and not (c in (18, 19, 21, 22) and block_k != K)
+                 and not (c in (23, 24) and not rings_f32))
 
 
 def block_k_candidates(dt: str, K: int):
@@ -284,7 +290,7 @@ def sweep_key(dt: str, N: int, K: int, profile: str, tie: float = 0.03, log=prin
     ncopies = max(2, min(128, math.ceil((512 << 20) / wbytes)))
     w0 = (torch.randn(N, K, generator=g) * 0.02).to(tdt)
     ws = [w0.to(dev)] + [w0.to(dev).clone() for _ in range(ncopies - 1)]
-    grid = sorted(set(DECODE_M + PREFILL_M + CROSS_M))
+    grid = sorted(set(DECODE_M + PREFILL_M + CROSS_M + SEGMENT_M))
     xs = {M: torch.randn(M, K, generator=g).to(tdt).to(dev) for M in grid}
     odt = torch.float32
     served = bi.bi_describe_recipe(bi.BI_F32 if dt == "f32" else bi.BI_BF16, N, K).block_k

@@ -262,7 +262,12 @@ const char* bi_status_str(bi_status_t status);
  * of `path` may name a persistent tile shape (0: automatic; fp32: 1 = 64x64,
  * 2 = 32x64, 3 = 32x32, 4 = 64x64 on 8 waves, 5 = 128x64, 6 = 64x128,
  * 7 = 32x32 with 32-k stages, 8 = 64x256 with 32-k stages, 9 = 32x64 with
- * 128-k stages, 10 = 64x64 on 8 waves with 128-k stages;
+ * 128-k stages, 10 = 64x64 on 8 waves with 128-k stages, 23 = 32x32 on 8
+ * waves fed by a ring of 64-k LDS stages through direct-to-LDS loads, four k
+ * tiles at a time (two where four do not divide the number of k tiles),
+ * 24 = 64x32 likewise, two k tiles at a time; 23 and 24 need K a multiple
+ * of 64 and k tiles of an even number of 32-k blocks (23 with several k
+ * tiles: at least four blocks);
  * bf16: 11 = 128x128, 12 = 64x64, 13 = 128x128 with 128-k stages,
  * 14 = 256x128, 15 = 128x256, 16 = 64x128 with 128-k stages, 17 = 64x64
  * with 32-k stages, 18 = 256x256 on 2x4 waves, 19 = 256x256 on 4x2 waves,

@@ -133,7 +133,7 @@ def test_every_persistent_tile_shape_gives_the_same_bits(bi, router):
     batch = wl.router_batch(300, w)
     x = dev(batch.x)
     ref = host(bi.bi_linear_f32(x, weight_t(wd), bd))
-    for code in range(1, 11):
+    for code in (*range(1, 11), 23, 24):
         banner(f"router fp32 M=300 persistent tile code {code}")
         y = host(bi.bi_lab_linear(x, weight_t(wd), bd, path=bi.BI_PATH_PERSISTENT | (code << 8)))
         assert_bitwise(y, ref, f"tile code {code}")
@@ -144,9 +144,37 @@ def test_every_persistent_tile_shape_gives_the_same_bits(bi, router):
     x2 = dev(g.standard_normal((70, 320)).astype(np.float32))
     ref2 = host(bi.bi_linear_f32(x2, weight_t(dev(w2)), None))
     assert_close(ref2, oracle.linear_f32(host(x2), w2, None), F32_ATOL, F32_RTOL, "N=48 K=320")
-    for code in range(1, 11):
+    for code in (*range(1, 11), 23, 24):
         y = host(bi.bi_lab_linear(x2, weight_t(dev(w2)), None, path=bi.BI_PATH_PERSISTENT | (code << 8)))
         assert_bitwise(y, ref2, f"N=48 tile code {code}")
+
+
+@pytest.mark.parametrize("M,N,K,block_k", [
+    (1000, 256, 7168, 256),    # 28 k tiles: the 32x32 ring works on four at a time
+    (300, 96, 768, 128),       # 6 k tiles: two at a time
+    (2047, 208, 4096, 64),     # k tiles of two blocks: the 64x32 ring only (ragged N)
+    (4100, 48, 1024, 256),     # more 32x32 tiles than compute units
+    (9000, 32, 512, 128),      # more tiles than compute units, one step per k tile group
+    (64, 32, 4096, 4096),      # one k tile: both fall back
+])
+def test_ring_fed_fp32_tiles(bi, M, N, K, block_k):
+    # the ring-fed fp32 shapes (32x32 on four or two k tiles at a time, 64x32
+    # on two) hand tile partials between waves and fold them in k tile order:
+    # bit for bit the 32x32 register-staged shape, which itself meets the oracle
+    g = np.random.default_rng(M + N + K)
+    w = g.standard_normal((N, K)).astype(np.float32) * 0.02
+    b = (g.standard_normal(N) * 0.01).astype(np.float32)
+    xh = g.standard_normal((M, K)).astype(np.float32)
+    x, wd, bd = dev(xh), dev(w), dev(b)
+    r = bi.bi_describe_recipe(bi.BI_F32, N, K)
+    r.block_k = block_k
+    banner(f"fp32 ring tiles M={M} N={N} K={K} block_k={block_k}")
+    y3 = host(bi.bi_lab_linear(x, weight_t(wd), bd, recipe=r, path=bi.BI_PATH_PERSISTENT | (3 << 8)))
+    if M * K <= 300 * 768:
+        assert_close(y3, oracle.linear_f32(xh, w, b), F32_ATOL, F32_RTOL, "oracle")
+    for code in (23, 24):
+        y = host(bi.bi_lab_linear(x, weight_t(wd), bd, recipe=r, path=bi.BI_PATH_PERSISTENT | (code << 8)))
+        assert_bitwise(y, y3, f"tile code {code} vs 3")
 
 
 def test_repeat_determinism_with_workspace_reuse(bi, router):
