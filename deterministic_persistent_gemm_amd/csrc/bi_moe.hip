@@ -504,23 +504,25 @@ __device__ __forceinline__ float topk_sum(const float* __restrict__ part, const 
 
 // Workgroup = TW x NW waves: TW waves split the k tile partials of one
 // output tile (folded in ascending order through LDS), NW waves take NW
-// neighbouring 16-column tiles.  A work unit is MT tiles of 16 rows of one
-// expert; each wave runs MT x NB independent chains over one weight slab.
-// ACT (kActNone: GEMM2, fp32 partial per pair; kActSwiGLU: each wave carries
-// a gate block and the matching up block; kActSqReLU: one block) applies the
-// activation in the epilogue.
-template <int TW, int NW, int MT, int ACT, int CH>
+// neighbouring groups of NT 16-column tiles.  A work unit is MT tiles of 16
+// rows of one expert; each wave runs MT x NB x NT independent chains, its
+// activation fragments shared by the NT column tiles.  ACT (kActNone: GEMM2,
+// fp32 partial per pair; kActSwiGLU: a gate block and the matching up block
+// per column tile; kActSqReLU: one block) applies the activation in the
+// epilogue.
+template <int TW, int NW, int MT, int ACT, int CH, int NT>
 __global__ __launch_bounds__(TW * NW * 64) void k_grouped(GroupedArgs g)
 {
-    constexpr int NB = ACT == kActSwiGLU ? 2 : 1;       // output blocks per wave
-    __shared__ f32x4 lds[(TW > 1) ? TW * NW * MT * NB * 64 : 1];
+    constexpr int NB = ACT == kActSwiGLU ? 2 : 1;       // output blocks per column tile
+    constexpr int NBT = NB * NT;                        // weight blocks per wave: b * NT + j
+    __shared__ f32x4 lds[(TW > 1) ? TW * NW * MT * NBT * 64 : 1];
     const int u = blockIdx.y;
     if (u >= g.nunits[0])
         return;
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     const int tw = wid % TW, nw = wid / TW;
     const int r = lane & 15, gslot = lane >> 4;
-    const int nt = blockIdx.x * NW + nw;
+    const int nt = (blockIdx.x * NW + nw) * NT;        // first column tile of the wave
     const bool nt_ok = nt * 16 < g.n_out;
     const int e = g.unit_expert[u];
     const int row0 = g.unit_row[u];
@@ -535,40 +537,44 @@ __global__ __launch_bounds__(TW * NW * 64) void k_grouped(GroupedArgs g)
         ap[m] = g.a + (int64_t)arow * g.lda + kSlotLen * gslot;
     }
     const uint16_t* we = g.w + (int64_t)e * g.w_stride;
-    const int ntc = nt_ok ? nt : 0;
-    const uint16_t* wp[NB];
-    wp[0] = we + (int64_t)(ntc * 16 + r) * g.ldw + kSlotLen * gslot;
-    if (ACT == kActSwiGLU)
-        wp[NB - 1] = we + (int64_t)(g.up_offset + ntc * 16 + r) * g.ldw + kSlotLen * gslot;
+    const uint16_t* wp[NBT];
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+        // column tiles past n_out read tile 0 and are never stored
+        const int ntc = (nt + j) * 16 < g.n_out ? nt + j : 0;
+        wp[j] = we + (int64_t)(ntc * 16 + r) * g.ldw + kSlotLen * gslot;
+        if (ACT == kActSwiGLU)
+            wp[NT + j] = we + (int64_t)(g.up_offset + ntc * 16 + r) * g.ldw + kSlotLen * gslot;
+    }
 
-    f32x4 acc[MT][NB];
+    f32x4 acc[MT][NBT];
     for (int t = tw; t < g.tiles_k; t += TW) {
-        f32x4 P[MT][NB];
+        f32x4 P[MT][NBT];
 #pragma unroll
         for (int m = 0; m < MT; ++m)
 #pragma unroll
-            for (int b = 0; b < NB; ++b)
+            for (int b = 0; b < NBT; ++b)
                 P[m][b] = f32x4{0.f, 0.f, 0.f, 0.f};
         const int64_t k0 = (int64_t)t * g.kbpt * kKBlock;
         // chunks of CH k blocks, the next chunk's loads in flight while the
         // current one feeds the chains (two fragment buffers)
         Frag<false> af0[CH][MT], af1[CH][MT];
-        Frag<false> bf0[CH][NB], bf1[CH][NB];
-        auto load_chunk = [&](Frag<false> (&af)[CH][MT], Frag<false> (&bf)[CH][NB], int c) {
+        Frag<false> bf0[CH][NBT], bf1[CH][NBT];
+        auto load_chunk = [&](Frag<false> (&af)[CH][MT], Frag<false> (&bf)[CH][NBT], int c) {
 #pragma unroll
             for (int i = 0; i < CH; ++i) {
 #pragma unroll
-                for (int b = 0; b < NB; ++b)
+                for (int b = 0; b < NBT; ++b)
                     load_frag<BF16>(bf[i][b], wp[b] + k0 + (int64_t)(c + i) * kKBlock);
 #pragma unroll
                 for (int m = 0; m < MT; ++m)
                     load_frag<BF16>(af[i][m], ap[m] + k0 + (int64_t)(c + i) * kKBlock);
             }
         };
-        auto run_chunk = [&](Frag<false> (&af)[CH][MT], Frag<false> (&bf)[CH][NB]) {
+        auto run_chunk = [&](Frag<false> (&af)[CH][MT], Frag<false> (&bf)[CH][NBT]) {
 #pragma unroll
             for (int i = 0; i < CH; ++i)
-                mfma_tiles<MT, NB>(af[i], bf[i], P);
+                mfma_tiles<MT, NBT>(af[i], bf[i], P);
         };
         load_chunk(af0, bf0, 0);
         for (int c = 0; c < g.kbpt; c += 2 * CH) {
@@ -587,15 +593,15 @@ __global__ __launch_bounds__(TW * NW * 64) void k_grouped(GroupedArgs g)
 #pragma unroll
             for (int m = 0; m < MT; ++m)
 #pragma unroll
-                for (int b = 0; b < NB; ++b)
+                for (int b = 0; b < NBT; ++b)
                     acc[m][b] = (t == 0) ? P[m][b] : acc[m][b] + P[m][b];
         } else {
             // one tile per wave (TW == tiles_k); stage it for the ordered fold
 #pragma unroll
             for (int m = 0; m < MT; ++m)
 #pragma unroll
-                for (int b = 0; b < NB; ++b)
-                    lds[(((t * NW + nw) * MT + m) * NB + b) * 64 + lane] = P[m][b];
+                for (int b = 0; b < NBT; ++b)
+                    lds[(((t * NW + nw) * MT + m) * NBT + b) * 64 + lane] = P[m][b];
         }
     }
     if (TW > 1) {
@@ -605,29 +611,32 @@ __global__ __launch_bounds__(TW * NW * 64) void k_grouped(GroupedArgs g)
 #pragma unroll
         for (int m = 0; m < MT; ++m)
 #pragma unroll
-            for (int b = 0; b < NB; ++b) {
-                acc[m][b] = lds[(((0 * NW + nw) * MT + m) * NB + b) * 64 + lane];
+            for (int b = 0; b < NBT; ++b) {
+                acc[m][b] = lds[(((0 * NW + nw) * MT + m) * NBT + b) * 64 + lane];
                 for (int t = 1; t < g.tiles_k; ++t)
-                    acc[m][b] = acc[m][b] + lds[(((t * NW + nw) * MT + m) * NB + b) * 64 + lane];
+                    acc[m][b] = acc[m][b] + lds[(((t * NW + nw) * MT + m) * NBT + b) * 64 + lane];
             }
     }
     if (ACT != kActNone && !nt_ok)
         return;
 
-    const int col = nt * 16 + acc_col(lane);
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+    const int col = (nt + j) * 16 + acc_col(lane);
+    const bool col_ok = (nt + j) * 16 < g.n_out;
 #pragma unroll
     for (int m = 0; m < MT; ++m)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const int p = row0 + m * kTileRows + acc_row(lane, q);
-            if (p >= row_end || !nt_ok)
+            if (p >= row_end || !col_ok)
                 continue;
             if (ACT == kActSwiGLU) {
                 // storage point of the gate/up projection, then the activation
                 // in fp32 (with the routing probability if asked), one
                 // rounding to bf16
-                const float hg = bf16_to_f32(f32_to_bf16_rne(acc[m][0][q]));
-                const float hu = bf16_to_f32(f32_to_bf16_rne(acc[m][NB - 1][q]));
+                const float hg = bf16_to_f32(f32_to_bf16_rne(acc[m][j][q]));
+                const float hu = bf16_to_f32(f32_to_bf16_rne(acc[m][NT + j][q]));
                 const float sg = 1.0f / (1.0f + expf(-hg));
                 float av = (hg * sg) * hu;
                 if (g.act_probs)
@@ -636,17 +645,18 @@ __global__ __launch_bounds__(TW * NW * 64) void k_grouped(GroupedArgs g)
             } else if (ACT == kActSqReLU) {
                 // squared ReLU of the bf16 storage point (exact in fp32: an
                 // 8-bit significand squared), then the optional probability
-                const float h = bf16_to_f32(f32_to_bf16_rne(acc[m][0][q]));
+                const float h = bf16_to_f32(f32_to_bf16_rne(acc[m][j][q]));
                 const float rl = h > 0.f ? h : 0.f;
                 float av = rl * rl;
                 if (g.act_probs)
                     av = av * g.probs[g.sorted[p]];
                 g.act[(int64_t)p * g.n_out + col] = f32_to_bf16_rne(av);
             } else {
-                g.part[(int64_t)g.sorted[p] * g.n_out + col] = acc[m][0][q];
+                g.part[(int64_t)g.sorted[p] * g.n_out + col] = acc[m][j][q];
             }
         }
-    if constexpr (ACT == kActNone && TW == 1) {
+    }
+    if constexpr (ACT == kActNone && TW == 1 && NT == 1) {
         // The top-k sum in the same launch (small M).  Every workgroup of
         // column block bx runs on XCD bx mod 8 (workgroups go to the XCDs
         // round-robin and the grid's row is a multiple of 8 blocks), so the
@@ -711,10 +721,10 @@ static int pick_ch(int kbpt)
     return 1;
 }
 
-template <int TW, int NW, int MT, int ACT>
+template <int TW, int NW, int MT, int ACT, int NT>
 static hipError_t launch_grouped_tw(const GroupedArgs& g, int64_t max_units, hipStream_t s)
 {
-    const int ntiles = (g.n_out / 16 + NW - 1) / NW;
+    const int ntiles = (g.n_out / 16 + NW * NT - 1) / (NW * NT);
     dim3 grid((unsigned)ntiles, (unsigned)max_units);
     // two buffers of CH k blocks of MT activation and NB weight fragments.
     // Short chunks keep the registers per wave low, and more waves per SIMD
@@ -727,23 +737,33 @@ static hipError_t launch_grouped_tw(const GroupedArgs& g, int64_t max_units, hip
     if (ch > ch_max)
         ch = ch_max;
     switch (ch) {
-    case 4:  k_grouped<TW, NW, MT, ACT, 4><<<grid, TW * NW * 64, 0, s>>>(g); break;
-    case 2:  k_grouped<TW, NW, MT, ACT, 2><<<grid, TW * NW * 64, 0, s>>>(g); break;
-    default: k_grouped<TW, NW, MT, ACT, 1><<<grid, TW * NW * 64, 0, s>>>(g); break;
+    case 4:  k_grouped<TW, NW, MT, ACT, 4, NT><<<grid, TW * NW * 64, 0, s>>>(g); break;
+    case 2:  k_grouped<TW, NW, MT, ACT, 2, NT><<<grid, TW * NW * 64, 0, s>>>(g); break;
+    default: k_grouped<TW, NW, MT, ACT, 1, NT><<<grid, TW * NW * 64, 0, s>>>(g); break;
     }
     return hipGetLastError();
 }
+
+// Column tiles per wave for 32-row work units of kernels with one weight
+// block per tile (the down projection, squared ReLU): the wave's activation
+// fragments serve both tiles, which halves the activation rows streamed per
+// weight byte (measured on MI355X, Qwen3-30B-A3B-shaped layer at M=256:
+// squared ReLU 245.6 -> 218.4 us, SwiGLU 306.7 -> 300.6; four tiles, or two
+// for the SwiGLU gate/up kernel with its gate and up blocks, cost more in
+// registers than they save)
+constexpr int kUnit32Tiles = 2;
 
 template <int MT, int ACT>
 static hipError_t launch_grouped_mt(const GroupedArgs& g, int64_t max_units, hipStream_t s)
 {
     // k tile partials of one output tile are spread over the workgroup's
     // waves when there are 2 or 4; otherwise the waves take more columns
+    constexpr int NT = (MT == 2 && ACT != kActSwiGLU) ? kUnit32Tiles : 1;
     if (g.tiles_k == 4)
-        return launch_grouped_tw<4, 1, MT, ACT>(g, max_units, s);
+        return launch_grouped_tw<4, 1, MT, ACT, NT>(g, max_units, s);
     if (g.tiles_k == 2)
-        return launch_grouped_tw<2, 2, MT, ACT>(g, max_units, s);
-    return launch_grouped_tw<1, 4, MT, ACT>(g, max_units, s);
+        return launch_grouped_tw<2, 2, MT, ACT, NT>(g, max_units, s);
+    return launch_grouped_tw<1, 4, MT, ACT, NT>(g, max_units, s);
 }
 
 template <int ACT>

@@ -215,7 +215,7 @@ def test_small_shape_storage_points(bi, M, E, topk):
 
 
 @pytest.mark.parametrize("v", [("sqrelu", False, True, False), ("sqrelu", False, False, True)])
-@pytest.mark.parametrize("M", [1, 16, 64])
+@pytest.mark.parametrize("M", [1, 16, 64, 256])
 def test_qwen_shape_squared_relu_storage_points(bi, M, v):
     act, pa, aw, f64 = v
     w = wl.moe_weights(0)
