@@ -83,6 +83,56 @@ __device__ __forceinline__ void store_acc(const LinearArgs& a, int row0, int col
 // 128-byte L2 line, at the start of the workspace.
 constexpr int kCounterStride = kDecodeCounterBytes / 4 / kDecodeMaxCounters;
 
+// The ordered fold of one output tile's partials, for the four accumulator
+// rows of this lane: acc = P0; acc = acc + P1; ... (p points at this lane's
+// entry of partial 0, partials 64 entries apart).  Up to 32 partials are
+// requested at once, so the usual case is one memory round trip.  NQ rows are
+// folded: where the M tile holds fewer than four rows (M < 4) the rows past M
+// are never stored, so their loads and adds are skipped; the folded rows get
+// exactly the same operations.
+template <int NQ>
+__device__ __forceinline__ f32x4 fold_partials_nq(const f32x4* __restrict__ p, int tiles_k)
+{
+    constexpr int kBatch = 32;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int u0 = 0; u0 < tiles_k; u0 += kBatch) {
+        const int n = min(kBatch, tiles_k - u0);
+        f32x4 v[kBatch];
+#pragma unroll
+        for (int i = 0; i < kBatch; ++i)
+            if (i < n) {
+                const f32x4* q = p + (int64_t)(u0 + i) * 64;
+                if constexpr (NQ == 4) {
+                    v[i] = *q;
+                } else if constexpr (NQ == 2) {
+                    const float2 t = *reinterpret_cast<const float2*>(q);
+                    v[i][0] = t.x;
+                    v[i][1] = t.y;
+                } else {
+                    v[i][0] = *reinterpret_cast<const float*>(q);
+                }
+            }
+#pragma unroll
+        for (int i = 0; i < kBatch; ++i)
+            if (i < n)
+#pragma unroll
+                for (int c = 0; c < NQ; ++c)
+                    acc[c] = (u0 + i == 0) ? v[i][c] : acc[c] + v[i][c];
+    }
+    return acc;
+}
+
+// rows: the rows of the M tile that exist (M - 16 mt, wave-uniform).  Below
+// four only the lanes of rows 0..3 store, and they hold that many rows.
+__device__ __forceinline__ f32x4 fold_partials(const f32x4* __restrict__ p, int tiles_k, int rows)
+{
+    if (rows >= 3)
+        return fold_partials_nq<4>(p, tiles_k);
+    if (rows == 2)
+        return fold_partials_nq<2>(p, tiles_k);
+    return fold_partials_nq<1>(p, tiles_k);
+}
+
 // One wave per (16-column N tile, k tile partial, group of MT 16-row M tiles).
 // The wave loads its slab of W once and runs MT independent chains over it,
 // one per M tile.  With a single k tile (block_k == K) the wave finishes the
@@ -215,29 +265,14 @@ __global__ __launch_bounds__(64) void k_decode(LinearArgs a, int kbpt, int tiles
             const int row0 = mt * 16 + acc_row(lane, 0);
             if (mt >= mtiles || row0 >= a.M)
                 continue;
+            // this wave's own partial is read back with the others
             const f32x4* p = partials + ((int64_t)mt * ntiles + nt) * tiles_k * 64 + lane;
-            constexpr int kBatch = 32;
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            for (int u0 = 0; u0 < tiles_k; u0 += kBatch) {
-                const int n = min(kBatch, tiles_k - u0);
-                f32x4 v[kBatch];
-#pragma unroll
-                for (int i = 0; i < kBatch; ++i)
-                    if (i < n)
-                        v[i] = p[(int64_t)(u0 + i) * 64];   // this wave's own partial included
-#pragma unroll
-                for (int i = 0; i < kBatch; ++i)
-                    if (i < n)
-                        acc = (u0 + i == 0) ? v[i] : acc + v[i];
-            }
-            store_acc(a, row0, col, acc, bcol);
+            store_acc(a, row0, col, fold_partials(p, tiles_k, a.M - mt * 16), bcol);
         }
     }
 }
 
-// Ordered fold of the tile partials: acc = P0; acc = acc + P1; ...; + bias.
-// Up to 32 partials are requested at once, so the usual case is a single
-// memory round trip.
+// Ordered fold of the tile partials (fold_partials), then the bias.
 __global__ __launch_bounds__(64) void k_decode_fold(LinearArgs a, int tiles_k,
                                                     const f32x4* __restrict__ partials)
 {
@@ -249,21 +284,7 @@ __global__ __launch_bounds__(64) void k_decode_fold(LinearArgs a, int tiles_k,
         return;
     const float b = load_bias(a, nt * 16 + acc_col(lane));
     const f32x4* p = partials + ((int64_t)mt * ntiles + nt) * tiles_k * 64 + lane;
-    constexpr int kBatch = 32;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int u0 = 0; u0 < tiles_k; u0 += kBatch) {
-        const int n = min(kBatch, tiles_k - u0);
-        f32x4 v[kBatch];
-#pragma unroll
-        for (int i = 0; i < kBatch; ++i)
-            if (i < n)
-                v[i] = p[(int64_t)(u0 + i) * 64];
-#pragma unroll
-        for (int i = 0; i < kBatch; ++i)
-            if (i < n)
-                acc = (u0 + i == 0) ? v[i] : acc + v[i];
-    }
-    store_acc(a, row0, nt * 16 + acc_col(lane), acc, b);
+    store_acc(a, row0, nt * 16 + acc_col(lane), fold_partials(p, tiles_k, a.M - mt * 16), b);
 }
 
 // One workgroup per (16-row M tile, 16-column N tile), NW waves.  Wave w
