@@ -196,6 +196,8 @@ __global__ __launch_bounds__(64) void k_decode(LinearArgs a, int kbpt, int tiles
     // loads are in flight (two fragment buffers, loop unrolled by two).
     FragOf<OW> wf0[CH][1], wf1[CH][1];
     FragOf<OX> xf0[CH][MT], xf1[CH][MT];
+    // block by block (weight, then its activation rows), so that the chain
+    // can start on the first block while the later ones are still arriving
     auto load_chunk = [&](FragOf<OW> (&wf)[CH][1], FragOf<OX> (&xf)[CH][MT], int c) {
 #pragma unroll
         for (int i = 0; i < CH; ++i) {
@@ -205,31 +207,39 @@ __global__ __launch_bounds__(64) void k_decode(LinearArgs a, int kbpt, int tiles
                 load_frag_nt<OW>(wf[i][0], wp + (int64_t)(c + i) * kKBlock);
             else
                 load_frag<OW>(wf[i][0], wp + (int64_t)(c + i) * kKBlock);
-        }
 #pragma unroll
-        for (int m = 0; m < MT; ++m)
-#pragma unroll
-            for (int i = 0; i < CH; ++i)
+            for (int m = 0; m < MT; ++m)
                 load_frag<OX>(xf[i][m], xp[m] + (int64_t)(c + i) * kKBlock);
+            // keep the issue order: the scheduler would otherwise put the
+            // first block's loads last and wait for all of them
+            __builtin_amdgcn_sched_barrier(0);
+        }
     };
     auto run_chunk = [&](FragOf<OW> (&wf)[CH][1], FragOf<OX> (&xf)[CH][MT]) {
 #pragma unroll
         for (int i = 0; i < CH; ++i)
             mfma_tiles<MT, 1>(xf[i], wf[i], P);
     };
-    load_chunk(wf0, xf0, 0);
-    for (int c = 0; c < kbpt; c += 2 * CH) {
-        if (c + CH < kbpt)
-            load_chunk(wf1, xf1, c + CH);
-        // every load issued so far is in flight before the chain waits on one
-        __builtin_amdgcn_sched_barrier(0);
+    if (kbpt == CH) {
+        // one chunk (the usual decode tile): straight-line code, so that each
+        // block's instructions wait only for that block's loads
+        load_chunk(wf0, xf0, 0);
         run_chunk(wf0, xf0);
-        if (c + CH >= kbpt)
-            break;
-        if (c + 2 * CH < kbpt)
-            load_chunk(wf0, xf0, c + 2 * CH);
-        __builtin_amdgcn_sched_barrier(0);
-        run_chunk(wf1, xf1);
+    } else {
+        load_chunk(wf0, xf0, 0);
+        for (int c = 0; c < kbpt; c += 2 * CH) {
+            if (c + CH < kbpt)
+                load_chunk(wf1, xf1, c + CH);
+            // every load issued so far is in flight before the chain waits on one
+            __builtin_amdgcn_sched_barrier(0);
+            run_chunk(wf0, xf0);
+            if (c + CH >= kbpt)
+                break;
+            if (c + 2 * CH < kbpt)
+                load_chunk(wf0, xf0, c + 2 * CH);
+            __builtin_amdgcn_sched_barrier(0);
+            run_chunk(wf1, xf1);
+        }
     }
 
     const int col = nt * 16 + acc_col(lane);
