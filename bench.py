@@ -200,7 +200,7 @@ def main():
     if not args.no_bf16:
         extra["dense_bf16"] = dense_bf16_leg(torch, np, bi, wl, dev)
     if not args.no_moe:
-        extra["moe"] = moe_leg(torch, np, bi, wl, dev)
+        extra["moe"] = moe_leg(torch, np, bi, wl, dev, floors["cold_read_1GiB"]["GBps"])
     if not args.no_topk:
         extra["indexer_topk"] = topk_leg(torch, np, bi, wl, dev)
 
@@ -319,9 +319,10 @@ def dense_bf16_leg(torch, np, bi, wl, dev):
     return res
 
 
-def moe_leg(torch, np, bi, wl, dev):
+def moe_leg(torch, np, bi, wl, dev, stream_gbs=None):
     """Qwen3-30B-A3B-shaped MoE layer; algorithmic bytes count each distinct
-    expert touched once (measured from the returned ids)."""
+    expert touched once (measured from the returned ids).  stream_frac: the
+    rate against the long cold read of the same run (floors.cold_read_1GiB)."""
     w = wl.moe_weights(0)
     wr = torch.from_numpy(w.w_router).to(dev)
     w13 = torch.from_numpy(w.w13.view(np.int16)).view(torch.bfloat16).to(dev)
@@ -338,6 +339,8 @@ def moe_leg(torch, np, bi, wl, dev):
         res[str(M)] = {"us": round(us, 2), "distinct_experts": distinct,
                        "GBps": round(nbytes / us / 1e3, 1), "TFLOPs": round(flops / us / 1e6, 2),
                        "hbm_frac": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4)}
+        if stream_gbs:
+            res[str(M)]["stream_frac"] = round(nbytes / us / 1e3 / stream_gbs, 4)
     # squared-ReLU experts (w1 = the gate half), weights applied in an fp32 top-k sum
     w1 = w13[:, :I, :].contiguous()
     for M in (16, 256):
@@ -351,6 +354,8 @@ def moe_leg(torch, np, bi, wl, dev):
         res[f"sqrelu_{M}"] = {"us": round(us, 2), "distinct_experts": distinct,
                               "GBps": round(nbytes / us / 1e3, 1),
                               "hbm_frac": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4)}
+        if stream_gbs:
+            res[f"sqrelu_{M}"]["stream_frac"] = round(nbytes / us / 1e3 / stream_gbs, 4)
     return res
 
 
@@ -456,7 +461,9 @@ def floors_leg(torch, bi, dev):
     Empty kernel: 512 workgroups, per launch in a replayed graph of 100
     launches (one or two per group).  Cold reads: 4 MiB (96 copies) and
     32 MiB (12 copies) read once each by a plain streaming kernel (256 and 512
-    workgroups of 256 threads, the fastest measured).  Clock: shader cycles
+    workgroups of 256 threads, the fastest measured), and 1 GiB (two copies,
+    1024 workgroups) for the streaming rate of a long read.  L2 read: the rate
+    at which the L2 delivers resident data to the compute units.  Clock: shader cycles
     (s_memtime) per 100 MHz wall tick over a dependent fp32 chain, with one
     wave per compute unit and with eight."""
     stream = torch.cuda.Stream(dev)
@@ -472,6 +479,22 @@ def floors_leg(torch, bi, dev):
         us = time_graph_calls(torch, [lambda b=b: bi.bi_lab_stream_read(b, sink, grid) for b in bufs], stream)
         res[f"cold_read_{mib}MiB"] = {"us": round(us, 3), "GBps": round(nb / us / 1e3, 1), "workgroups": grid}
         del bufs
+    # the streaming rate of a long read: what any kernel that reads a large
+    # weight once can reach (two 1 GiB buffers, 1024 workgroups)
+    nb = 1 << 30
+    bufs = [torch.ones(nb // 4, dtype=torch.float32, device=dev) for _ in range(2)]
+    sink = torch.empty(1024, dtype=torch.int32, device=dev)
+    us = time_graph_calls(torch, [lambda b=b: bi.bi_lab_stream_read(b, sink, 1024) for b in bufs], stream)
+    res["cold_read_1GiB"] = {"us": round(us, 1), "GBps": round(nb / us / 1e3, 1), "workgroups": 1024}
+    del bufs
+    # L2 to compute units: 512 workgroups each read the same 1 MiB (held in
+    # every XCD's L2 after the first pass) four times
+    src = torch.ones(1 << 18, dtype=torch.float32, device=dev)
+    sink = torch.empty(512, dtype=torch.int32, device=dev)
+    us = time_graph_calls(torch, [lambda: bi.bi_lab_l2_read(src, sink, 512, 4)] * 4, stream)
+    gbs = 512 * 4 * (1 << 20) / us / 1e3
+    res["l2_read"] = {"GBps": round(gbs, 1), "GBps_per_CU": round(gbs / 256, 1), "workgroups": 512,
+                      "probe": "every workgroup reads the same L2-resident 1 MiB, 16-byte loads, 8 in flight"}
     out = torch.zeros((2048, 3), dtype=torch.int64, device=dev)
     for grid, name in ((256, "sclk_MHz_one_wave_per_CU"), (2048, "sclk_MHz_eight_waves_per_CU")):
         with torch.cuda.stream(stream):

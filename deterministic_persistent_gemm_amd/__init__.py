@@ -64,6 +64,7 @@ _lib.bi_moe_grouped_gemm_ex.argtypes = [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I
 _lib.bi_lab_xcc_ids.argtypes = [_P, _I32, _I32, _P]
 _lib.bi_lab_empty.argtypes = [_I32, _I32, _P]
 _lib.bi_lab_stream_read.argtypes = [_P, _I64, _P, _I32, _P]
+_lib.bi_lab_l2_read.argtypes = [_P, _I64, _I32, _P, _I32, _P]
 _lib.bi_lab_clock.argtypes = [_P, _I32, _I32, _P]
 _lib.bi_lab_lds_read.argtypes = [_P, _I32, _I32, _P]
 _lib.bi_lab_mfma_rate.argtypes = [_P, _I32, _I32, _I32, _P]
@@ -74,7 +75,7 @@ for _f in (_lib.bi_linear_f32, _lib.bi_linear_bf16, _lib.bi_negctl_linear_f32, _
            _lib.bi_moe_grouped_gemm, _lib.bi_describe_recipe, _lib.bi_indexer_topk,
            _lib.bi_moe_grouped_gemm_ex, _lib.bi_lab_xcc_ids, _lib.bi_lab_empty, _lib.bi_lab_stream_read,
            _lib.bi_lab_clock, _lib.bi_lab_plan, _lib.bi_lab_moe_layout, _lib.bi_linear_f32_noalloc,
-           _lib.bi_lab_lds_read, _lib.bi_lab_mfma_rate):
+           _lib.bi_lab_lds_read, _lib.bi_lab_mfma_rate, _lib.bi_lab_l2_read):
     _f.restype = _I32
 for _f in (_lib.bi_linear_workspace_size, _lib.bi_lab_workspace_size, _lib.bi_moe_workspace_size):
     _f.restype = _SZ
@@ -404,6 +405,18 @@ def bi_lab_stream_read(src: torch.Tensor, sink: torch.Tensor, grid: int):
     s = _stream(src.device)
     _check(_lib.bi_lab_stream_read(_ptr(src), src.numel() * src.element_size(), _ptr(sink), grid,
                                    ctypes.c_void_p(s.cuda_stream)), "bi_lab_stream_read")
+
+
+def bi_lab_l2_read(src: torch.Tensor, sink: torch.Tensor, grid: int, iters: int):
+    """Every one of `grid` workgroups reads all of `src` (32 KiB .. 2 MiB, a
+    power of two: L2-resident after the first pass) `iters` times (L2-to-CU
+    delivery rate); sink: int32 [>= grid]."""
+    if not (src.is_cuda and src.is_contiguous() and sink.is_cuda and sink.dtype == torch.int32
+            and sink.numel() >= grid and src.device == sink.device):
+        raise ValueError("bi_lab_l2_read: contiguous CUDA src and an int32 sink of >= grid entries")
+    s = _stream(src.device)
+    _check(_lib.bi_lab_l2_read(_ptr(src), src.numel() * src.element_size(), iters, _ptr(sink), grid,
+                               ctypes.c_void_p(s.cuda_stream)), "bi_lab_l2_read")
 
 
 def bi_lab_clock(out: torch.Tensor, grid: int, iters: int):

@@ -235,6 +235,18 @@ bi_status_t bi_lab_stream_read(const void* src, int64_t bytes, uint32_t* sink, i
     return launch_stream_read(src, bytes, sink, grid, stream) == hipSuccess ? BI_OK : BI_EHIP;
 }
 
+bi_status_t bi_lab_l2_read(const void* src, int64_t bytes, int32_t iters, uint32_t* sink, int32_t grid,
+                           hipStream_t stream)
+{
+    // a power of two of at least one full round (256 lanes x 8 loads x 16 B)
+    // and at most 2 MiB
+    if (!src || !sink || bytes < 32768 || bytes > (int64_t(2) << 20) || (bytes & (bytes - 1)) != 0 ||
+        iters <= 0 || grid <= 0 || grid > 65535 || (reinterpret_cast<uintptr_t>(src) & 15u) != 0 ||
+        (reinterpret_cast<uintptr_t>(sink) & 3u) != 0)
+        return BI_EINVAL;
+    return launch_l2_read(src, bytes, iters, sink, grid, stream) == hipSuccess ? BI_OK : BI_EHIP;
+}
+
 bi_status_t bi_lab_clock(uint64_t* out, int32_t grid, int32_t iters, hipStream_t stream)
 {
     if (!out || grid <= 0 || grid > 65535 || iters <= 0 || (reinterpret_cast<uintptr_t>(out) & 7u) != 0)

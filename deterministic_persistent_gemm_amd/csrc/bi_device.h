@@ -160,6 +160,38 @@ __device__ __forceinline__ void mfma_tiles(const Frag<false> (&xf)[FM], const Fr
             part[fm][fn] = mfma_block(xf[fm], wf[fn], part[fm][fn]);
 }
 
+// Double-buffered walk over nblk k blocks in chunks of CH blocks (CH divides
+// nblk): while one buffer's chunk feeds the chains the other buffer's chunk
+// is in flight.  load0/load1(c) issue the loads of the chunk starting at
+// block c into buffer 0/1, run0/run1(c) feed that chunk to the chains.  The
+// steady-state loop issues both of its loads unconditionally and the tail is
+// peeled, so every chunk waits only for its own loads; with a load guarded
+// by a branch inside the loop the compiler's wait at the join covers the
+// loads just issued as well (a full wait before every chunk).
+template <int CH, typename L0, typename L1, typename R0, typename R1>
+__device__ __forceinline__ void chunk_pipeline(int nblk, L0&& load0, L1&& load1, R0&& run0, R1&& run1)
+{
+    load0(0);
+    int c = 0;
+    for (; c + 2 * CH < nblk; c += 2 * CH) {
+        load1(c + CH);
+        __builtin_amdgcn_sched_barrier(0);
+        run0(c);
+        load0(c + 2 * CH);
+        __builtin_amdgcn_sched_barrier(0);
+        run1(c + CH);
+    }
+    if (c + CH < nblk) {
+        load1(c + CH);
+        __builtin_amdgcn_sched_barrier(0);
+        run0(c);
+        run1(c + CH);
+    } else {
+        __builtin_amdgcn_sched_barrier(0);
+        run0(c);
+    }
+}
+
 // Inclusive prefix sum over the wave's lanes: a Hillis-Steele scan inside
 // each row of 16 lanes with DPP row shifts (lanes whose source falls outside
 // the row add 0), then the totals of the rows below are added.

@@ -71,6 +71,48 @@ hipError_t launch_stream_read(const void* src, int64_t bytes, uint32_t* sink, in
     return hipGetLastError();
 }
 
+// L2-to-compute-unit delivery rate.  Every workgroup reads the same region
+// of n16 16-byte chunks (n16 a power of two, at most 2 MiB, so that after
+// its first pass the region stays in each XCD's L2) `iters` times with
+// 16-byte loads, eight in flight per lane; each workgroup starts at its own
+// offset (and each pass one KiB further on) so that the workgroups of an XCD
+// spread over the L2 channels and no pass repeats the previous one's
+// addresses.
+__global__ __launch_bounds__(256) void k_l2_read(const u32x4* __restrict__ src, int n16, int iters,
+                                                 uint32_t* __restrict__ sink)
+{
+    const int mask = n16 - 1;
+    const int rounds = n16 / (256 * 8);
+    u32x4 acc = {0u, 0u, 0u, 0u};
+    for (int it = 0; it < iters; ++it) {
+        const int i0 = (int)(((uint32_t)blockIdx.x * 4099u + (uint32_t)it * 64u) & (uint32_t)mask) + threadIdx.x;
+        for (int r = 0; r < rounds; ++r) {
+            u32x4 v[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                v[j] = src[(i0 + (r * 8 + j) * 256) & mask];
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                acc ^= v[j];
+        }
+    }
+    uint32_t x = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
+    __shared__ uint32_t red[256];
+    red[threadIdx.x] = x;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        for (int j = 1; j < 256; ++j)
+            x ^= red[j];
+        sink[blockIdx.x] = x;
+    }
+}
+
+hipError_t launch_l2_read(const void* src, int64_t bytes, int iters, uint32_t* sink, int grid, hipStream_t s)
+{
+    k_l2_read<<<(unsigned)grid, 256, 0, s>>>(reinterpret_cast<const u32x4*>(src), (int)(bytes / 16), iters, sink);
+    return hipGetLastError();
+}
+
 // Each workgroup's first wave runs `iters` rounds of a dependent chain of 64
 // fp32 multiply-adds and records the shader-clock cycles (s_memtime) and the
 // constant-rate wall-clock ticks (s_memrealtime) it took.

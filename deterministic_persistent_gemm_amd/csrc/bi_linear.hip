@@ -226,20 +226,9 @@ __global__ __launch_bounds__(64) void k_decode(LinearArgs a, int kbpt, int tiles
         load_chunk(wf0, xf0, 0);
         run_chunk(wf0, xf0);
     } else {
-        load_chunk(wf0, xf0, 0);
-        for (int c = 0; c < kbpt; c += 2 * CH) {
-            if (c + CH < kbpt)
-                load_chunk(wf1, xf1, c + CH);
-            // every load issued so far is in flight before the chain waits on one
-            __builtin_amdgcn_sched_barrier(0);
-            run_chunk(wf0, xf0);
-            if (c + CH >= kbpt)
-                break;
-            if (c + 2 * CH < kbpt)
-                load_chunk(wf0, xf0, c + 2 * CH);
-            __builtin_amdgcn_sched_barrier(0);
-            run_chunk(wf1, xf1);
-        }
+        chunk_pipeline<CH>(
+            kbpt, [&](int c) { load_chunk(wf0, xf0, c); }, [&](int c) { load_chunk(wf1, xf1, c); },
+            [&](int) { run_chunk(wf0, xf0); }, [&](int) { run_chunk(wf1, xf1); });
     }
 
     const int col = nt * 16 + acc_col(lane);
@@ -346,21 +335,10 @@ __global__ __launch_bounds__(NW * 64) void k_decode_wg(LinearArgs a, int kbpt, i
         if ((c + CH) % kbpt == 0)
             lds_part[(w + (c / kbpt) * NW) * 64 + lane] = P[0][0];
     };
-    if (nblk > 0) {
-        load_chunk(wf0, xf0, 0);
-        for (int c = 0; c < nblk; c += 2 * CH) {
-            if (c + CH < nblk)
-                load_chunk(wf1, xf1, c + CH);
-            __builtin_amdgcn_sched_barrier(0);
-            run_chunk(wf0, xf0, c);
-            if (c + CH >= nblk)
-                break;
-            if (c + 2 * CH < nblk)
-                load_chunk(wf0, xf0, c + 2 * CH);
-            __builtin_amdgcn_sched_barrier(0);
-            run_chunk(wf1, xf1, c + CH);
-        }
-    }
+    if (nblk > 0)
+        chunk_pipeline<CH>(
+            nblk, [&](int c) { load_chunk(wf0, xf0, c); }, [&](int c) { load_chunk(wf1, xf1, c); },
+            [&](int c) { run_chunk(wf0, xf0, c); }, [&](int c) { run_chunk(wf1, xf1, c); });
     __syncthreads();
     if (w != 0)
         return;

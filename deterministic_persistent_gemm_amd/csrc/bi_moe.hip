@@ -576,19 +576,9 @@ __global__ __launch_bounds__(TW * NW * 64) void k_grouped(GroupedArgs g)
             for (int i = 0; i < CH; ++i)
                 mfma_tiles<MT, NBT>(af[i], bf[i], P);
         };
-        load_chunk(af0, bf0, 0);
-        for (int c = 0; c < g.kbpt; c += 2 * CH) {
-            if (c + CH < g.kbpt)
-                load_chunk(af1, bf1, c + CH);
-            __builtin_amdgcn_sched_barrier(0);
-            run_chunk(af0, bf0);
-            if (c + CH >= g.kbpt)
-                break;
-            if (c + 2 * CH < g.kbpt)
-                load_chunk(af0, bf0, c + 2 * CH);
-            __builtin_amdgcn_sched_barrier(0);
-            run_chunk(af1, bf1);
-        }
+        chunk_pipeline<CH>(
+            g.kbpt, [&](int c) { load_chunk(af0, bf0, c); }, [&](int c) { load_chunk(af1, bf1, c); },
+            [&](int) { run_chunk(af0, bf0); }, [&](int) { run_chunk(af1, bf1); });
         if (TW == 1) {
 #pragma unroll
             for (int m = 0; m < MT; ++m)

@@ -348,6 +348,14 @@ bi_status_t bi_lab_moe_layout(int64_t M, int64_t H, int64_t E, int64_t I, int64_
  *                      threads and writes one word per workgroup to sink
  *                      (device, `grid` uint32): the cold-read rate the
  *                      chip achieves, the practical HBM reference.
+ *  bi_lab_l2_read      each of `grid` workgroups of 256 threads reads the
+ *                      same `bytes` at `src` (device, 16-byte aligned; a
+ *                      power of two from 32 KiB to 2 MiB, so that it stays
+ *                      in every XCD's L2 after the first pass) `iters` times
+ *                      and writes one word per workgroup to sink (device,
+ *                      `grid` uint32): the rate at which the L2 delivers
+ *                      data to the compute units (grid x iters x bytes per
+ *                      call).
  *  bi_lab_clock        each of `grid` 64-thread workgroups runs iters x 64
  *                      dependent fp32 multiply-adds and writes three uint64
  *                      to out[3 wg ..]: shader-clock cycles (s_memtime),
@@ -370,6 +378,8 @@ bi_status_t bi_lab_moe_layout(int64_t M, int64_t H, int64_t E, int64_t I, int64_
 bi_status_t bi_lab_empty(int32_t grid, int32_t threads, hipStream_t stream);
 bi_status_t bi_lab_stream_read(const void* src, int64_t bytes, uint32_t* sink, int32_t grid,
                                hipStream_t stream);
+bi_status_t bi_lab_l2_read(const void* src, int64_t bytes, int32_t iters, uint32_t* sink, int32_t grid,
+                           hipStream_t stream);
 bi_status_t bi_lab_clock(uint64_t* out, int32_t grid, int32_t iters, hipStream_t stream);
 bi_status_t bi_lab_lds_read(uint64_t* out, int32_t grid, int32_t iters, hipStream_t stream);
 bi_status_t bi_lab_mfma_rate(uint64_t* out, int32_t dtype, int32_t grid, int32_t iters, hipStream_t stream);

@@ -211,3 +211,16 @@ def test_noalloc_entry_rejects_on_the_host():
     assert f(None, 4096, FAKE, 4096, None, FAKE, 256, 1, 256, 4096, None) == bi.BI_EINVAL
     assert f(FAKE, 4095, FAKE, 4096, None, FAKE, 256, 1, 256, 4096, None) == bi.BI_EINVAL
     assert f(FAKE, 4096, FAKE, 4096, None, FAKE, 256, 0, 256, 4096, None) == bi.BI_OK
+
+
+def test_l2_read_probe_rejects_on_the_host():
+    # the region must be a power of two from 32 KiB to 2 MiB (one full round
+    # of the probe's loads, small enough to stay in one XCD's L2)
+    f = L.bi_lab_l2_read
+    assert f(FAKE, 3 << 20, 1, FAKE, 256, None) == bi.BI_EINVAL
+    assert f(FAKE, 4 << 20, 1, FAKE, 256, None) == bi.BI_EINVAL
+    assert f(FAKE, 16 << 10, 1, FAKE, 256, None) == bi.BI_EINVAL
+    assert f(FAKE, 1 << 20, 0, FAKE, 256, None) == bi.BI_EINVAL
+    assert f(FAKE, 1 << 20, 1, FAKE, 0, None) == bi.BI_EINVAL
+    assert f(None, 1 << 20, 1, FAKE, 256, None) == bi.BI_EINVAL
+    assert f(FAKE, 1 << 20, 1, None, 256, None) == bi.BI_EINVAL
