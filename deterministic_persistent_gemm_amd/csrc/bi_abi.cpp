@@ -62,7 +62,8 @@ bi_status_t run_linear(int xkind, const void* x, int64_t ldx, const void* w, int
 namespace bi {
 
 bi_status_t linear_f32_checked(const float* x, int64_t ldx, const float* w, int64_t ldw, const float* bias,
-                               float* y, int64_t ldy, int64_t M, int64_t N, int64_t K, size_t* ws_needed)
+                               float* y, int64_t ldy, int64_t M, int64_t N, int64_t K, size_t* ws_needed,
+                               bool no_split)
 {
     bi_status_t st = check_linear(x, ldx, w, ldw, bias, y, ldy, M, N, K, 4, 4, 4);
     if (st != BI_OK || M == 0) {
@@ -73,7 +74,7 @@ bi_status_t linear_f32_checked(const float* x, int64_t ldx, const float* w, int6
     if ((st = recipe_for(BI_F32, N, K, &r)) != BI_OK)
         return st;
     Plan p;
-    if ((st = make_plan(r, BI_PATH_AUTO, M, N, K, &p)) != BI_OK)
+    if ((st = make_plan(r, BI_PATH_AUTO | (no_split ? kPathNoSplit : 0), M, N, K, &p)) != BI_OK)
         return st;
     *ws_needed = p.ws_bytes;
     return BI_OK;
@@ -81,7 +82,7 @@ bi_status_t linear_f32_checked(const float* x, int64_t ldx, const float* w, int6
 
 bi_status_t linear_f32_run(const float* x, int64_t ldx, const float* w, int64_t ldw, const float* bias, float* y,
                            int64_t ldy, int64_t M, int64_t N, int64_t K, void* ws, size_t ws_bytes,
-                           hipStream_t stream)
+                           hipStream_t stream, bool no_split)
 {
     bi_status_t st = check_linear(x, ldx, w, ldw, bias, y, ldy, M, N, K, 4, 4, 4);
     if (st != BI_OK || M == 0)
@@ -89,7 +90,8 @@ bi_status_t linear_f32_run(const float* x, int64_t ldx, const float* w, int64_t 
     bi_recipe_t r;
     if ((st = recipe_for(BI_F32, N, K, &r)) != BI_OK)
         return st;
-    return run_linear(kXF32, x, ldx, w, ldw, bias, y, 0, ldy, M, N, K, r, BI_PATH_AUTO, ws, ws_bytes, stream);
+    return run_linear(kXF32, x, ldx, w, ldw, bias, y, 0, ldy, M, N, K, r,
+                      BI_PATH_AUTO | (no_split ? kPathNoSplit : 0), ws, ws_bytes, stream);
 }
 
 }  // namespace bi

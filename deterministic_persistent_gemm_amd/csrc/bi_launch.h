@@ -33,11 +33,13 @@ hipError_t launch_linear(int xkind, const LinearArgs& a, const Plan& p, void* ws
 
 // bi_linear_f32 in two steps (bi_abi.cpp): the validation and the workspace
 // bytes the automatic plan needs (nothing enqueued), and the call itself.
+// no_split: the ring-fed fp32 tiles run unsplit (no workspace, same bits).
 bi_status_t linear_f32_checked(const float* x, int64_t ldx, const float* w, int64_t ldw, const float* bias,
-                               float* y, int64_t ldy, int64_t M, int64_t N, int64_t K, size_t* ws_needed);
+                               float* y, int64_t ldy, int64_t M, int64_t N, int64_t K, size_t* ws_needed,
+                               bool no_split = false);
 bi_status_t linear_f32_run(const float* x, int64_t ldx, const float* w, int64_t ldw, const float* bias, float* y,
                            int64_t ldy, int64_t M, int64_t N, int64_t K, void* ws, size_t ws_bytes,
-                           hipStream_t stream);
+                           hipStream_t stream, bool no_split = false);
 
 // Diagnostic kernels (bi_lab.hip).
 hipError_t launch_xcc_ids(uint32_t* out, int gx, int gy, hipStream_t s);

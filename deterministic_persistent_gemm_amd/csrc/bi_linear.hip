@@ -1505,9 +1505,26 @@ static hipError_t launch_persistent_t(const LinearArgs& a, const Plan& p, hipStr
 // for the fragment reads; 128-byte rows of 32-k stages are not, with either
 // key tried).  A direct-to-LDS load covers 4 rows (1 KiB); lane i lands at
 // row i / 16, position i % 16, and so fetches chunk (i % 16) ^ (row & 15).
-template <int BM, int PAR, int R>
+//
+// SPLIT: the k tiles of one output tile are split evenly over ksplit
+// workgroups (workgroup b takes tile b % tiles, part b / tiles), so that a
+// grid of tiles x ksplit workgroups fills the chip when the tiles alone
+// would not.  Part 0 folds its k tiles as above into a prefix (acc after
+// its last k tile); a later part cannot add its partials to anything yet,
+// so every one of its waves stores each k tile's partial as soon as the
+// tile is done.  The tile count is a multiple of 8, so every part of a tile
+// runs on the same XCD (workgroups go to the XCDs round-robin) and meets the
+// others in that L2: a workgroup's stores are complete there before it
+// counts itself in at the tile's counter, and the part that arrives last
+// drops its L1 and finishes the fold in ascending k tile order -- the
+// prefix, then each later partial -- then adds the bias: the same
+// operations as one workgroup doing the whole k range, and no workgroup
+// ever waits for another.  The counter wraps to zero at the last arrival.
+template <int BM, int PAR, int R, bool SPLIT = false>
 __global__ __launch_bounds__(512) void k_ring_f32(LinearArgs a, int kbpt, int tiles_k, int tiles_m, int tiles_n,
-                                                  int xbm, int xbn)
+                                                  int xbm, int xbn, int ksplit = 1,
+                                                  f32x4* __restrict__ partials = nullptr,
+                                                  uint32_t* __restrict__ counters = nullptr)
 {
     constexpr int kRow = 256;                               // 64 k of fp32
     constexpr int kUnit = (BM + 32) * kRow;
@@ -1523,9 +1540,14 @@ __global__ __launch_bounds__(512) void k_ring_f32(LinearArgs a, int kbpt, int ti
     const int sm = sub >> 1, sn = sub & 1;
     const int r = lane & 15, g = lane >> 4;
     const int spt = kbpt / 2;                               // stages per k tile
-    const int nsteps = (tiles_k / PAR) * spt;
-    const int nst = a.K / 64;                               // stages of the whole K
+    const int kts = tiles_k / ksplit;                       // k tiles of this workgroup
+    const int nsteps = (kts / PAR) * spt;
     const int tiles = tiles_m * tiles_n;
+    const int part = SPLIT ? (int)blockIdx.x / tiles : 0;
+    const int kt0 = part * kts;                             // its first k tile
+    const int st_end = (kt0 + kts) * spt;                   // one past its last stage
+    // a later part stores its partials instead of folding them
+    const bool stores = SPLIT && part > 0;
     const float* xg = reinterpret_cast<const float*>(a.x);
     const float* wg = reinterpret_cast<const float*>(a.w);
     const uint32_t lds0 = lds_addr(ring);
@@ -1537,7 +1559,7 @@ __global__ __launch_bounds__(512) void k_ring_f32(LinearArgs a, int kbpt, int ti
     // the choice of X or W (whole 4-row groups) stay a scalar base
     const int wu = __builtin_amdgcn_readfirstlane(w);
 
-    for (int it = blockIdx.x; it < tiles; it += gridDim.x) {
+    for (int it = SPLIT ? (int)blockIdx.x % tiles : (int)blockIdx.x; it < tiles; it += SPLIT ? tiles : gridDim.x) {
         const int tile = xcd_tile(it, tiles_n, xbm, xbn);
         const int m0 = (tile / tiles_n) * BM, n0 = (tile % tiles_n) * 32;
         // wave w loads the 4-row groups w LPU .. w LPU + LPU - 1 of each unit
@@ -1559,7 +1581,7 @@ __global__ __launch_bounds__(512) void k_ring_f32(LinearArgs a, int kbpt, int ti
         // slot u % R
         auto issue_unit = [&](int u) {
             const int j = u / PAR, h = u % PAR;
-            const int st = min((PAR * (j / spt) + h) * spt + j % spt, nst - 1);
+            const int st = min((kt0 + PAR * (j / spt) + h) * spt + j % spt, st_end - 1);
             const uint32_t slot = lds0 + (uint32_t)(u % R) * kUnit + wu * LPU * 1024;
 #pragma unroll
             for (int t = 0; t < LPU; ++t)
@@ -1580,6 +1602,13 @@ __global__ __launch_bounds__(512) void k_ring_f32(LinearArgs a, int kbpt, int ti
                     B[c][b].hi = *reinterpret_cast<const f32x4*>(fw + slot * kUnit + (((c0 + 1) ^ r) << 4));
                 }
             }
+        };
+        // workspace slot q of this tile (slot 0: part 0's prefix; slot
+        // kt - kts + 1: the partial of k tile kt of a later part), this
+        // wave's 16x16 sub-tile
+        const int nslots = tiles_k - kts + 1;
+        auto slot_ptr = [&](int q) {
+            return partials + ((int64_t)(it * nslots + q) * S + sub) * 64 + lane;
         };
         // the group's partials in ascending k tile order, after the barrier
         // that follows the hand-over
@@ -1617,7 +1646,7 @@ __global__ __launch_bounds__(512) void k_ring_f32(LinearArgs a, int kbpt, int ti
             wait_vm<(R - 2 * PAR) * LPU>();
             wait_lgkm0();
             bar();
-            if (j > 0 && j % spt == 0 && grp == 0)
+            if (j > 0 && j % spt == 0 && grp == 0 && !stores)
                 fold(j == spt);
 #pragma unroll
             for (int h = 0; h < PAR; ++h)
@@ -1651,7 +1680,14 @@ __global__ __launch_bounds__(512) void k_ring_f32(LinearArgs a, int kbpt, int ti
                 BI_RING_STEP(7)
 #undef BI_RING_STEP
             }
-            if (G > 1 && j % spt == spt - 1 && grp > 0) {
+            if (stores) {
+                // k tile kt0 + PAR (j / spt) + C grp + c is complete
+                if (j % spt == spt - 1) {
+#pragma unroll
+                    for (int c = 0; c < C; ++c)
+                        *slot_ptr(kt0 - kts + PAR * (j / spt) + grp * C + c + 1) = P[c];
+                }
+            } else if (G > 1 && j % spt == spt - 1 && grp > 0) {
 #pragma unroll
                 for (int c = 0; c < C; ++c)
                     hand[((grp - 1) * S + sub) * C + c][lane] = P[c];
@@ -1665,9 +1701,45 @@ __global__ __launch_bounds__(512) void k_ring_f32(LinearArgs a, int kbpt, int ti
         wait_vm<0>();
         wait_lgkm0();
         bar();
-        if (grp == 0) {
+        if (grp == 0 && !stores)
             fold(nsteps == spt);
-            store_acc(a, m0 + sm * 16 + acc_row(lane, 0), n0 + sn * 16 + acc_col(lane), acc);
+        const int row = m0 + sm * 16 + acc_row(lane, 0), col = n0 + sn * 16 + acc_col(lane);
+        if constexpr (!SPLIT) {
+            if (grp == 0)
+                store_acc(a, row, col, acc);
+        } else {
+            if (part == 0 && grp == 0)
+                *slot_ptr(0) = acc;
+            // this workgroup's stores are complete in the XCD's L2 before
+            // it counts itself in
+            wait_vm<0>();
+            __shared__ uint32_t last;
+            __syncthreads();
+            if (threadIdx.x == 0)
+                last = __builtin_amdgcn_atomic_inc32(counters + it * kCounterStride, (uint32_t)(ksplit - 1),
+                                                     __ATOMIC_RELAXED, "workgroup") == (uint32_t)(ksplit - 1);
+            __syncthreads();
+            if (!last)
+                return;
+            // last arrival: drop stale L1 lines, then the prefix and every
+            // later partial in ascending k tile order, up to 32 per round trip
+            asm volatile("buffer_inv sc0" ::: "memory");
+            if (grp == 0) {
+                f32x4 r = part == 0 ? acc : *slot_ptr(0);
+                constexpr int kB = 16;
+                for (int q0 = 1; q0 < nslots; q0 += kB) {
+                    f32x4 v[kB];
+#pragma unroll
+                    for (int i = 0; i < kB; ++i)
+                        if (q0 + i < nslots)
+                            v[i] = *slot_ptr(q0 + i);
+#pragma unroll
+                    for (int i = 0; i < kB; ++i)
+                        if (q0 + i < nslots)
+                            r = r + v[i];
+                }
+                store_acc(a, row, col, r);
+            }
         }
     }
 }
@@ -1699,11 +1771,81 @@ static hipError_t launch_ring_f32(const LinearArgs& a, const Plan& p, hipStream_
     return hipGetLastError();
 }
 
+// The k split of the ring-fed tiles (tile codes 28: 32x32, 29: 64x32): the
+// largest power of two S >= 2 for which tiles x S workgroups fit one per
+// compute unit and every part holds a whole number of k tile groups, with
+// the tile count a multiple of 8 (every part of a tile on one XCD) and at
+// most one counter per tile; 0 where no split serves (the launcher then runs
+// the unsplit ring tile of the same shape).
+static bool ring_split_ok(const LinearArgs& a, const Plan& p, int bm, int par, int ks)
+{
+    if (p.tiles_k % ks != 0)
+        return false;
+    Plan q = p;
+    q.tiles_k = p.tiles_k / ks;
+    return ring_f32_ok(a, q, bm, par);
+}
+
+RingSplit ring_split_plan(const Plan& p, int64_t M, int64_t N, int64_t K, int code)
+{
+    RingSplit r{};
+    if (code != 28 && code != 29)
+        return r;
+    const int bm = code == 28 ? 32 : 64;
+    const int64_t tiles = ((M + bm - 1) / bm) * ((N + 31) / 32);
+    if (tiles % 8 != 0 || tiles > kDecodeMaxCounters)
+        return r;
+    LinearArgs a{};
+    a.M = (int)M;
+    a.N = (int)N;
+    a.K = (int)K;
+    a.ldx = a.K;
+    a.ldw = a.K;
+    const int cus = device_cu_count();
+    for (int ks = 2; tiles * ks <= cus && ks <= p.tiles_k; ks *= 2) {
+        for (int par : {4, 2}) {
+            if (bm == 64 && par == 4)
+                continue;
+            if (ring_split_ok(a, p, bm, par, ks)) {
+                r.ksplit = ks;
+                r.par = par;
+                r.bm = bm;
+                r.tiles = (int)tiles;
+                break;
+            }
+        }
+    }
+    if (r.ksplit) {
+        const int64_t nslots = p.tiles_k - p.tiles_k / r.ksplit + 1;
+        r.ws_bytes = kDecodeCounterBytes + (size_t)tiles * (size_t)nslots * (size_t)(bm / 8) * 64 * 16;
+    }
+    return r;
+}
+
+template <int BM, int PAR, int R>
+static hipError_t launch_ring_f32_split(const LinearArgs& a, const Plan& p, void* ws, hipStream_t s)
+{
+    const int ks = p.ksplit;
+    if (!ws || ks < 2 || !ring_split_ok(a, p, BM, PAR, ks))
+        return hipErrorInvalidValue;
+    const int tiles_m = (a.M + BM - 1) / BM;
+    const int tiles_n = (a.N + 31) / 32;
+    const int tiles = tiles_m * tiles_n;
+    if (tiles % 8 != 0 || tiles > kDecodeMaxCounters)
+        return hipErrorInvalidValue;
+    const XcdBlock xb = xcd_block(tiles_m, tiles_n, BM, 32, tiles);
+    uint32_t* counters = reinterpret_cast<uint32_t*>(ws);
+    f32x4* partials = reinterpret_cast<f32x4*>(reinterpret_cast<char*>(ws) + kDecodeCounterBytes);
+    k_ring_f32<BM, PAR, R, true><<<tiles * ks, 512, 0, s>>>(a, p.kbpt, p.tiles_k, tiles_m, tiles_n, xb.xbm, xb.xbn,
+                                                            ks, partials, counters);
+    return hipGetLastError();
+}
+
 // Persistent tile shapes (BM x BN, waves WM x WN, k blocks per LDS stage).
 // Code 0 picks automatically: the largest tile that still gives every compute
 // unit a tile.  Tiling never changes the numerics, only the speed.
 template <typename OX, typename OW>
-static hipError_t launch_persistent(const LinearArgs& a, const Plan& p, hipStream_t s)
+static hipError_t launch_persistent(const LinearArgs& a, const Plan& p, void* ws, hipStream_t s)
 {
     const int cus = device_cu_count();
     auto tiles = [&](int bm, int bn) { return ((a.M + bm - 1) / bm) * ((a.N + bn - 1) / bn); };
@@ -1732,6 +1874,18 @@ static hipError_t launch_persistent(const LinearArgs& a, const Plan& p, hipStrea
         if constexpr (rings) {
             // the ring-fed 32x32 tile works on four k tiles at once where
             // their number allows, else on two; the 64x32 tile on two
+            // the k-split forms; the planner set p.ksplit (0: the tiles fill
+            // the chip or no split serves, and the unsplit tile runs)
+            if (code == 28 && p.ksplit >= 2 && ring_split_ok(a, p, 32, 4, p.ksplit))
+                return launch_ring_f32_split<32, 4, 8>(a, p, ws, s);
+            if (code == 28 && p.ksplit >= 2 && ring_split_ok(a, p, 32, 2, p.ksplit))
+                return launch_ring_f32_split<32, 2, 8>(a, p, ws, s);
+            if (code == 29 && p.ksplit >= 2 && ring_split_ok(a, p, 64, 2, p.ksplit))
+                return launch_ring_f32_split<64, 2, 6>(a, p, ws, s);
+            if (code == 28)
+                code = 23;
+            if (code == 29)
+                code = 24;
             if (code == 23 && ring_f32_ok(a, p, 32, 4))
                 return launch_ring_f32<32, 4, 8>(a, p, s);
             if (code == 23 && ring_f32_ok(a, p, 32, 2))
@@ -1739,7 +1893,7 @@ static hipError_t launch_persistent(const LinearArgs& a, const Plan& p, hipStrea
             if (code == 24 && ring_f32_ok(a, p, 64, 2))
                 return launch_ring_f32<64, 2, 6>(a, p, s);
         }
-        if (code == 23 || code == 24)
+        if (code == 23 || code == 24 || code == 28 || code == 29)
             code = 3;
         if (!stage_fits(code))
             code = 7;
@@ -1806,7 +1960,7 @@ static hipError_t launch_typed(const LinearArgs& a, const Plan& p, void* ws, hip
     }
     if (p.path == kPathDecode || p.path == kPathDecodeWg || p.path == kPathDecodeXcd)
         return launch_decode<OX, OW>(a, p, ws, s, fold);
-    return launch_persistent<OX, OW>(a, p, s);
+    return launch_persistent<OX, OW>(a, p, ws, s);
 }
 
 hipError_t launch_linear(int xkind, const LinearArgs& a, const Plan& p, void* ws, hipStream_t s, bool fold)

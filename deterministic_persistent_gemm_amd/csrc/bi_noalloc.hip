@@ -74,6 +74,17 @@ extern "C" bi_status_t bi_linear_f32_noalloc(const float* x, int64_t ldx, const 
     bi_status_t st = linear_f32_checked(x, ldx, w, ldw, bias, y, ldy, M, N, K, &need);
     if (st != BI_OK || M == 0)
         return st;
+    // a k-split plan whose partials do not fit runs its tiles unsplit (the
+    // same bits, no workspace)
+    bool no_split = false;
+    if (need > kNoallocScratchBytes) {
+        size_t need_unsplit = 0;
+        if (linear_f32_checked(x, ldx, w, ldw, bias, y, ldy, M, N, K, &need_unsplit, true) == BI_OK &&
+            need_unsplit <= kNoallocScratchBytes) {
+            need = need_unsplit;
+            no_split = true;
+        }
+    }
     if (need > kNoallocScratchBytes)
         return BI_EWORKSPACE;
     void* ws = nullptr;
@@ -86,5 +97,5 @@ extern "C" bi_status_t bi_linear_f32_noalloc(const float* x, int64_t ldx, const 
             return BI_EHIP;
         ws = g_scratch[dev];
     }
-    return linear_f32_run(x, ldx, w, ldw, bias, y, ldy, M, N, K, ws, need, stream);
+    return linear_f32_run(x, ldx, w, ldw, bias, y, ldy, M, N, K, ws, need, stream, no_split);
 }

@@ -143,7 +143,7 @@ bool decode_xcd_ok(const Plan& p)
 bool tile_code_valid(int dtype, int code)
 {
     if (dtype == BI_F32)
-        return (code >= 1 && code <= 10) || code == 23 || code == 24;
+        return (code >= 1 && code <= 10) || code == 23 || code == 24 || code == 28 || code == 29;
     return code >= 11 && code <= 22;
 }
 
@@ -170,6 +170,7 @@ bi_status_t make_plan(const bi_recipe_t& r, int32_t path_req, int64_t M, int64_t
     p.tiling = persistent_tiling(r);
     // bits 8..15: a persistent tile shape, or the M tiles per wave of the
     // k-tile-parallel decode paths (experiments only; never the numerics)
+    const bool no_split = (path_req & kPathNoSplit) != 0;
     const int tile_code = (path_req >> 8) & 0xff;
     path_req &= 0xff;
     if (tile_code != 0) {
@@ -238,6 +239,16 @@ bi_status_t make_plan(const bi_recipe_t& r, int32_t path_req, int64_t M, int64_t
     p.ws_bytes = 0;
     if ((p.path == kPathDecode || p.path == kPathDecodeXcd) && p.tiles_k > 1)
         p.ws_bytes = kDecodeCounterBytes + (size_t)p.mtiles * (size_t)p.ntiles * (size_t)p.tiles_k * 64 * 16;
+    // the k-split ring tiles (fp32 operands): the parts' partials
+    if (p.path == kPathPersistent && r.dtype == BI_F32 && (p.tile_code == 28 || p.tile_code == 29)) {
+        if (no_split) {
+            p.tile_code = p.tile_code == 28 ? 23 : 24;
+        } else {
+            const RingSplit rs = ring_split_plan(p, M, N, K, p.tile_code);
+            p.ksplit = rs.ksplit;
+            p.ws_bytes = rs.ws_bytes;
+        }
+    }
     *plan = p;
     return BI_OK;
 }

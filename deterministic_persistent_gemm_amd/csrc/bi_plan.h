@@ -63,7 +63,8 @@ struct Plan {
     Tiling tiling;   // persistent path
     int tile_code;   // persistent tile shape, 0 = automatic (table entry or heuristic)
     int m_per_wave;  // decode paths: 16-row M tiles one wave carries (1, 2, 4), 0 = automatic
-    size_t ws_bytes; // workspace the plan needs (decode tile partials)
+    int ksplit;      // persistent tile codes 28, 29: workgroups per output tile (0: unsplit)
+    size_t ws_bytes; // workspace the plan needs (decode or k-split tile partials)
 };
 
 // The recipe of a key -- a pure function of (dtype, N, K).
@@ -71,6 +72,11 @@ bi_status_t recipe_for(int32_t dtype, int64_t N, int64_t K, bi_recipe_t* out);
 
 // Checks a recipe is one the kernels can carry out for this (N, K).
 bi_status_t recipe_valid(const bi_recipe_t& r, int64_t N, int64_t K);
+
+// Internal request bit of make_plan: serve the ring-fed fp32 tiles unsplit
+// (tile codes 28, 29 run as 23, 24 and need no workspace); same bits, for a
+// caller whose workspace is capped.
+constexpr int32_t kPathNoSplit = 1 << 16;
 
 // Picks the kernel path and its shape for M rows.  path_req: BI_PATH_*.
 bi_status_t make_plan(const bi_recipe_t& r, int32_t path_req, int64_t M, int64_t N, int64_t K,
@@ -93,6 +99,15 @@ int xcd_m_per_wave(const Plan& p);
 // multiple of 8 (so every wave of an output tile runs on one XCD), and no
 // more output-tile groups than there are counters.
 bool decode_xcd_ok(const Plan& p);
+
+// The k split of the ring-fed fp32 tiles (tile codes 28, 29; bi_linear.hip):
+// workgroups per output tile (0: no split serves this plan), the k tiles
+// worked on at once, the tile rows, the tile count and the workspace.
+struct RingSplit {
+    int ksplit, par, bm, tiles;
+    size_t ws_bytes;
+};
+RingSplit ring_split_plan(const Plan& p, int64_t M, int64_t N, int64_t K, int code);
 
 // Number of compute units of the current device (cached per device).
 int device_cu_count();

@@ -65,7 +65,7 @@ DECODE_MARGIN = 0.05        # the persistent kernel takes over once it is this m
 TABLE_HEADER = ("// Measured key table, written by deterministic_persistent_gemm_amd/sweep.py.\n"
                 "// {dtype, N, K, block_k, m_decode_max, decode_path, m_a, tile_a, m_b, tile_b, tile_c, "
                 "m_xcd_max}\n")
-F32_CODES = tuple(range(1, 11)) + (23, 24)
+F32_CODES = tuple(range(1, 11)) + (23, 24, 28, 29)
 BF16_CODES = tuple(range(11, 23))
 PATH_DECODE, PATH_PERSISTENT, PATH_DECODE_WG, PATH_DECODE_DMA, PATH_DECODE_XCD = 1, 2, 3, 4, 5
 
@@ -84,19 +84,20 @@ def parse_key(s: str, profile: str = "decode"):
 def stage_k(code: int) -> int:
     """k per LDS stage of a persistent tile shape (shapes whose stage does
     not divide K are served by the 32-k-stage shape of the dtype)."""
-    return 32 if code in (7, 8, 17) else 128 if code in (9, 10, 13, 16) else 64   # 20-24: 64
+    return 32 if code in (7, 8, 17) else 128 if code in (9, 10, 13, 16) else 64   # 20-24, 28, 29: 64
 
 
 def tile_codes(dt: str, K: int, block_k: int):
     """The distinct tile shapes a recipe can run: shapes whose stage does not
     divide K, the 256x256 shapes (single k tile only: 18, 19 and the
     ring-fed 21, 22) of a recipe with several k tiles, and the ring-fed fp32
-    shapes (23, 24: an even number of k tiles of 64-k multiples) of a recipe
-    without, would fall back to another shape and are left out."""
+    shapes (23, 24 and their k-split forms 28, 29: an even number of k tiles
+    of 64-k multiples) of a recipe without, would fall back to another shape
+    and are left out."""
     codes = F32_CODES if dt == "f32" else BF16_CODES
     rings_f32 = (K // block_k) % 2 == 0 and block_k % 64 == 0
     return tuple(c for c in codes if K % stage_k(c) == 0 and not (c in (18, 19, 21, 22) and block_k != K)
-                 and not (c in (23, 24) and not rings_f32))
+                 and not (c in (23, 24, 28, 29) and not rings_f32))
 
 
 def block_k_candidates(dt: str, K: int):

@@ -267,7 +267,10 @@ const char* bi_status_str(bi_status_t status);
  * tiles at a time (two where four do not divide the number of k tiles),
  * 24 = 64x32 likewise, two k tiles at a time; 23 and 24 need K a multiple
  * of 64 and k tiles of an even number of 32-k blocks (23 with several k
- * tiles: at least four blocks);
+ * tiles: at least four blocks); 28 and 29 = 23 and 24 with the k tiles of
+ * each output tile split over 2 to 16 workgroups on one XCD whose last
+ * arrival folds the partials in k tile order (workspace; a number of tiles
+ * that is a multiple of 8 and at most 128, else they run as 23 and 24);
  * bf16: 11 = 128x128, 12 = 64x64, 13 = 128x128 with 128-k stages,
  * 14 = 256x128, 15 = 128x256, 16 = 64x128 with 128-k stages, 17 = 64x64
  * with 32-k stages, 18 = 256x256 on 2x4 waves, 19 = 256x256 on 4x2 waves,

@@ -133,7 +133,7 @@ def test_every_persistent_tile_shape_gives_the_same_bits(bi, router):
     batch = wl.router_batch(300, w)
     x = dev(batch.x)
     ref = host(bi.bi_linear_f32(x, weight_t(wd), bd))
-    for code in (*range(1, 11), 23, 24):
+    for code in (*range(1, 11), 23, 24, 28, 29):
         banner(f"router fp32 M=300 persistent tile code {code}")
         y = host(bi.bi_lab_linear(x, weight_t(wd), bd, path=bi.BI_PATH_PERSISTENT | (code << 8)))
         assert_bitwise(y, ref, f"tile code {code}")
@@ -144,7 +144,7 @@ def test_every_persistent_tile_shape_gives_the_same_bits(bi, router):
     x2 = dev(g.standard_normal((70, 320)).astype(np.float32))
     ref2 = host(bi.bi_linear_f32(x2, weight_t(dev(w2)), None))
     assert_close(ref2, oracle.linear_f32(host(x2), w2, None), F32_ATOL, F32_RTOL, "N=48 K=320")
-    for code in (*range(1, 11), 23, 24):
+    for code in (*range(1, 11), 23, 24, 28, 29):
         y = host(bi.bi_lab_linear(x2, weight_t(dev(w2)), None, path=bi.BI_PATH_PERSISTENT | (code << 8)))
         assert_bitwise(y, ref2, f"N=48 tile code {code}")
 
@@ -172,7 +172,7 @@ def test_ring_fed_fp32_tiles(bi, M, N, K, block_k):
     y3 = host(bi.bi_lab_linear(x, weight_t(wd), bd, recipe=r, path=bi.BI_PATH_PERSISTENT | (3 << 8)))
     if M * K <= 300 * 768:
         assert_close(y3, oracle.linear_f32(xh, w, b), F32_ATOL, F32_RTOL, "oracle")
-    for code in (23, 24):
+    for code in (23, 24, 28, 29):
         y = host(bi.bi_lab_linear(x, weight_t(wd), bd, recipe=r, path=bi.BI_PATH_PERSISTENT | (code << 8)))
         assert_bitwise(y, y3, f"tile code {code} vs 3")
 

@@ -43,7 +43,7 @@ def test_profiles_pick_the_trade_off():
 
 
 def test_tile_codes_skip_shapes_that_fall_back():
-    assert sweep.tile_codes("f32", 4096, 128) == tuple(range(1, 11)) + (23, 24)
+    assert sweep.tile_codes("f32", 4096, 128) == tuple(range(1, 11)) + (23, 24, 28, 29)
     # 128-k stages (9, 10) do not divide 320; the rings (23, 24) need several k tiles
     assert sweep.tile_codes("f32", 320, 320) == (1, 2, 3, 4, 5, 6, 7, 8)
     assert 18 not in sweep.tile_codes("bf16", 4096, 512)        # 256x256 needs one k tile
@@ -97,7 +97,7 @@ def test_compiled_table_is_what_the_library_serves():
         assert rec.block_k == r["block_k"], r
         assert rec.m_decode_max == r["m_decode_max"], r
         assert r["K"] % r["block_k"] == 0 and r["block_k"] % 32 == 0
-        codes = (*range(1, 11), 23, 24) if dt == bi.BI_F32 else range(11, 23)
+        codes = (*range(1, 11), 23, 24, 28, 29) if dt == bi.BI_F32 else range(11, 23)
         for t in (r["tile_a"], r["tile_b"], r["tile_c"]):
             assert t == 0 or t in codes, r
         assert r["decode_path"] in (0, 1, 3, 4)
