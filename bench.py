@@ -232,9 +232,11 @@ def main():
 
 
 def prefill_leg(torch, np, bi, wl, w, copies, bias, dev):
+    """The router at the prefill sizes (M = 1024, 4096) and, between decode
+    and prefill, at M = 256 and 512 (the k-split ring tiles)."""
     res = {}
     stream = torch.cuda.Stream(dev)
-    for M in wl.ROUTER_PREFILL_M:
+    for M in (256, 512) + tuple(wl.ROUTER_PREFILL_M):
         x = torch.from_numpy(wl.router_batch(M, w).x).to(dev)
         out = torch.empty((M, 256), dtype=torch.float32, device=dev)
         calls = [lambda wd=wd: bi.bi_linear_f32(x, wd.t(), bias, out=out) for wd in copies[:24]]
