@@ -158,3 +158,28 @@ def test_no_alloc_entry_runs_split_plans_unsplit_when_they_do_not_fit(bi, router
                                         256, 4096, ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
     assert st == bi.BI_OK
     assert_bitwise(host(y), host(bi.bi_linear_f32(x, weight_t(wd), bd)), "no-allocation entry vs bi_linear_f32")
+
+
+def test_split_ring_without_bias_strided_rows_and_bf16_output(bi):
+    # no bias term (nothing added, -0.0 kept), an X row pitch wider than K,
+    # and bf16 output: each equal to the unsplit tile's result in the same form
+    import torch
+    g = np.random.default_rng(4242)
+    M, N, K = 200, 256, 4096
+    w = (g.standard_normal((N, K)) * 0.02).astype(np.float32)
+    xh = g.standard_normal((M, K + 64)).astype(np.float32)
+    xw = dev(xh)
+    x = xw[:, :K]                                   # row pitch K + 64
+    wd = dev(w)
+    r = bi.bi_describe_recipe(bi.BI_F32, N, K)
+    split = bi.BI_PATH_PERSISTENT | (28 << 8)
+    assert bi.lib().bi_lab_workspace_size(ctypes.byref(r), split, M, N, K) > bi.WS_COUNTER_BYTES
+    for out_dtype in (torch.float32, torch.bfloat16):
+        banner(f"split ring M={M} no bias, strided X, out {out_dtype}")
+        y = bi.bi_lab_linear(x, weight_t(wd), None, recipe=r, path=split, out_dtype=out_dtype)
+        ref = bi.bi_lab_linear(x, weight_t(wd), None, recipe=r, path=bi.BI_PATH_PERSISTENT | (3 << 8),
+                               out_dtype=out_dtype)
+        assert torch.equal(y.view(torch.int16 if out_dtype == torch.bfloat16 else torch.int32),
+                           ref.view(torch.int16 if out_dtype == torch.bfloat16 else torch.int32)), out_dtype
+    y = host(bi.bi_lab_linear(x, weight_t(wd), None, recipe=r, path=split))
+    assert_close(y[:8], oracle.linear_f32(xh[:8, :K].copy(), w, None), F32_ATOL, F32_RTOL, "oracle, no bias")
