@@ -224,3 +224,47 @@ def test_l2_read_probe_rejects_on_the_host():
     assert f(FAKE, 1 << 20, 1, FAKE, 0, None) == bi.BI_EINVAL
     assert f(None, 1 << 20, 1, FAKE, 256, None) == bi.BI_EINVAL
     assert f(FAKE, 1 << 20, 1, None, 256, None) == bi.BI_EINVAL
+
+
+def _split_ws_model(M, N, K, block_k, code, cus=256):
+    # the k split of the ring-fed fp32 tiles as a plain function: the largest
+    # power of two S >= 2 with tiles x S <= cus whose parts each hold a whole
+    # number of k tile groups (four or two k tiles at a time for 32-row tiles,
+    # two for 64-row tiles), a tile count that is a multiple of 8 and at most
+    # 128; workspace = counters + tiles x (k tiles - k tiles per part + 1)
+    # partial tiles of BM x 32 fp32
+    bm = 32 if code == 28 else 64
+    tiles = -(-M // bm) * -(-N // 32)
+    T, kbpt = K // block_k, block_k // 32
+    spt = kbpt // 2
+    if tiles % 8 or tiles > 128 or K % 64 or kbpt % 2 or kbpt < (4 if bm == 32 else 2):
+        return 0
+    best, ks = 0, 2
+    while tiles * ks <= cus and ks <= T:
+        if T % ks == 0:
+            kts = T // ks
+            for par in ((4, 2) if bm == 32 else (2,)):
+                if kts >= par and kts % par == 0 and ((kts // par) * spt) % 2 == 0:
+                    best = ks
+                    break
+        ks *= 2
+    return 0 if not best else bi.WS_COUNTER_BYTES + tiles * (T - T // best + 1) * (bm // 8) * 64 * 16
+
+
+@pytest.mark.parametrize("N,K,block_k", [(256, 4096, 128), (256, 7168, 256), (128, 4096, 256), (128, 2048, 128),
+                                         (96, 1024, 64), (256, 4096, 4096), (512, 3072, 192)])
+def test_k_split_plan_and_workspace(N, K, block_k):
+    # the planner's k split of tile codes 28 and 29 and the workspace it asks
+    # for, against the plain model above, over a range of M (no GPU: 256
+    # compute units are assumed, the MI355X count)
+    r = bi.bi_describe_recipe(bi.BI_F32, N, K)
+    r.block_k = block_k
+    split_seen = 0
+    for code in (28, 29):
+        for M in (1, 5, 16, 31, 32, 33, 64, 96, 100, 128, 200, 256, 300, 512, 777, 1000, 1024, 2048):
+            got = L.bi_lab_workspace_size(ctypes.byref(r), bi.BI_PATH_PERSISTENT | (code << 8), M, N, K)
+            want = _split_ws_model(M, N, K, block_k, code)
+            assert got == want, (code, M, got, want)
+            split_seen += want > 0
+    if (N, K, block_k) == (256, 4096, 128):
+        assert split_seen >= 20
