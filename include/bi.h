@@ -127,9 +127,11 @@ bi_status_t bi_linear_bf16(const uint16_t* x, int64_t ldx,
  * HIP graph capture, tight serving loops, harnesses that forbid allocation):
  * the same arguments, plan and kernels, hence the same bits, with no caller
  * workspace.  The workspace is a static device array of the library, 16 MiB
- * + 16 KiB per GPU, held until the process ends; shapes whose plan needs more
- * (none of the compiled fp32 keys up to its decode limit) return
- * BI_EWORKSPACE before anything is enqueued.  Its first call on a device
+ * + 16 KiB per GPU, held until the process ends; a plan that splits the k
+ * tiles of its fp32 ring tiles over workgroups (tile codes 28, 29) and needs
+ * more runs those tiles unsplit, with the same bits and no workspace; any
+ * other shape whose plan needs more (none of the compiled fp32 keys up to
+ * its decode limit) returns BI_EWORKSPACE before anything is enqueued.  Its first call on a device
  * finds the array's address and clears its counters with a small kernel on
  * `stream`.  The library allocates nothing here.  All calls on one GPU share
  * the array: calls that overlap on one GPU (other streams, other host threads)
