@@ -1520,7 +1520,13 @@ static hipError_t launch_persistent_t(const LinearArgs& a, const Plan& p, hipStr
 // prefix, then each later partial -- then adds the bias: the same
 // operations as one workgroup doing the whole k range, and no workgroup
 // ever waits for another.  The counter wraps to zero at the last arrival.
-template <int BM, int PAR, int R, bool SPLIT = false>
+//
+// SPT: stages per k tile fixed at compile time (0: kbpt / 2 at run time).
+// With it fixed the step loop is unrolled over whole k tiles and a chain's
+// first MFMA takes a zero accumulator itself; a run-time choice between zero
+// and the running sum is a select on the previous MFMA's result, which makes
+// every step wait for the matrix pipe to drain (the same bits either way).
+template <int BM, int PAR, int R, bool SPLIT = false, int SPT = 0>
 __global__ __launch_bounds__(512) void k_ring_f32(LinearArgs a, int kbpt, int tiles_k, int tiles_m, int tiles_n,
                                                   int xbm, int xbn, int ksplit = 1,
                                                   f32x4* __restrict__ partials = nullptr,
@@ -1539,7 +1545,7 @@ __global__ __launch_bounds__(512) void k_ring_f32(LinearArgs a, int kbpt, int ti
     const int sub = w % S, grp = w / S;
     const int sm = sub >> 1, sn = sub & 1;
     const int r = lane & 15, g = lane >> 4;
-    const int spt = kbpt / 2;                               // stages per k tile
+    const int spt = SPT > 0 ? SPT : kbpt / 2;               // stages per k tile
     const int kts = tiles_k / ksplit;                       // k tiles of this workgroup
     const int nsteps = (kts / PAR) * spt;
     const int tiles = tiles_m * tiles_n;
@@ -1641,18 +1647,24 @@ __global__ __launch_bounds__(512) void k_ring_f32(LinearArgs a, int kbpt, int ti
         // step j: step j + 1 is visible (this wave's loads of it waited for,
         // then the barrier); the next step's fragments are read while this
         // step's MFMAs issue, the chains interleaved block by block
-        auto step = [&](int j, const Frag<true> (&A)[C][2], const Frag<true> (&B)[C][2], Frag<true> (&An)[C][2],
-                        Frag<true> (&Bn)[C][2]) {
+        auto step = [&](int j, auto ph, const Frag<true> (&A)[C][2], const Frag<true> (&B)[C][2],
+                        Frag<true> (&An)[C][2], Frag<true> (&Bn)[C][2]) {
+            // the step's place in its k tile: fixed at compile time where the
+            // loop is unrolled over whole k tiles, so that a chain's first
+            // MFMA takes a zero accumulator without a select
+            constexpr int PH = decltype(ph)::value, SP = SPT > 0 ? SPT : 1;
+            const bool first = PH >= 0 ? PH % SP == 0 : j % spt == 0;
+            const bool last = PH >= 0 ? PH % SP == SP - 1 : j % spt == spt - 1;
             wait_vm<(R - 2 * PAR) * LPU>();
             wait_lgkm0();
             bar();
-            if (j > 0 && j % spt == 0 && grp == 0 && !stores)
+            if (j > 0 && first && grp == 0 && !stores)
                 fold(j == spt);
 #pragma unroll
             for (int h = 0; h < PAR; ++h)
                 issue_unit(PAR * j + R + h);
             frags(An, Bn, j + 1);
-            if (j % spt == 0) {
+            if (first) {
 #pragma unroll
                 for (int c = 0; c < C; ++c)
                     P[c] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -1682,20 +1694,36 @@ __global__ __launch_bounds__(512) void k_ring_f32(LinearArgs a, int kbpt, int ti
             }
             if (stores) {
                 // k tile kt0 + PAR (j / spt) + C grp + c is complete
-                if (j % spt == spt - 1) {
+                if (last) {
 #pragma unroll
                     for (int c = 0; c < C; ++c)
                         *slot_ptr(kt0 - kts + PAR * (j / spt) + grp * C + c + 1) = P[c];
                 }
-            } else if (G > 1 && j % spt == spt - 1 && grp > 0) {
+            } else if (G > 1 && last && grp > 0) {
 #pragma unroll
                 for (int c = 0; c < C; ++c)
                     hand[((grp - 1) * S + sub) * C + c][lane] = P[c];
             }
         };
-        for (int j = 0; j < nsteps; j += 2) {
-            step(j, Aa, Ba, Ab, Bb);
-            step(j + 1, Ab, Bb, Aa, Ba);
+        using Run = std::integral_constant<int, -1>;
+        if constexpr (SPT == 0) {
+            for (int j = 0; j < nsteps; j += 2) {
+                step(j, Run{}, Aa, Ba, Ab, Bb);
+                step(j + 1, Run{}, Ab, Bb, Aa, Ba);
+            }
+        } else if constexpr (SPT <= 2) {
+            for (int j = 0; j < nsteps; j += 2) {
+                step(j, std::integral_constant<int, 0>{}, Aa, Ba, Ab, Bb);
+                step(j + 1, std::integral_constant<int, 1>{}, Ab, Bb, Aa, Ba);
+            }
+        } else {
+            static_assert(SPT == 4, "stages per k tile");
+            for (int j = 0; j < nsteps; j += 4) {
+                step(j, std::integral_constant<int, 0>{}, Aa, Ba, Ab, Bb);
+                step(j + 1, std::integral_constant<int, 1>{}, Ab, Bb, Aa, Ba);
+                step(j + 2, std::integral_constant<int, 2>{}, Aa, Ba, Ab, Bb);
+                step(j + 3, std::integral_constant<int, 3>{}, Ab, Bb, Aa, Ba);
+            }
         }
         // the last group: its hand-over is in LDS after one more barrier
         wait_vm<0>();
@@ -1758,6 +1786,28 @@ static bool ring_f32_ok(const LinearArgs& a, const Plan& p, int bm, int par)
            (int64_t)31 * a.ldw * 4 + (int64_t)a.K * 4 < (int64_t(1) << 32);
 }
 
+// k tiles of 4 or 8 32-k blocks (2 on the 64-row tile) run the step loop
+// unrolled over whole k tiles, with each step's place in its k tile known at
+// compile time; other even block counts keep it a run-time value
+template <int BM, int PAR, int R, bool SPLIT>
+static void ring_f32_kernel(int kbpt, int grid, hipStream_t s, const LinearArgs& a, int kb, int tiles_k,
+                            int tiles_m, int tiles_n, int xbm, int xbn, int ks, f32x4* partials, uint32_t* counters)
+{
+    const dim3 g((unsigned)grid), b(512);
+    if (BM == 64 && kbpt == 2)
+        k_ring_f32<BM, PAR, R, SPLIT, 1><<<g, b, 0, s>>>(a, kb, tiles_k, tiles_m, tiles_n, xbm, xbn, ks, partials,
+                                                          counters);
+    else if (kbpt == 4)
+        k_ring_f32<BM, PAR, R, SPLIT, 2><<<g, b, 0, s>>>(a, kb, tiles_k, tiles_m, tiles_n, xbm, xbn, ks, partials,
+                                                          counters);
+    else if (kbpt == 8)
+        k_ring_f32<BM, PAR, R, SPLIT, 4><<<g, b, 0, s>>>(a, kb, tiles_k, tiles_m, tiles_n, xbm, xbn, ks, partials,
+                                                          counters);
+    else
+        k_ring_f32<BM, PAR, R, SPLIT><<<g, b, 0, s>>>(a, kb, tiles_k, tiles_m, tiles_n, xbm, xbn, ks, partials,
+                                                       counters);
+}
+
 template <int BM, int PAR, int R>
 static hipError_t launch_ring_f32(const LinearArgs& a, const Plan& p, hipStream_t s)
 {
@@ -1767,7 +1817,8 @@ static hipError_t launch_ring_f32(const LinearArgs& a, const Plan& p, hipStream_
     const int tiles_n = (a.N + 31) / 32;
     const int grid = min(tiles_m * tiles_n, device_cu_count());
     const XcdBlock xb = xcd_block(tiles_m, tiles_n, BM, 32, grid);
-    k_ring_f32<BM, PAR, R><<<grid, 512, 0, s>>>(a, p.kbpt, p.tiles_k, tiles_m, tiles_n, xb.xbm, xb.xbn);
+    ring_f32_kernel<BM, PAR, R, false>(p.kbpt, grid, s, a, p.kbpt, p.tiles_k, tiles_m, tiles_n, xb.xbm, xb.xbn, 1,
+                                       nullptr, nullptr);
     return hipGetLastError();
 }
 
@@ -1836,8 +1887,8 @@ static hipError_t launch_ring_f32_split(const LinearArgs& a, const Plan& p, void
     const XcdBlock xb = xcd_block(tiles_m, tiles_n, BM, 32, tiles);
     uint32_t* counters = reinterpret_cast<uint32_t*>(ws);
     f32x4* partials = reinterpret_cast<f32x4*>(reinterpret_cast<char*>(ws) + kDecodeCounterBytes);
-    k_ring_f32<BM, PAR, R, true><<<tiles * ks, 512, 0, s>>>(a, p.kbpt, p.tiles_k, tiles_m, tiles_n, xb.xbm, xb.xbn,
-                                                            ks, partials, counters);
+    ring_f32_kernel<BM, PAR, R, true>(p.kbpt, tiles * ks, s, a, p.kbpt, p.tiles_k, tiles_m, tiles_n, xb.xbm, xb.xbn,
+                                      ks, partials, counters);
     return hipGetLastError();
 }
 
