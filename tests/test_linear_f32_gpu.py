@@ -156,6 +156,8 @@ def test_every_persistent_tile_shape_gives_the_same_bits(bi, router):
     (4100, 48, 1024, 256),     # more 32x32 tiles than compute units
     (9000, 32, 512, 128),      # more tiles than compute units, one step per k tile group
     (64, 32, 4096, 4096),      # one k tile: both fall back
+    (500, 64, 1536, 192),      # k tiles of six blocks: the step's place in its k tile known at run time only
+    (700, 128, 4096, 512),     # k tiles of sixteen blocks: likewise
 ])
 def test_ring_fed_fp32_tiles(bi, M, N, K, block_k):
     # the ring-fed fp32 shapes (32x32 on four or two k tiles at a time, 64x32
