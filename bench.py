@@ -513,7 +513,7 @@ def ceilings_leg(torch, bi, dev):
     bytes per shader clock (one 16-wave workgroup per CU reading 64 KiB of LDS
     with conflict-free 16-byte loads) and the issue interval of the recipe's
     MFMA instructions on register operands (eight waves per CU, two per SIMD,
-    eight independent chains each).  Cycles and clock come from the probes'
+    eight independent chains each, and one, two or four).  Cycles and clock come from the probes'
     own shader-cycle and wall-tick counters (median over the workgroups)."""
     grid = 256
     out = torch.zeros((grid, 3), dtype=torch.int64, device=dev)
@@ -541,6 +541,12 @@ def ceilings_leg(torch, bi, dev):
         res[name] = {"cycles_per_instr_per_SIMD": round(per, 2), "MHz": round(mhz, 1),
                      "TFLOPs": round(tf, 1), "frac_of_peak": round(tf / peak, 3),
                      "probe": "register operands, 8 waves per CU, 8 independent chains per wave"}
+        # the same with fewer accumulators per wave: each MFMA depends on the
+        # one `chains` before it, as the recipe's tile partials do
+        res[name]["cycles_per_instr_per_SIMD_by_chains"] = {
+            str(ch): round(run(lambda d=dtype, n=iters, c=ch: bi.bi_lab_mfma_rate(out, d, grid, n, c))[0]
+                           / (iters * 8 * 2), 2)
+            for ch in (1, 2, 4)}
     return res
 
 

@@ -67,7 +67,7 @@ _lib.bi_lab_stream_read.argtypes = [_P, _I64, _P, _I32, _P]
 _lib.bi_lab_l2_read.argtypes = [_P, _I64, _I32, _P, _I32, _P]
 _lib.bi_lab_clock.argtypes = [_P, _I32, _I32, _P]
 _lib.bi_lab_lds_read.argtypes = [_P, _I32, _I32, _P]
-_lib.bi_lab_mfma_rate.argtypes = [_P, _I32, _I32, _I32, _P]
+_lib.bi_lab_mfma_rate.argtypes = [_P, _I32, _I32, _I32, _I32, _P]
 _lib.bi_lab_plan.argtypes = [_I32, _I64, _I64, _I64, ctypes.POINTER(_I32)]
 _lib.bi_lab_moe_layout.argtypes = [_I64, _I64, _I64, _I64, _I64, ctypes.POINTER(_I64)]
 _lib.bi_linear_f32_noalloc.argtypes = [_P, _I64, _P, _I64, _P, _P, _I64, _I64, _I64, _I64, _P]
@@ -439,11 +439,12 @@ def bi_lab_lds_read(out: torch.Tensor, grid: int, iters: int):
     _check(_lib.bi_lab_lds_read(_ptr(out), grid, iters, ctypes.c_void_p(s.cuda_stream)), "bi_lab_lds_read")
 
 
-def bi_lab_mfma_rate(out: torch.Tensor, dtype: int, grid: int, iters: int):
-    """MFMA issue-rate probe (BI_F32: 16x16x4 f32, BI_BF16: 16x16x32 bf16): out int64 [grid, 3]."""
+def bi_lab_mfma_rate(out: torch.Tensor, dtype: int, grid: int, iters: int, chains: int = 8):
+    """MFMA issue-rate probe (BI_F32: 16x16x4 f32, BI_BF16: 16x16x32 bf16) over `chains`
+    independent accumulators per wave: out int64 [grid, 3]."""
     _check_probe_out(out, grid, "bi_lab_mfma_rate")
     s = _stream(out.device)
-    _check(_lib.bi_lab_mfma_rate(_ptr(out), dtype, grid, iters, ctypes.c_void_p(s.cuda_stream)),
+    _check(_lib.bi_lab_mfma_rate(_ptr(out), dtype, chains, grid, iters, ctypes.c_void_p(s.cuda_stream)),
            "bi_lab_mfma_rate")
 
 

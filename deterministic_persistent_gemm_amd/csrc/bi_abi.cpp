@@ -263,12 +263,13 @@ bi_status_t bi_lab_lds_read(uint64_t* out, int32_t grid, int32_t iters, hipStrea
     return launch_lds_read(out, grid, iters, stream) == hipSuccess ? BI_OK : BI_EHIP;
 }
 
-bi_status_t bi_lab_mfma_rate(uint64_t* out, int32_t dtype, int32_t grid, int32_t iters, hipStream_t stream)
+bi_status_t bi_lab_mfma_rate(uint64_t* out, int32_t dtype, int32_t chains, int32_t grid, int32_t iters,
+                             hipStream_t stream)
 {
-    if (!out || (dtype != BI_F32 && dtype != BI_BF16) || grid <= 0 || grid > 65535 || iters <= 0 ||
-        (reinterpret_cast<uintptr_t>(out) & 7u) != 0)
+    if (!out || (dtype != BI_F32 && dtype != BI_BF16) || (chains != 1 && chains != 2 && chains != 4 && chains != 8) ||
+        grid <= 0 || grid > 65535 || iters <= 0 || (reinterpret_cast<uintptr_t>(out) & 7u) != 0)
         return BI_EINVAL;
-    return launch_mfma_rate(out, dtype == BI_BF16, grid, iters, stream) == hipSuccess ? BI_OK : BI_EHIP;
+    return launch_mfma_rate(out, dtype == BI_BF16, chains, grid, iters, stream) == hipSuccess ? BI_OK : BI_EHIP;
 }
 
 size_t bi_moe_workspace_size(int64_t M, int64_t H, int64_t E, int64_t I, int64_t topk)

@@ -187,7 +187,9 @@ hipError_t launch_lds_read(uint64_t* out, int grid, int iters, hipStream_t s)
 }
 
 // MFMA issue rate on register operands: eight waves per workgroup, each
-// running eight independent accumulator chains (two A and four B operands,
+// running CH independent accumulator chains, eight MFMAs per round taking the
+// chains in turn, so that each MFMA depends on the one CH before it (two A
+// and four B operands,
 // fixed pseudo-random values with random signs and mantissas, as switching
 // data costs clock) of the recipe's instruction for `iters` rounds.  Thread
 // 0 records shader cycles and wall ticks; the accumulators are folded into a
@@ -202,7 +204,7 @@ __device__ __forceinline__ uint32_t lab_hash(uint32_t x)
     return x;
 }
 
-template <bool BF16>
+template <bool BF16, int CH>
 __global__ __launch_bounds__(512) void k_mfma_rate(uint64_t* __restrict__ out, int iters)
 {
     const int tid = threadIdx.x;
@@ -229,7 +231,7 @@ __global__ __launch_bounds__(512) void k_mfma_rate(uint64_t* __restrict__ out, i
         for (int it = 0; it < iters; ++it) {
 #pragma unroll
             for (int c = 0; c < 8; ++c)
-                acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[c & 1], b[c >> 1], acc[c], 0, 0, 0);
+                acc[c % CH] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[c & 1], b[c >> 1], acc[c % CH], 0, 0, 0);
         }
     } else {
         float a[2], b[4];
@@ -244,7 +246,7 @@ __global__ __launch_bounds__(512) void k_mfma_rate(uint64_t* __restrict__ out, i
         for (int it = 0; it < iters; ++it) {
 #pragma unroll
             for (int c = 0; c < 8; ++c)
-                acc[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[c & 1], b[c >> 1], acc[c], 0, 0, 0);
+                acc[c % CH] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[c & 1], b[c >> 1], acc[c % CH], 0, 0, 0);
         }
     }
     __syncthreads();
@@ -263,12 +265,23 @@ __global__ __launch_bounds__(512) void k_mfma_rate(uint64_t* __restrict__ out, i
         out[3 * blockIdx.x + 2] = 1;
 }
 
-hipError_t launch_mfma_rate(uint64_t* out, bool bf16, int grid, int iters, hipStream_t s)
+template <bool BF16>
+static void launch_mfma_chains(uint64_t* out, int chains, int grid, int iters, hipStream_t s)
+{
+    switch (chains) {
+    case 1:  k_mfma_rate<BF16, 1><<<(unsigned)grid, 512, 0, s>>>(out, iters); break;
+    case 2:  k_mfma_rate<BF16, 2><<<(unsigned)grid, 512, 0, s>>>(out, iters); break;
+    case 4:  k_mfma_rate<BF16, 4><<<(unsigned)grid, 512, 0, s>>>(out, iters); break;
+    default: k_mfma_rate<BF16, 8><<<(unsigned)grid, 512, 0, s>>>(out, iters); break;
+    }
+}
+
+hipError_t launch_mfma_rate(uint64_t* out, bool bf16, int chains, int grid, int iters, hipStream_t s)
 {
     if (bf16)
-        k_mfma_rate<true><<<(unsigned)grid, 512, 0, s>>>(out, iters);
+        launch_mfma_chains<true>(out, chains, grid, iters, s);
     else
-        k_mfma_rate<false><<<(unsigned)grid, 512, 0, s>>>(out, iters);
+        launch_mfma_chains<false>(out, chains, grid, iters, s);
     return hipGetLastError();
 }
 

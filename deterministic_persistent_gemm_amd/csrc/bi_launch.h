@@ -48,6 +48,6 @@ hipError_t launch_stream_read(const void* src, int64_t bytes, uint32_t* sink, in
 hipError_t launch_clock(uint64_t* out, int grid, int iters, hipStream_t s);
 hipError_t launch_lds_read(uint64_t* out, int grid, int iters, hipStream_t s);
 hipError_t launch_l2_read(const void* src, int64_t bytes, int iters, uint32_t* sink, int grid, hipStream_t s);
-hipError_t launch_mfma_rate(uint64_t* out, bool bf16, int grid, int iters, hipStream_t s);
+hipError_t launch_mfma_rate(uint64_t* out, bool bf16, int chains, int grid, int iters, hipStream_t s);
 
 }  // namespace bi

@@ -371,11 +371,13 @@ bi_status_t bi_lab_moe_layout(int64_t M, int64_t H, int64_t E, int64_t I, int64_
  *                      conflict-free 16-byte loads (64 KiB per round):
  *                      the LDS read rate a compute unit sustains.
  *  bi_lab_mfma_rate    each of `grid` workgroups of 512 threads runs, per
- *                      wave, iters x 8 independent MFMAs of the recipe's
- *                      instruction for `dtype` (BI_F32: 16x16x4 f32,
- *                      BI_BF16: 16x16x32 bf16) on register operands: the
- *                      issue rate the matrix cores sustain with nothing else
- *                      in the way.
+ *                      wave, iters x 8 MFMAs of the recipe's instruction for
+ *                      `dtype` (BI_F32: 16x16x4 f32, BI_BF16: 16x16x32
+ *                      bf16) on register operands, spread over `chains`
+ *                      (1, 2, 4 or 8) independent accumulators taken in
+ *                      turn: with 8 the issue rate the matrix cores sustain
+ *                      with nothing else in the way, with fewer the rate of
+ *                      dependent chains like the recipe's tile partials.
  *                      Both write three uint64 per workgroup to out[3 wg ..]
  *                      (device, 8-byte aligned): shader cycles and wall ticks
  *                      of the loop, and a word that keeps its results alive.
@@ -387,7 +389,8 @@ bi_status_t bi_lab_l2_read(const void* src, int64_t bytes, int32_t iters, uint32
                            hipStream_t stream);
 bi_status_t bi_lab_clock(uint64_t* out, int32_t grid, int32_t iters, hipStream_t stream);
 bi_status_t bi_lab_lds_read(uint64_t* out, int32_t grid, int32_t iters, hipStream_t stream);
-bi_status_t bi_lab_mfma_rate(uint64_t* out, int32_t dtype, int32_t grid, int32_t iters, hipStream_t stream);
+bi_status_t bi_lab_mfma_rate(uint64_t* out, int32_t dtype, int32_t chains, int32_t grid, int32_t iters,
+                             hipStream_t stream);
 
 #ifdef __cplusplus
 }

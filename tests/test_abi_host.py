@@ -226,6 +226,19 @@ def test_l2_read_probe_rejects_on_the_host():
     assert f(FAKE, 1 << 20, 1, None, 256, None) == bi.BI_EINVAL
 
 
+def test_mfma_rate_probe_rejects_on_the_host():
+    # one, two, four or eight accumulator chains per wave; a recipe dtype; an
+    # 8-byte aligned output
+    f = L.bi_lab_mfma_rate
+    for chains in (0, 3, 16, -1):
+        assert f(FAKE, bi.BI_F32, chains, 256, 10, None) == bi.BI_EINVAL, chains
+    assert f(FAKE, 7, 8, 256, 10, None) == bi.BI_EINVAL
+    assert f(FAKE, bi.BI_BF16, 8, 0, 10, None) == bi.BI_EINVAL
+    assert f(FAKE, bi.BI_BF16, 8, 256, 0, None) == bi.BI_EINVAL
+    assert f(None, bi.BI_F32, 8, 256, 10, None) == bi.BI_EINVAL
+    assert f(ctypes.c_void_p(FAKE.value + 4), bi.BI_F32, 8, 256, 10, None) == bi.BI_EINVAL
+
+
 def _split_ws_model(M, N, K, block_k, code, cus=256):
     # the k split of the ring-fed fp32 tiles as a plain function: the largest
     # power of two S >= 2 with tiles x S <= cus whose parts each hold a whole
